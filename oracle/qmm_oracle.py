@@ -1,0 +1,205 @@
+"""CPU oracle for the weight-only, group-wise asymmetric integer quantized matmul.
+
+TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this module. The product path (the HIP
+library and its Python binding) never calls it, and it shares no code with
+that path.
+
+What it computes, step by step, in the order the sources state it:
+
+* Packing: integer codes are stored K-major in 32-bit words, ``eps = 32 // bits``
+  codes per word; code ``k`` of column ``n`` sits in word ``k // eps`` of that
+  column at bit offset ``(k % eps) * bits``. (dashq_kernel.py, module
+  docstring and ``_pack_kmajor`` / ``_unpack_kmajor``.)
+* 3-bit codes are two planes: a 2-bit plane holding ``q >> 1`` and a 1-bit
+  plane holding ``q & 1``; ``q = (hi << 1) | lo``. (dashq_kernel.py, module
+  docstring, ``TritonQuantLinear.__init__`` and ``dequantize_weight``.)
+* Groups: row ``k`` of the weight belongs to group ``k // group_size``;
+  ``group_size == -1`` means one group for the whole column.
+  (GPTQModel-Compatible Triton Kernel README, "Group Quantization".)
+* Dequantization: ``w[k, n] = scale[g, n] * (q[k, n] - zero[g, n])``.
+  (GPTQModel-Compatible Triton Kernel README, "Dequantization Formula";
+  dashq_kernel.py, ``dequantize_weight``.)
+* Product: ``y = x @ w`` with x of shape (M, K). (GPTQModel-Compatible Triton
+  Kernel README, "API Reference", ``gptqmodel_quantized_matmul``.)
+
+Arithmetic is float64 throughout. Every fp16 input is widened to float64
+exactly; for the workloads' integer zero points every product ``x * w`` is exact
+in float64, so the only rounding is in the K-term sums (relative error about
+K * 2**-53). The matrix product uses numpy's float64 matmul as a library step.
+
+Parity pins: every function here is pinned by CPU tests (hand-worked words and
+products from the definitions, exact integer and rational recomputation,
+invariants); none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# Bit widths whose codes pack into one plane of 32-bit words. 3 is handled as
+# two planes (2 + 1); 1 is the width of the low 3-bit plane.
+PLANE_BITS = (1, 2, 4, 8)
+SUPPORTED_BITS = (2, 3, 4, 8)
+
+# Element-wise parity rule: |y - y_ref| <= REL_TOL * sum_k |x_k w_kn| + ABS_TOL.
+REL_TOL = 2e-3
+ABS_TOL = 1e-3
+
+
+def elements_per_word(bits: int) -> int:
+    """Codes per 32-bit word for a single plane of ``bits``-bit codes."""
+    if bits not in PLANE_BITS:
+        raise ValueError(f"no single-plane packing for {bits}-bit codes")
+    return 32 // bits
+
+
+def count_out_of_range(codes: np.ndarray, bits: int) -> int:
+    """Number of codes that do not fit in ``bits`` bits (they are masked on packing)."""
+    return int(np.count_nonzero(np.asarray(codes, dtype=np.int64) >> bits))
+
+
+def pack_kmajor(codes: np.ndarray, bits: int) -> np.ndarray:
+    """(K, N) codes -> (K // eps, N) int32 words, K-major.
+
+    Code k of a column goes to word k // eps of that column, at bit offset
+    (k % eps) * bits; codes are first masked to ``bits`` bits.
+    """
+    codes = np.asarray(codes)
+    K, N = codes.shape
+    eps = elements_per_word(bits)
+    if K % eps:
+        raise ValueError(f"K={K} is not a multiple of {eps} codes per word")
+    mask = np.uint32((1 << bits) - 1)
+    words = np.zeros((K // eps, N), dtype=np.uint32)
+    for k in range(K):
+        shift = np.uint32((k % eps) * bits)
+        words[k // eps] |= (codes[k].astype(np.uint32) & mask) << shift
+    return words.view(np.int32)
+
+
+def unpack_kmajor(words: np.ndarray, bits: int, K: int) -> np.ndarray:
+    """(K // eps, N) int32 words -> (K, N) uint8 codes; inverse of ``pack_kmajor``.
+
+    Words are read as unsigned 32-bit patterns, so shifts are logical.
+    """
+    u = np.asarray(words).view(np.uint32)
+    eps = elements_per_word(bits)
+    if u.shape[0] * eps < K:
+        raise ValueError("too few word rows for K")
+    mask = np.uint32((1 << bits) - 1)
+    q = np.empty((K, u.shape[1]), dtype=np.uint8)
+    for k in range(K):
+        shift = np.uint32((k % eps) * bits)
+        q[k] = (u[k // eps] >> shift) & mask
+    return q
+
+
+def pack_3bit(codes: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """(K, N) codes in [0, 7] -> (2-bit plane (K/16, N), 1-bit plane (K/32, N)).
+
+    The 2-bit plane holds the top two bits of each code, the 1-bit plane the
+    lowest bit. Codes are masked to 3 bits first.
+    """
+    q = np.asarray(codes).astype(np.uint8) & np.uint8(7)
+    return pack_kmajor(q >> 1, 2), pack_kmajor(q & 1, 1)
+
+
+def unpack_3bit(plane2: np.ndarray, plane1: np.ndarray, K: int) -> np.ndarray:
+    """Two planes -> (K, N) codes, q = (hi << 1) | lo."""
+    hi = unpack_kmajor(plane2, 2, K).astype(np.uint8)
+    lo = unpack_kmajor(plane1, 1, K).astype(np.uint8)
+    return (hi << 1) | lo
+
+
+def pack(codes: np.ndarray, bits: int) -> tuple[np.ndarray, np.ndarray | None]:
+    """Pack for any supported width: (qweight, qweight_lo); qweight_lo is None unless bits == 3."""
+    if bits == 3:
+        return pack_3bit(codes)
+    if bits not in SUPPORTED_BITS:
+        raise ValueError(f"unsupported bit width {bits}")
+    return pack_kmajor(codes, bits), None
+
+
+def unpack(qweight: np.ndarray, qweight_lo: np.ndarray | None, bits: int, K: int) -> np.ndarray:
+    if bits == 3:
+        return unpack_3bit(qweight, qweight_lo, K)
+    if bits not in SUPPORTED_BITS:
+        raise ValueError(f"unsupported bit width {bits}")
+    return unpack_kmajor(qweight, bits, K)
+
+
+def group_rows(K: int, group_size: int) -> int:
+    """Rows of the weight per group: group_size, or K when group_size == -1."""
+    if group_size == -1:
+        return K
+    if group_size <= 0 or K % group_size:
+        raise ValueError(f"group_size={group_size} does not divide K={K}")
+    return group_size
+
+
+def num_groups(K: int, group_size: int) -> int:
+    return K // group_rows(K, group_size)
+
+
+def dequantize(q: np.ndarray, scales: np.ndarray, zeros: np.ndarray, group_size: int) -> np.ndarray:
+    """(K, N) codes -> (K, N) float64 weights, w = scale[g] * (q - zero[g]), g = k // group_size."""
+    q = np.asarray(q)
+    K = q.shape[0]
+    rows = group_rows(K, group_size)
+    g = np.arange(K) // rows
+    s = np.asarray(scales).astype(np.float64)
+    z = np.asarray(zeros).astype(np.float64)
+    if s.shape[0] != K // rows or z.shape[0] != K // rows:
+        raise ValueError("scales/zeros must have one row per group")
+    return s[g] * (q.astype(np.float64) - z[g])
+
+
+def matmul(x: np.ndarray, w: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """y = x @ w and the tolerance reference a = sum_k |x_k * w_kn|, both float64."""
+    x64 = np.asarray(x).astype(np.float64)
+    w64 = np.asarray(w, dtype=np.float64)
+    return x64 @ w64, np.abs(x64) @ np.abs(w64)
+
+
+def quantized_matmul(x, qweight, qweight_lo, zeros, scales, bits: int, group_size: int):
+    """Reference for ``y = x @ dequantize(qweight)`` from packed words.
+
+    Arguments follow the functional statement of the problem (x, packed weight,
+    zeros, scales, bits, group_size); ``qweight_lo`` is the 1-bit plane for
+    3-bit weights. Returns (y, a) in float64, a being the tolerance reference.
+    """
+    K = np.asarray(x).shape[1]
+    q = unpack(qweight, qweight_lo, bits, K)
+    return matmul(x, dequantize(q, scales, zeros, group_size))
+
+
+def quantized_matmul_codes(x, codes, zeros, scales, group_size: int):
+    """Same product from unpacked codes (skips the packing step)."""
+    return matmul(x, dequantize(codes, scales, zeros, group_size))
+
+
+def parity_bound(a: np.ndarray) -> np.ndarray:
+    return REL_TOL * np.asarray(a, dtype=np.float64) + ABS_TOL
+
+
+def parity_report(y_dev: np.ndarray, y_ref: np.ndarray, a: np.ndarray) -> dict:
+    """Compare a device result (any float dtype, decoded exactly) with the reference.
+
+    ``ok`` holds iff every element is finite and within the bound.
+    ``max_ratio`` is the largest |err| / bound; the bound alone is loose, so a
+    healthy kernel sits far below 1.
+    """
+    yd = np.asarray(y_dev).astype(np.float64)
+    err = np.abs(yd - y_ref)
+    bound = parity_bound(a)
+    finite = np.isfinite(yd)
+    ratio = np.where(finite, err / bound, np.inf)
+    bad = ~finite | (err > bound)
+    return {
+        "ok": bool(not bad.any()),
+        "violations": int(bad.sum()),
+        "nonfinite": int((~finite).sum()),
+        "max_ratio": float(ratio.max()) if ratio.size else 0.0,
+        "median_ratio": float(np.median(ratio)) if ratio.size else 0.0,
+        "max_abs_err": float(err.max()) if err.size else 0.0,
+    }
