@@ -1,0 +1,309 @@
+#!/usr/bin/env python3
+"""Throughput of the weight-only group-quantized matmul on one MI355X.
+
+One step is one decode product y = x @ dequant(W) at M=1, K=4096, N=4096,
+4-bit codes, group size 128 (one transformer projection), on seeded synthetic
+inputs already resident in HBM. The value is achieved HBM bandwidth in GB/s
+counting the algorithmic bytes (packed words, scales, zeros, x, y).
+
+Cold cache: every step reads a different copy of the weights, and the copies
+together exceed twice the 256 MB Infinity Cache, so each step streams its
+weights from HBM. The K timed steps are one HIP graph replay (one kernel node
+per step), so host launch overhead is outside the timed region but each
+node's dispatch is inside it.
+
+The JSON line also carries:
+  roofline      the GEMV kernel against 8 TB/s: algorithmic bytes per launch
+                over its average launch duration, each launch bracketed by
+                events on its own stream; `traffic` is the HBM bytes the
+                FETCH_SIZE / WRITE_SIZE counters saw per launch (from the
+                committed profile summary, null if the kernel source changed)
+  cpu_baseline  the CPU oracle on the same workload on this host
+  gemm          the prefill product M=2048, K=4096, N=14336, 8-bit, one group
+                per column: TFLOP/s against the 2.5 PFLOP/s fp16 dense peak
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+FP16_DENSE_PEAK_TFLOPS = 2500.0
+COLD_BYTES = 512 * 1024 * 1024  # twice the Infinity Cache
+METRIC = "M=1 GEMV achieved HBM GB/s (% of peak); M=2048 GEMM TOPS (% MFMA peak)"
+
+
+def algorithmic_bytes(wl) -> int:
+    words = wl.K * wl.N * wl.bits // 8
+    sz = 2 * wl.groups * wl.N * 2
+    return words + sz + wl.M * wl.K * 2 + wl.M * wl.N * 2
+
+
+def kernel_source_hash(name: str) -> str:
+    p = os.path.join(ROOT, "weight_only_group_amd", "csrc", name)
+    h = hashlib.sha256()
+    for f in (p, os.path.join(ROOT, "weight_only_group_amd", "csrc", "common.h")):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(kind: str):
+    """HBM bytes per launch from profiles/traffic_<kind>.txt, if taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kind}.txt")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            rec = json.loads("".join(line for line in f if not line.startswith("#")))
+    except (ValueError, OSError):
+        return None
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash(rec.get("source", "")):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return 1
+
+
+def bench_gemv(w, torch, datagen, steps: int, warmup: int):
+    wl = datagen.WORKLOADS[datagen.HEADLINE_GEMV]
+    dev = torch.device("cuda:0")
+    d = datagen.generate(wl)
+    x = torch.from_numpy(d["x"]).to(dev)
+    z0 = torch.from_numpy(d["zeros"]).to(dev)
+    s0 = torch.from_numpy(d["scales"]).to(dev)
+    qw0, qlo0 = w.qmm_pack(torch.from_numpy(d["codes"]).to(dev), wl.bits)
+    per_copy = qw0.nbytes + z0.nbytes + s0.nbytes + (qlo0.nbytes if qlo0 is not None else 0)
+    R = max(1, math.ceil(COLD_BYTES / per_copy))
+    copies = [(qw0, qlo0, z0, s0)] + [
+        (qw0.clone(), None if qlo0 is None else qlo0.clone(), z0.clone(), s0.clone()) for _ in range(R - 1)]
+    y = torch.empty((wl.M, wl.N), dtype=torch.float16, device=dev)
+    nbytes = w.workspace_bytes(wl.M, wl.K, wl.N, wl.bits, wl.group_size)
+    ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    lib = w.library()
+
+    def launch(i: int, stream_ptr: int):
+        qw, qlo, z, s = copies[i % R]
+        st = lib.qmm_gemv(x.data_ptr(), wl.M, wl.K, qw.data_ptr(), None if qlo is None else qlo.data_ptr(),
+                          z.data_ptr(), s.data_ptr(), wl.N, wl.bits, wl.group_size, y.data_ptr(), ws.data_ptr(),
+                          ws.numel(), stream_ptr)
+        if st != 0:
+            raise RuntimeError(f"qmm_gemv failed: {lib.qmm_last_error().decode()}")
+
+    # eager warm-up (also loads the code object)
+    cur = torch.cuda.current_stream().cuda_stream
+    for i in range(max(warmup, 3)):
+        launch(i, cur)
+    torch.cuda.synchronize()
+
+    def capture(n: int, offset: int):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            sp = torch.cuda.current_stream().cuda_stream
+            for i in range(n):
+                launch(offset + i, sp)
+        return g
+
+    g_warm = capture(max(warmup, 1), 0)
+    g_timed = capture(steps, warmup)
+    g_warm.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    g_timed.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    total_ms = e0.elapsed_time(e1)
+
+    # Per-launch duration: each launch bracketed by events on the stream it runs on.
+    n_ev = min(steps, 100)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
+    cur = torch.cuda.current_stream().cuda_stream
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        launch(steps + warmup + i, cur)
+        b.record()
+    torch.cuda.synchronize()
+    per_launch_us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+    mean_launch_us = sum(per_launch_us) / len(per_launch_us)
+
+    # parity spot check of the last output against the oracle-free invariant: finite
+    assert bool(torch.isfinite(y).all())
+    return {
+        "wl": wl, "R": R, "total_ms": total_ms, "ms_per_step": total_ms / steps,
+        "bytes": algorithmic_bytes(wl), "mean_launch_us": mean_launch_us,
+        "median_launch_us": per_launch_us[len(per_launch_us) // 2], "d": d, "ws_bytes": nbytes,
+    }
+
+
+def bench_gemm(w, torch, datagen, steps: int, warmup: int):
+    wl = datagen.WORKLOADS[datagen.HEADLINE_GEMM]
+    dev = torch.device("cuda:0")
+    d = datagen.generate(wl)
+    x = torch.from_numpy(d["x"]).to(dev)
+    z0 = torch.from_numpy(d["zeros"]).to(dev)
+    s0 = torch.from_numpy(d["scales"]).to(dev)
+    qw0, _ = w.qmm_pack(torch.from_numpy(d["codes"]).to(dev), wl.bits)
+    R = 4  # weight copies rotated (235 MB of packed weights)
+    copies = [(qw0, z0, s0)] + [(qw0.clone(), z0.clone(), s0.clone()) for _ in range(R - 1)]
+    y = torch.empty((wl.M, wl.N), dtype=torch.float16, device=dev)
+    lib = w.library()
+
+    def launch(i: int):
+        qw, z, s = copies[i % R]
+        st = lib.qmm_gemm(x.data_ptr(), wl.M, wl.K, qw.data_ptr(), None, z.data_ptr(), s.data_ptr(), wl.N, wl.bits,
+                          wl.group_size, y.data_ptr(), torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"qmm_gemm failed: {lib.qmm_last_error().decode()}")
+
+    for i in range(warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        launch(warmup + i)
+        b.record()
+    e1.record()
+    torch.cuda.synchronize()
+    total_ms = e0.elapsed_time(e1)
+    per = sorted(a.elapsed_time(b) for a, b in evs)
+    assert bool(torch.isfinite(y).all())
+    flops = 2.0 * wl.M * wl.N * wl.K
+    mean_ms = sum(per) / len(per)
+    return {"wl": wl, "total_ms": total_ms, "ms_per_step": total_ms / steps, "mean_launch_ms": mean_ms,
+            "flops": flops, "bytes": algorithmic_bytes(wl), "d": d}
+
+
+def cpu_baseline_gemv(datagen, d, seconds: float):
+    import oracle
+    wl = datagen.WORKLOADS[datagen.HEADLINE_GEMV]
+    qw, qlo = oracle.pack(d["codes"], wl.bits)
+    n, t0 = 0, time.perf_counter()
+    while True:
+        oracle.quantized_matmul(d["x"], qw, qlo, d["zeros"], d["scales"], wl.bits, wl.group_size)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    per = el / n
+    return {"value": round(algorithmic_bytes(wl) / per / 1e9, 4), "unit": "GB/s", "cores": cpu_threads(),
+            "kind": "oracle",
+            "sample": f"the whole workload ({wl.name}) from packed words: unpack, float64 dequantize and "
+                      f"product; {n} calls in {el:.1f} s, {per * 1e3:.1f} ms each"}
+
+
+def cpu_baseline_gemm(datagen, d, rows: int):
+    import oracle
+    wl = datagen.WORKLOADS[datagen.HEADLINE_GEMM]
+    qw, _ = oracle.pack(d["codes"], wl.bits)
+    t0 = time.perf_counter()
+    oracle.quantized_matmul(d["x"][:rows], qw, None, d["zeros"], d["scales"], wl.bits, wl.group_size)
+    el = time.perf_counter() - t0
+    return {"value": round(2.0 * rows * wl.N * wl.K / el / 1e12, 6), "unit": "TFLOP/s", "cores": cpu_threads(),
+            "kind": "oracle",
+            "sample": f"first {rows} of {wl.M} rows of {wl.name} from packed words (unpack, float64 dequantize of "
+                      f"the whole weight, product), one call, {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500, help="timed decode products")
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--gemm-steps", type=int, default=20)
+    ap.add_argument("--gemm-warmup", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle time budget for the GEMV baseline")
+    ap.add_argument("--cpu-gemm-rows", type=int, default=256)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gemm", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (no sharding, no collectives); "
+              "run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import datagen
+    import weight_only_group_amd as w
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    w.library()  # fails loudly if the HIP library is missing
+
+    gv = bench_gemv(w, torch, datagen, args.steps, args.warmup)
+    wl = gv["wl"]
+    value = gv["bytes"] / (gv["ms_per_step"] * 1e-3) / 1e9
+    achieved = gv["bytes"] / (gv["mean_launch_us"] * 1e-6) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(gv["ms_per_step"], 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "M": wl.M, "K": wl.K, "N": wl.N, "bits": wl.bits, "group_size": wl.group_size,
+            "seed": wl.seed, "weight_copies_rotated": gv["R"], "algorithmic_bytes_per_step": gv["bytes"],
+            "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+            "timing": "one HIP graph replay of the timed steps, events around it",
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": committed_traffic("gemv"),
+            "kernel": "gemv_kernel<4,4>", "mean_launch_us": round(gv["mean_launch_us"], 3),
+            "median_launch_us": round(gv["median_launch_us"], 3),
+        },
+    }
+    if not args.no_gemm:
+        gm = bench_gemm(w, torch, datagen, args.gemm_steps, args.gemm_warmup)
+        tflops = gm["flops"] / (gm["ms_per_step"] * 1e-3) / 1e12
+        k_tflops = gm["flops"] / (gm["mean_launch_ms"] * 1e-3) / 1e12
+        out["gemm"] = {
+            "workload": gm["wl"].name, "value": round(tflops, 2), "unit": "TFLOP/s",
+            "ms_per_step": round(gm["ms_per_step"], 4), "pct_of_fp16_dense_peak": round(100 * tflops / FP16_DENSE_PEAK_TFLOPS, 2),
+            "roofline": {"bound": "mfma", "achieved": round(k_tflops, 2), "peak": FP16_DENSE_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(k_tflops / FP16_DENSE_PEAK_TFLOPS, 4),
+                         "traffic": committed_traffic("gemm"), "kernel": "gemm_kernel<8,true>",
+                         "mean_launch_ms": round(gm["mean_launch_ms"], 4)},
+        }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_gemv(datagen, gv["d"], args.cpu_seconds)
+        if not args.no_gemm:
+            out["gemm"]["cpu_baseline"] = cpu_baseline_gemm(datagen, gm["d"], args.cpu_gemm_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,326 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Packing and unpacking must match bit for bit. Products must satisfy, element
+by element, |y - y_ref| <= 2e-3 * sum_k |x_k w_kn| + 1e-3 with y decoded
+exactly from fp16. One-hot activations select single rows of the
+dequantized weight; those outputs are exact fp16 roundings and must match the
+oracle's rounding bit for bit, which pins every index of the kernels.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("a GPU is required for the parity tests")
+    import weight_only_group_amd as w
+    w.library()  # raises if the HIP library is missing
+    return w
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _t(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.view(dtype)
+    return t.to(DEV)
+
+
+def _to_gpu_case(d):
+    return {k: _t(v) for k, v in d.items()}
+
+
+def _pack_gpu(w, codes_np, bits):
+    qw, qlo = w.qmm_pack(_t(codes_np), bits)
+    return qw, qlo
+
+
+def _product(w, path, x, qw, qlo, z, s, bits, gs):
+    if path == "gemv":
+        return w.qmm_gemv(x, qw, qlo, z, s, bits, gs)
+    return w.qmm_gemm(x, qw, qlo, z, s, bits, gs)
+
+
+def _check(y_gpu, y_ref, a, label, max_ratio=0.35):
+    rep = oracle.parity_report(y_gpu, y_ref, a)
+    _say(f"  {label}: max|err|/bound={rep['max_ratio']:.4f} median={rep['median_ratio']:.5f} "
+         f"violations={rep['violations']} nonfinite={rep['nonfinite']}")
+    assert rep["ok"], (label, rep)
+    # The bound is loose; a sound kernel stays well inside it.
+    assert rep["max_ratio"] < max_ratio, (label, rep)
+
+
+# ------------------------------------------------------------------ packing
+
+PACK_SHAPES = [(32, 8), (64, 24), (96, 520), (512, 256), (256, 1000)]
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("K,N", PACK_SHAPES)
+def test_pack_unpack_bit_exact(gpu, bits, K, N):
+    if K % (32 if bits == 3 else 32 // bits):
+        pytest.skip("K not a multiple of the word size")
+    _say(f"pack/unpack bits={bits} K={K} N={N}")
+    codes = datagen.draw_codes(K, N, bits, seed=K + N + bits)
+    qw_ref, qlo_ref = oracle.pack(codes, bits)
+    qw, qlo = _pack_gpu(gpu, codes, bits)
+    torch.cuda.synchronize()
+    assert np.array_equal(qw.cpu().numpy(), qw_ref)
+    if bits == 3:
+        assert np.array_equal(qlo.cpu().numpy(), qlo_ref)
+    back = gpu.qmm_unpack(_t(qw_ref), None if qlo_ref is None else _t(qlo_ref), K, bits)
+    assert np.array_equal(back.cpu().numpy(), codes)
+
+
+@pytest.mark.parametrize("name", list(datagen.WORKLOADS))
+def test_pack_workload_shapes_bit_exact(gpu, name):
+    wl = datagen.WORKLOADS[name]
+    _say(f"pack/unpack workload {name}")
+    codes = datagen.draw_codes(wl.K, wl.N, wl.bits, wl.seed)
+    qw_ref, qlo_ref = oracle.pack(codes, wl.bits)
+    qw, qlo = _pack_gpu(gpu, codes, wl.bits)
+    assert np.array_equal(qw.cpu().numpy(), qw_ref)
+    if wl.bits == 3:
+        assert np.array_equal(qlo.cpu().numpy(), qlo_ref)
+    back = gpu.qmm_unpack(qw, qlo, wl.K, wl.bits)
+    assert np.array_equal(back.cpu().numpy(), codes)
+
+
+def test_pack_counts_and_masks_out_of_range_codes(gpu):
+    rng = np.random.default_rng(1)
+    for bits in (2, 3, 4):
+        codes = rng.integers(0, 256, size=(64, 40), dtype=np.uint8)
+        qw, qlo, bad = gpu.qmm_pack(_t(codes), bits, count_bad=True)
+        qw_ref, qlo_ref = oracle.pack(codes, bits)
+        assert np.array_equal(qw.cpu().numpy(), qw_ref)
+        if bits == 3:
+            assert np.array_equal(qlo.cpu().numpy(), qlo_ref)
+        assert int(bad.item()) == oracle.count_out_of_range(codes, bits)
+
+
+# ------------------------------------------------------------------ products
+
+def _run(gpu, path, M, K, N, bits, gs, seed=0, zero_range=None, nonint_zero=False, scale_range=(0.005, 0.05)):
+    d = datagen.small_case(M, K, N, bits, gs, seed=seed, zero_range=zero_range, scale_range=scale_range)
+    if nonint_zero:
+        rng = np.random.default_rng(seed + 99)
+        d["zeros"] = rng.uniform(-1.5, (1 << bits) + 0.5, size=d["zeros"].shape).astype(np.float16)
+    qw_ref, qlo_ref = oracle.pack(d["codes"], bits)
+    g = _to_gpu_case(d)
+    qw, qlo = _pack_gpu(gpu, d["codes"], bits)
+    y = _product(gpu, path, g["x"], qw, qlo, g["zeros"], g["scales"], bits, gs)
+    y_ref, a = oracle.quantized_matmul(d["x"], qw_ref, qlo_ref, d["zeros"], d["scales"], bits, gs)
+    return y.cpu().numpy(), y_ref, a
+
+
+SWEEP_GEMV = [
+    # (M, K, N, bits, gs): ragged N tails (not multiples of 64), K spanning several units and groups
+    (1, 256, 64, 4, 128), (1, 512, 200, 4, 32), (3, 1024, 264, 4, 64), (16, 256, 520, 4, -1),
+    (1, 256, 72, 8, 32), (5, 512, 136, 8, 128), (8, 1024, 8, 8, -1),
+    (1, 512, 96, 2, 64), (8, 256, 264, 2, 32), (16, 2048, 40, 2, 128),
+    (1, 512, 128, 3, 128), (2, 256, 200, 3, 32), (8, 1024, 520, 3, 64), (1, 96, 24, 3, -1),
+    (1, 32, 8, 4, 32), (16, 32, 8, 8, -1),
+]
+
+
+@pytest.mark.parametrize("M,K,N,bits,gs", SWEEP_GEMV)
+def test_gemv_sweep(gpu, M, K, N, bits, gs):
+    _say(f"gemv M={M} K={K} N={N} bits={bits} gs={gs}")
+    y, y_ref, a = _run(gpu, "gemv", M, K, N, bits, gs, seed=M * 7 + K + N)
+    _check(y, y_ref, a, "gemv")
+
+
+SWEEP_GEMM = [
+    (1, 256, 64, 4, 128), (17, 512, 264, 4, 64), (300, 256, 520, 4, -1), (257, 320, 264, 4, 32),
+    (100, 512, 136, 8, 128), (260, 1024, 264, 8, -1), (64, 96, 8, 8, 32),
+    (33, 512, 96, 2, 64), (270, 256, 264, 2, 32),
+    (40, 512, 128, 3, 128), (300, 256, 520, 3, 32), (8, 1024, 40, 3, -1),
+]
+
+
+@pytest.mark.parametrize("M,K,N,bits,gs", SWEEP_GEMM)
+def test_gemm_sweep(gpu, M, K, N, bits, gs):
+    _say(f"gemm M={M} K={K} N={N} bits={bits} gs={gs}")
+    y, y_ref, a = _run(gpu, "gemm", M, K, N, bits, gs, seed=M * 5 + K + N)
+    _check(y, y_ref, a, "gemm")
+
+
+@pytest.mark.parametrize("path", ["gemv", "gemm"])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+def test_non_integer_zero_points(gpu, path, bits):
+    _say(f"{path} non-integer zeros bits={bits}")
+    M = 4 if path == "gemv" else 70
+    y, y_ref, a = _run(gpu, path, M, 512, 264, bits, 64, seed=bits, nonint_zero=True)
+    _check(y, y_ref, a, f"{path} nonint-z")
+
+
+@pytest.mark.parametrize("path", ["gemv", "gemm"])
+@pytest.mark.parametrize("bits,gs", [(2, 32), (3, 64), (4, 128), (8, -1), (4, 32)])
+def test_one_hot_rows_bit_exact(gpu, path, bits, gs):
+    """x = e_k gives y = fp16(w[k, :]); probes every word slot and the first and last k of each group."""
+    K, N = 256, 136
+    d = datagen.small_case(1, K, N, bits, gs, seed=bits * 3 + (gs if gs > 0 else 1))
+    qw, qlo = _pack_gpu(gpu, d["codes"], bits)
+    g = _to_gpu_case(d)
+    rows = K if gs == -1 else gs
+    eps = 16 if bits == 3 else 32 // bits
+    probe = sorted(set(list(range(0, 2 * max(eps, 32))) + [g0 * rows for g0 in range(K // rows)] +
+                       [g0 * rows + rows - 1 for g0 in range(K // rows)] + [K - 1]))
+    _say(f"one-hot {path} bits={bits} gs={gs}: {len(probe)} rows")
+    # Each probe is one row of x; run up to 16 rows per call on the GEMV, all at once on the GEMM.
+    X = np.zeros((len(probe), K), dtype=np.float16)
+    for i, k in enumerate(probe):
+        X[i, k] = 1
+    w_ref = oracle.dequantize(d["codes"], d["scales"], d["zeros"], gs)
+    want = w_ref[probe].astype(np.float16)
+    got = []
+    if path == "gemv":
+        for c in range(0, len(probe), 16):
+            got.append(gpu.qmm_gemv(_t(X[c:c + 16]), qw, qlo, g["zeros"], g["scales"], bits, gs).cpu().numpy())
+        got = np.concatenate(got)
+    else:
+        got = gpu.qmm_gemm(_t(X), qw, qlo, g["zeros"], g["scales"], bits, gs).cpu().numpy()
+    mism = np.argwhere(got.view(np.uint16) != want.view(np.uint16))
+    assert mism.size == 0, [(probe[i], n, float(got[i, n]), float(want[i, n])) for i, n in mism[:10]]
+
+
+@pytest.mark.parametrize("path", ["gemv", "gemm"])
+def test_column_sums(gpu, path):
+    """x = 1 sums every column of the dequantized weight."""
+    K, N, bits, gs = 512, 264, 4, 128
+    d = datagen.small_case(2, K, N, bits, gs, seed=21)
+    x = np.ones((2, K), dtype=np.float16)
+    x[1] = -1
+    qw, qlo = _pack_gpu(gpu, d["codes"], bits)
+    g = _to_gpu_case(d)
+    y = _product(gpu, path, _t(x), qw, qlo, g["zeros"], g["scales"], bits, gs).cpu().numpy()
+    y_ref, a = oracle.quantized_matmul_codes(x, d["codes"], d["zeros"], d["scales"], gs)
+    _check(y, y_ref, a, f"{path} column sums")
+
+
+def test_gemv_is_deterministic_and_reuses_workspace(gpu):
+    wl = datagen.WORKLOADS["gemv_m1_k4096_n4096_int4_g128"]
+    d = datagen.generate(wl)
+    g = _to_gpu_case(d)
+    qw, qlo = _pack_gpu(gpu, d["codes"], wl.bits)
+    outs = [gpu.qmm_gemv(g["x"], qw, qlo, g["zeros"], g["scales"], wl.bits, wl.group_size).cpu().numpy()
+            for _ in range(3)]
+    # a different shape through the same cached workspace in between
+    d2 = datagen.small_case(3, 1024, 264, 4, 64, seed=5)
+    g2 = _to_gpu_case(d2)
+    qw2, _ = _pack_gpu(gpu, d2["codes"], 4)
+    y2 = gpu.qmm_gemv(g2["x"], qw2, None, g2["zeros"], g2["scales"], 4, 64).cpu().numpy()
+    outs.append(gpu.qmm_gemv(g["x"], qw, qlo, g["zeros"], g["scales"], wl.bits, wl.group_size).cpu().numpy())
+    for o in outs[1:]:
+        assert np.array_equal(o.view(np.uint16), outs[0].view(np.uint16))
+    qw2_ref, _ = oracle.pack(d2["codes"], 4)
+    y2_ref, a2 = oracle.quantized_matmul(d2["x"], qw2_ref, None, d2["zeros"], d2["scales"], 4, 64)
+    _check(y2, y2_ref, a2, "gemv after reuse")
+
+
+def test_gemm_is_deterministic(gpu):
+    d = datagen.small_case(300, 512, 520, 8, -1, seed=3, zero_range=(96, 160))
+    g = _to_gpu_case(d)
+    qw, qlo = _pack_gpu(gpu, d["codes"], 8)
+    a = gpu.qmm_gemm(g["x"], qw, qlo, g["zeros"], g["scales"], 8, -1).cpu().numpy()
+    b = gpu.qmm_gemm(g["x"], qw, qlo, g["zeros"], g["scales"], 8, -1).cpu().numpy()
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+
+
+def test_non_default_stream(gpu):
+    d = datagen.small_case(1, 1024, 264, 3, 128, seed=8)
+    g = _to_gpu_case(d)
+    qw, qlo = _pack_gpu(gpu, d["codes"], 3)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        y = gpu.qmm_gemv(g["x"], qw, qlo, g["zeros"], g["scales"], 3, 128)
+        y2 = gpu.qmm_gemm(g["x"], qw, qlo, g["zeros"], g["scales"], 3, 128)
+    s.synchronize()
+    qw_ref, qlo_ref = oracle.pack(d["codes"], 3)
+    y_ref, a = oracle.quantized_matmul(d["x"], qw_ref, qlo_ref, d["zeros"], d["scales"], 3, 128)
+    _check(y.cpu().numpy(), y_ref, a, "gemv side stream")
+    _check(y2.cpu().numpy(), y_ref, a, "gemm side stream")
+
+
+def test_errors_on_device(gpu):
+    """Invalid requests are refused on a real device too, and leave the output untouched."""
+    import weight_only_group_amd as w
+    x = torch.zeros((1, 256), dtype=torch.float16, device=DEV)
+    qw = torch.zeros((32, 64), dtype=torch.int32, device=DEV)
+    z = torch.zeros((2, 64), dtype=torch.float16, device=DEV)
+    y = torch.full((1, 64), 7.0, dtype=torch.float16, device=DEV)
+    with pytest.raises(w.QmmError) as e:
+        w.qmm_gemv(x, qw, None, z, z, 4, 100, out=y)
+    assert e.value.status == 4
+    with pytest.raises(w.QmmError) as e:
+        w.qmm_gemm(x, qw, None, z, z, 5, 128, out=y)
+    assert e.value.status == 2
+    lib = w.library()
+    st = lib.qmm_gemv(x.data_ptr() + 2, 1, 256, qw.data_ptr(), None, z.data_ptr(), z.data_ptr(), 64, 4, 128,
+                      y.data_ptr(), None, 0, None)
+    assert st == 5
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0)
+
+
+# ------------------------------------------------------------------ the five workloads
+
+@pytest.mark.parametrize("name", [n for n, wl in datagen.WORKLOADS.items() if wl.M <= 16])
+def test_workload_gemv_full(gpu, name):
+    wl = datagen.WORKLOADS[name]
+    _say(f"workload {name} (full output)")
+    d = datagen.generate(wl)
+    g = _to_gpu_case(d)
+    qw, qlo = _pack_gpu(gpu, d["codes"], wl.bits)
+    y = gpu.qmm_gemv(g["x"], qw, qlo, g["zeros"], g["scales"], wl.bits, wl.group_size).cpu().numpy()
+    y_ref, a = oracle.quantized_matmul_codes(d["x"], d["codes"], d["zeros"], d["scales"], wl.group_size)
+    _check(y, y_ref, a, name)
+    # the prefill kernel computes the same function
+    y2 = gpu.qmm_gemm(g["x"], qw, qlo, g["zeros"], g["scales"], wl.bits, wl.group_size).cpu().numpy()
+    _check(y2, y_ref, a, name + " via gemm")
+
+
+def test_workload_prefill_sampled_rows(gpu):
+    """The prefill product at full size, launched exactly as the benchmark launches it;
+    sampled rows (and every column) are compared with the oracle."""
+    wl = datagen.WORKLOADS["gemm_m2048_k4096_n14336_int8_gchan"]
+    _say(f"workload {wl.name} (sampled rows)")
+    d = datagen.generate(wl)
+    g = _to_gpu_case(d)
+    qw, qlo = _pack_gpu(gpu, d["codes"], wl.bits)
+    y = gpu.qmm_gemm(g["x"], qw, qlo, g["zeros"], g["scales"], wl.bits, wl.group_size)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(y).all())
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, 1023, 2047], rng.choice(wl.M, 58, replace=False)]))
+    y_rows = y[torch.as_tensor(rows, device=DEV)].cpu().numpy()
+    w_ref = oracle.dequantize(d["codes"], d["scales"], d["zeros"], wl.group_size)
+    y_ref, a = oracle.matmul(d["x"][rows], w_ref)
+    _check(y_rows, y_ref, a, f"{wl.name} rows={len(rows)}")
+
+
+def test_workspace_shared_across_shapes(gpu):
+    """Calls of different shapes share one cached workspace: wider problems place their
+    partial sums where a narrower problem's would not, and the arrival counters never move."""
+    cases = [(1, 1024, 4096, 4, 128), (1, 1024, 6144, 3, 128), (2, 2048, 264, 2, 64), (1, 1024, 4096, 4, 128),
+             (1, 1024, 6144, 3, 128)]
+    for i, (M, K, N, bits, gs) in enumerate(cases):
+        _say(f"shared workspace call {i}: M={M} K={K} N={N} bits={bits} gs={gs}")
+        y, y_ref, a = _run(gpu, "gemv", M, K, N, bits, gs, seed=i)
+        _check(y, y_ref, a, f"shared workspace {i}")

@@ -1,0 +1,230 @@
+"""Python binding of libqmm: the weight-only group-quantized matmul on MI355X.
+
+Argument marshalling only: every step runs in the HIP library (libqmm.so,
+built in-tree by ``weight_only_group_amd.build``). PyTorch provides device
+memory and the current stream. There is no fallback: if the library is
+missing or a tensor is not on a GPU, the call raises.
+
+Functions mirror the C ABI (include/qmm.h):
+
+* ``qmm_pack(codes, bits)`` -> ``(qweight, qweight_lo)``
+* ``qmm_unpack(qweight, qweight_lo, K, bits)`` -> codes
+* ``qmm_gemv(x, qweight, qweight_lo, zeros, scales, bits, group_size)`` (1 <= M <= 16)
+* ``qmm_gemm(x, qweight, qweight_lo, zeros, scales, bits, group_size)`` (any M)
+* ``quantized_matmul(x, qweight, qzeros, scales, bits, group_size, qweight_lo=None)``:
+  the functional form, M <= 16 to the GEMV, larger M to the GEMM.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqmm.so")
+
+QMM_OK = 0
+STATUS_NAMES = {
+    0: "QMM_OK", 1: "QMM_ERR_NULL", 2: "QMM_ERR_BITS", 3: "QMM_ERR_SHAPE", 4: "QMM_ERR_GROUP",
+    5: "QMM_ERR_ALIGN", 6: "QMM_ERR_WORKSPACE", 7: "QMM_ERR_HIP",
+}
+# Every symbol the header declares.
+EXPORTS = (
+    "qmm_abi_version", "qmm_status_string", "qmm_last_error", "qmm_pack", "qmm_unpack",
+    "qmm_workspace_bytes", "qmm_gemv", "qmm_gemm",
+)
+GEMV_MAX_M = 16
+
+_lib = None
+_lock = threading.Lock()
+
+
+class QmmError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)}: {detail}")
+
+
+def _declare(lib):
+    P, I, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.qmm_abi_version.restype = I
+    lib.qmm_abi_version.argtypes = []
+    lib.qmm_status_string.restype = ctypes.c_char_p
+    lib.qmm_status_string.argtypes = [I]
+    lib.qmm_last_error.restype = ctypes.c_char_p
+    lib.qmm_last_error.argtypes = []
+    lib.qmm_pack.restype = I
+    lib.qmm_pack.argtypes = [P, I, I, I, P, P, P, P]
+    lib.qmm_unpack.restype = I
+    lib.qmm_unpack.argtypes = [P, P, I, I, I, P, P]
+    lib.qmm_workspace_bytes.restype = SZ
+    lib.qmm_workspace_bytes.argtypes = [I, I, I, I, I]
+    lib.qmm_gemv.restype = I
+    lib.qmm_gemv.argtypes = [P, I, I, P, P, P, P, I, I, I, P, P, SZ, P]
+    lib.qmm_gemm.restype = I
+    lib.qmm_gemm.argtypes = [P, I, I, P, P, P, P, I, I, I, P, P]
+    return lib
+
+
+def library(path: str | None = None):
+    """The loaded libqmm (ctypes.CDLL). Raises if it has not been built."""
+    global _lib
+    if path is not None:
+        return _declare(ctypes.CDLL(path))
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    f"{LIB_PATH} is missing: build it with `python -m weight_only_group_amd.build` "
+                    "(there is no fallback implementation)")
+            _lib = _declare(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def _check(status: int, where: str):
+    if status != QMM_OK:
+        raise QmmError(status, where, library().qmm_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _gpu(t, name, dtype, ndim=2):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions (got shape {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def packed_shapes(K: int, N: int, bits: int):
+    """Shapes of (qweight, qweight_lo) for K x N codes (qweight_lo None unless bits == 3)."""
+    if bits == 3:
+        return (K // 16, N), (K // 32, N)
+    return (K // (32 // bits), N), None
+
+
+def qmm_pack(codes: torch.Tensor, bits: int, count_bad: bool = False):
+    """(K, N) uint8 codes on the GPU -> (qweight, qweight_lo[, bad_count])."""
+    _gpu(codes, "codes", torch.uint8)
+    K, N = codes.shape
+    shp, shp_lo = packed_shapes(K, N, bits) if bits in (2, 3, 4, 8) else ((1, 1), None)
+    dev = codes.device
+    qw = torch.empty(shp, dtype=torch.int32, device=dev)
+    qlo = torch.empty(shp_lo, dtype=torch.int32, device=dev) if shp_lo else None
+    bad = torch.zeros(1, dtype=torch.int32, device=dev) if count_bad else None
+    with torch.cuda.device(dev):
+        _check(library().qmm_pack(_ptr(codes), K, N, bits, _ptr(qw), _ptr(qlo), _ptr(bad), _stream(dev)), "qmm_pack")
+    return (qw, qlo, bad) if count_bad else (qw, qlo)
+
+
+def qmm_unpack(qweight: torch.Tensor, qweight_lo: torch.Tensor | None, K: int, bits: int) -> torch.Tensor:
+    _gpu(qweight, "qweight", torch.int32)
+    if qweight_lo is not None:
+        _gpu(qweight_lo, "qweight_lo", torch.int32)
+    N = qweight.shape[1]
+    shp, shp_lo = packed_shapes(K, N, bits) if bits in (2, 3, 4, 8) else (None, None)
+    if shp is not None and tuple(qweight.shape) != shp:
+        raise ValueError(f"qweight has shape {tuple(qweight.shape)}, expected {shp}")
+    if shp_lo is not None and (qweight_lo is None or tuple(qweight_lo.shape) != shp_lo):
+        raise ValueError(f"qweight_lo must have shape {shp_lo}")
+    dev = qweight.device
+    codes = torch.empty((K, N), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        _check(library().qmm_unpack(_ptr(qweight), _ptr(qweight_lo), K, N, bits, _ptr(codes), _stream(dev)),
+               "qmm_unpack")
+    return codes
+
+
+def workspace_bytes(M: int, K: int, N: int, bits: int, group_size: int) -> int:
+    return int(library().qmm_workspace_bytes(M, K, N, bits, group_size))
+
+
+# Zero-filled GEMV workspaces, one per (device, stream); the kernels leave their
+# counters at zero, so a workspace is reused call after call on its stream.
+_workspaces: dict = {}
+
+
+def gemv_workspace(device, nbytes: int, stream=None) -> torch.Tensor | None:
+    if nbytes == 0:
+        return None
+    dev = torch.device(device)
+    s = torch.cuda.current_stream(dev) if stream is None else stream
+    key = (dev.index, s.cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
+        _workspaces[key] = ws
+    return ws
+
+
+def _check_product_args(x, qweight, qweight_lo, zeros, scales, bits):
+    _gpu(x, "x", torch.float16)
+    _gpu(qweight, "qweight", torch.int32)
+    if bits == 3:
+        if qweight_lo is None:
+            raise ValueError("3-bit weights need qweight_lo (the 1-bit plane)")
+        _gpu(qweight_lo, "qweight_lo", torch.int32)
+    _gpu(zeros, "zeros", torch.float16)
+    _gpu(scales, "scales", torch.float16)
+    M, K = x.shape
+    N = qweight.shape[1]
+    if bits in (2, 3, 4, 8):
+        shp, shp_lo = packed_shapes(K, N, bits)
+        if tuple(qweight.shape) != shp or (shp_lo and tuple(qweight_lo.shape) != shp_lo):
+            raise ValueError(f"packed weight shapes {tuple(qweight.shape)} do not match K={K}, N={N}, bits={bits}")
+    if zeros.shape != scales.shape or zeros.shape[1] != N:
+        raise ValueError("zeros and scales must both be (G, N)")
+    return M, K, N
+
+
+def qmm_gemv(x, qweight, qweight_lo, zeros, scales, bits: int, group_size: int, out=None, workspace=None):
+    """y = x @ dequantize(W) for 1 <= M <= 16; returns (M, N) fp16."""
+    M, K, N = _check_product_args(x, qweight, qweight_lo, zeros, scales, bits)
+    dev = x.device
+    y = torch.empty((M, N), dtype=torch.float16, device=dev) if out is None else out
+    nbytes = workspace_bytes(M, K, N, bits, group_size) if M <= GEMV_MAX_M else 0
+    ws = workspace if workspace is not None else gemv_workspace(dev, nbytes)
+    with torch.cuda.device(dev):
+        _check(library().qmm_gemv(_ptr(x), M, K, _ptr(qweight), _ptr(qweight_lo), _ptr(zeros), _ptr(scales), N, bits,
+                                  group_size, _ptr(y), _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev)),
+               "qmm_gemv")
+    return y
+
+
+def qmm_gemm(x, qweight, qweight_lo, zeros, scales, bits: int, group_size: int, out=None):
+    """y = x @ dequantize(W) for any M on the matrix cores; returns (M, N) fp16."""
+    M, K, N = _check_product_args(x, qweight, qweight_lo, zeros, scales, bits)
+    dev = x.device
+    y = torch.empty((M, N), dtype=torch.float16, device=dev) if out is None else out
+    with torch.cuda.device(dev):
+        _check(library().qmm_gemm(_ptr(x), M, K, _ptr(qweight), _ptr(qweight_lo), _ptr(zeros), _ptr(scales), N, bits,
+                                  group_size, _ptr(y), _stream(dev)),
+               "qmm_gemm")
+    return y
+
+
+def quantized_matmul(x, qweight, qzeros, scales, bits: int, group_size: int, qweight_lo=None):
+    """output = x @ dequantize(qweight), in the argument order of the functional API.
+
+    ``qzeros`` are the (G, N) fp16 zero points; M <= 16 runs the decode GEMV,
+    larger M the prefill GEMM.
+    """
+    if x.dim() != 2:
+        raise ValueError("x must be (M, K)")
+    if x.shape[0] <= GEMV_MAX_M:
+        return qmm_gemv(x, qweight, qweight_lo, qzeros, scales, bits, group_size)
+    return qmm_gemm(x, qweight, qweight_lo, qzeros, scales, bits, group_size)

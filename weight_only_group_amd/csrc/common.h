@@ -1,0 +1,64 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qmm {
+
+typedef _Float16 f16;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Two fp16 1024.0 values. OR-ing a code q < 1024 into the low mantissa bits of
+// a half gives exactly 1024 + q, so one integer op turns two codes into two
+// halves; subtracting 1024 (+ the zero point) afterwards is exact.
+constexpr uint32_t kMagic1024x2 = 0x64006400u;
+
+__device__ __forceinline__ f16x2 as_f16x2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
+__device__ __forceinline__ uint32_t as_u32(f16x2 h) { return __builtin_bit_cast(uint32_t, h); }
+__device__ __forceinline__ float half_bits_to_float(uint16_t b) {
+  return (float)__builtin_bit_cast(f16, b);
+}
+
+// Rows of the weight per group: group_size, or K for group_size == -1.
+inline int group_rows(int K, int group_size) { return group_size == -1 ? K : group_size; }
+
+// ---- decode GEMV (small M) ----------------------------------------------
+// Column strips of the decode product are at least 32 columns wide; the
+// workspace header has one arrival counter per strip.
+constexpr int kGemvMaxN = 1 << 20;
+constexpr int kGemvMaxStrips = kGemvMaxN / 32;
+struct GemvPlan {
+  int vec;          // adjacent columns per lane (2 or 4); a wave covers 16 * vec columns
+  int waves;        // waves per block (4 or 16), each taking a slice of the block's K range
+  int strip_cols;   // columns per block
+  int nstrips;      // blocks along N
+  int ksplit;       // blocks along K
+  int units_per_block;  // 32-row units of K per block
+  int upg;          // 32-row units per group
+  int upg_log2;     // log2(upg) if upg is a power of two, else -1
+  size_t counters_bytes;  // arrival counters (one per strip), padded
+  size_t workspace_bytes; // counters + split-K partial sums
+};
+GemvPlan gemv_plan(int M, int K, int N, int bits, int group_size);
+hipError_t launch_gemv(const GemvPlan& p, const uint16_t* x, int M, int K, const uint32_t* qw,
+                       const uint32_t* qlo, const uint16_t* zeros, const uint16_t* scales, int N,
+                       int bits, int group_size, uint16_t* y, void* workspace, hipStream_t stream);
+
+// ---- prefill GEMM ---------------------------------------------------------
+hipError_t launch_gemm(const uint16_t* x, int M, int K, const uint32_t* qw, const uint32_t* qlo,
+                       const uint16_t* zeros, const uint16_t* scales, int N, int bits,
+                       int group_size, uint16_t* y, hipStream_t stream);
+
+// ---- pack / unpack ----------------------------------------------------------
+hipError_t launch_pack(const uint8_t* codes, int K, int N, int bits, uint32_t* qw, uint32_t* qlo,
+                       int32_t* bad_count, hipStream_t stream);
+hipError_t launch_unpack(const uint32_t* qw, const uint32_t* qlo, int K, int N, int bits,
+                         uint8_t* codes, hipStream_t stream);
+
+}  // namespace qmm
