@@ -240,6 +240,8 @@ def main():
     ap.add_argument("--cpu-gemm-rows", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemm", action="store_true")
+    ap.add_argument("--only", choices=("gemv", "gemm"), default=None,
+                    help="run one product only and print its own line (for profiling runs)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -256,7 +258,17 @@ def main():
         sys.exit(1)
     w.library()  # fails loudly if the HIP library is missing
 
+    if args.only == "gemm":
+        gm = bench_gemm(w, torch, datagen, args.gemm_steps, args.gemm_warmup)
+        print(json.dumps({"workload": gm["wl"].name, "ms_per_step": round(gm["ms_per_step"], 4),
+                          "mean_launch_ms": round(gm["mean_launch_ms"], 4),
+                          "TFLOP/s": round(gm["flops"] / (gm["mean_launch_ms"] * 1e-3) / 1e12, 2)}), flush=True)
+        return
     gv = bench_gemv(w, torch, datagen, args.steps, args.warmup)
+    if args.only == "gemv":
+        print(json.dumps({"workload": gv["wl"].name, "ms_per_step": round(gv["ms_per_step"], 6),
+                          "GB/s": round(gv["bytes"] / (gv["ms_per_step"] * 1e-3) / 1e9, 2)}), flush=True)
+        return
     wl = gv["wl"]
     value = gv["bytes"] / (gv["ms_per_step"] * 1e-3) / 1e9
     achieved = gv["bytes"] / (gv["mean_launch_us"] * 1e-6) / 1e9

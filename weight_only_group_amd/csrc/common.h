@@ -11,6 +11,7 @@ typedef _Float16 f16;
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -34,8 +35,8 @@ inline int group_rows(int K, int group_size) { return group_size == -1 ? K : gro
 constexpr int kGemvMaxN = 1 << 20;
 constexpr int kGemvMaxStrips = kGemvMaxN / 32;
 struct GemvPlan {
-  int vec;          // adjacent columns per lane (2 or 4); a wave covers 16 * vec columns
-  int waves;        // waves per block (4 or 16), each taking a slice of the block's K range
+  int vec;          // adjacent columns per lane (1, 2 or 4); a wave covers 16 * vec columns
+  int waves;        // waves per block (4, 8 or 16), each taking a slice of the block's K range
   int strip_cols;   // columns per block
   int nstrips;      // blocks along N
   int ksplit;       // blocks along K

@@ -37,10 +37,10 @@ namespace qmm {
 namespace {
 
 constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int kThreads = 256;
-constexpr int LDK = BK + 8;  // halves per LDS row of a staged slab
+constexpr int LDK = BK + 8;  // halves per LDS row of a staged activation slab
 constexpr int LDY = BN + 8;  // halves per LDS row of the staged output tile
-constexpr int kLdsHalves = 2 * (BM + BN) * LDK;  // two slab buffers; the output tile reuses them
+constexpr int kLdsHalves = BM * LDY;  // the output tile; the three activation buffers fit inside
+static_assert(3 * BM * LDK <= kLdsHalves, "activation buffers must fit in the LDS allocation");
 static_assert(BM * LDY <= kLdsHalves, "output tile must fit in the slab buffers");
 
 struct GemmArgs {
@@ -56,53 +56,58 @@ struct GemmArgs {
   int mblocks, nblocks;
 };
 
-// Word rows of one plane a 64-k slab spans.
-template <int BITS> struct Slab;
-template <> struct Slab<8> { static constexpr int R = 16, RLO = 0, EPS = 4; };
-template <> struct Slab<4> { static constexpr int R = 8, RLO = 0, EPS = 8; };
-template <> struct Slab<2> { static constexpr int R = 4, RLO = 0, EPS = 16; };
-template <> struct Slab<3> { static constexpr int R = 4, RLO = 2, EPS = 16; };
+// Words one lane needs for one 32-column tile and one 16-k step: a 32 x 32 x 16
+// MFMA B fragment gives lane l the 8 consecutive k of chunk l / 32 of the
+// step, for column l % 32. NW words of the main plane, NL of the 1-bit plane
+// (3-bit codes).
+template <int BITS> struct Frag;
+template <> struct Frag<8> { static constexpr int NW = 2, NL = 0, EPS = 4; };
+template <> struct Frag<4> { static constexpr int NW = 1, NL = 0, EPS = 8; };
+template <> struct Frag<2> { static constexpr int NW = 1, NL = 0, EPS = 16; };
+template <> struct Frag<3> { static constexpr int NW = 1, NL = 1, EPS = 16; };
 
-// One slab's weight words held by one thread (its column), plus the zero
-// point and scale of each 32-k half when every group has its own.
-template <int BITS, bool POST_SCALE> struct StageB {
-  uint32_t w[Slab<BITS>::R];
-  uint32_t l[Slab<BITS>::RLO > 0 ? Slab<BITS>::RLO : 1];
-  uint16_t z[POST_SCALE ? 1 : 2], s[POST_SCALE ? 1 : 2];
-};
-
-// Four fp16 pairs 1024 + q for codes k = 8c .. 8c + 7 of a 64-k slab, k
-// ascending (pair i = codes 8c + 2i, 8c + 2i + 1), from the words of one
-// column covering the slab.
+// Word row (within the plane) of word w of k-step s of slab ks, for lane
+// chunk kc; and the bit offset of the lane's first code in that word.
 template <int BITS>
-__device__ __forceinline__ void codes8(const uint32_t* w, const uint32_t* wl, int c, uint32_t (&h)[4]) {
+__device__ __forceinline__ int frag_row(int ks, int s, int kc, int w) {
+  if constexpr (BITS == 8) return ks * 16 + 4 * s + 2 * kc + w;
+  else if constexpr (BITS == 4) return ks * 8 + 2 * s + kc;
+  else return ks * 4 + s;  // 2-bit and the 2-bit plane of 3-bit codes
+}
+
+// Four fp16 pairs 1024 + q (pair p = codes 2p, 2p + 1 of the lane's 8 k) from
+// the fragment's words. kc selects the lane's half of a 16-code word; s the
+// 16-k step within the 32 codes of a 1-bit plane word.
+template <int BITS>
+__device__ __forceinline__ void frag_codes(const uint32_t* w, const uint32_t* l, int kc, int s, uint32_t (&h)[4]) {
   if constexpr (BITS == 8) {
     // byte permute: (byte, 0x64, byte, 0x64) = halves 1024 + q
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      h[2 * r] = __builtin_amdgcn_perm(0x64646464u, w[2 * c + r], 0x04010400u);
-      h[2 * r + 1] = __builtin_amdgcn_perm(0x64646464u, w[2 * c + r], 0x04030402u);
-    }
+    h[0] = __builtin_amdgcn_perm(0x64646464u, w[0], 0x04010400u);
+    h[1] = __builtin_amdgcn_perm(0x64646464u, w[0], 0x04030402u);
+    h[2] = __builtin_amdgcn_perm(0x64646464u, w[1], 0x04010400u);
+    h[3] = __builtin_amdgcn_perm(0x64646464u, w[1], 0x04030402u);
   } else if constexpr (BITS == 4) {
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      const uint32_t t = w[c] >> (8 * p);
+      const uint32_t t = w[0] >> (8 * p);
       h[p] = (t & 0xFu) | ((t << 12) & 0xF0000u) | kMagic1024x2;
     }
   } else if constexpr (BITS == 2) {
+    const uint32_t u = w[0] >> (16 * kc);
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      const uint32_t t = w[c >> 1] >> (16 * (c & 1) + 4 * p);
+      const uint32_t t = u >> (4 * p);
       h[p] = (t & 0x3u) | ((t << 14) & 0x30000u) | kMagic1024x2;
     }
   } else {
-    const uint32_t hw = w[c >> 1] >> (16 * (c & 1));
-    const uint32_t lw = wl[c >> 2] >> (8 * (c & 3));
+    const uint32_t u = w[0] >> (16 * kc);
+    const uint32_t v = l[0] >> (16 * (s & 1) + 8 * kc);
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      const uint32_t a = (((hw >> (4 * p)) & 0x3u) << 1) | ((lw >> (2 * p)) & 1u);
-      const uint32_t b = (((hw >> (4 * p + 2)) & 0x3u) << 1) | ((lw >> (2 * p + 1)) & 1u);
-      h[p] = a | (b << 16) | kMagic1024x2;
+      const uint32_t t = u >> (4 * p), b = v >> (2 * p);
+      const uint32_t hi = ((t & 0x3u) << 1) | ((t << 15) & 0x60000u);
+      const uint32_t lo = (b & 0x1u) | ((b << 15) & 0x10000u);
+      h[p] = hi | lo | kMagic1024x2;
     }
   }
 }
@@ -120,22 +125,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, size_
 }
 constexpr int kNonTemporal = 2;  // buffer-load cache policy: streamed data
 
-// Scheduling-group mask of vector-memory reads (AMDGPU sched_group_barrier).
-constexpr int kSchedVmemRead = 0x020;
-
-template <int BITS, bool POST_SCALE, bool KTAIL>
-__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
+template <int BITS, bool POST_SCALE, bool KTAIL, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) f16 lds[kLdsHalves];
-  constexpr int R = Slab<BITS>::R;
-  constexpr int RLO = Slab<BITS>::RLO;
-  constexpr int EPS = Slab<BITS>::EPS;
-  using SB = StageB<BITS, POST_SCALE>;
+  constexpr int THREADS = 64 * WM * WN;
+  constexpr int TM = BM / WM / 32;           // 32-row MFMA tiles per wave
+  constexpr int TN = BN / WN / 32;           // 32-column MFMA tiles per wave
+  constexpr int CA = BM * BK / 8 / THREADS;  // 16-byte activation chunks per thread per slab
+  constexpr int NW = Frag<BITS>::NW, NL = Frag<BITS>::NL;
+  constexpr int NG = POST_SCALE ? 1 : 2;     // zero/scale pairs per column per slab (one per 32 k)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
-  const int i16 = lane & 15, j4 = lane >> 4;
+  const int wm = wave / WN, wn = wave % WN;
+  const int kc = lane >> 5;  // k chunk of the lane in a fragment
 
   const int tile = remap_block(blockIdx.x, g.mblocks * g.nblocks);
   const int nb = tile / g.mblocks;
@@ -144,183 +148,195 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   const int nk = (g.K + BK - 1) / BK;
 
   // Buffer resources: every global load below is a 32-bit per-lane offset
-  // plus a scalar per-slab offset, which keeps address arithmetic out of the
-  // vector registers.
+  // plus a scalar offset, which keeps address arithmetic out of the vector
+  // registers.
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(g.x, (size_t)g.M * g.K * 2);
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(g.qw, (size_t)(g.K / EPS) * g.N * 4);
-  const __amdgpu_buffer_rsrc_t rl = make_rsrc(RLO > 0 ? g.qlo : g.qw, RLO > 0 ? (size_t)(g.K / 32) * g.N * 4 : 4);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(g.qw, (size_t)(g.K / Frag<BITS>::EPS) * g.N * 4);
+  const __amdgpu_buffer_rsrc_t rl = make_rsrc(NL > 0 ? g.qlo : g.qw, NL > 0 ? (size_t)(g.K / 32) * g.N * 4 : 4);
   const __amdgpu_buffer_rsrc_t rz = make_rsrc(g.zeros, (size_t)(g.K / 32 / g.upg) * g.N * 2);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(g.scales, (size_t)(g.K / 32 / g.upg) * g.N * 2);
 
-  // A loader: rows a_row + 32 i (clamped to M - 1: rows beyond M only feed
-  // outputs that are never stored), 8 halves at column chunk a_chk.
+  // A (activations) go through LDS: rows a_row + (THREADS / 8) i, clamped to
+  // M - 1 (rows beyond M only feed outputs that are never stored), 8 halves
+  // at column chunk a_chk.
   const int a_row = tid >> 3, a_chk = tid & 7;
-  uint32_t a_voff[8];  // byte offsets into x
+  uint32_t a_voff[CA];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) a_voff[i] = (uint32_t)(min(m0 + a_row + 32 * i, g.M - 1) * g.K + 8 * a_chk) * 2u;
-  // B loader: one column per thread (clamped to N - 1 likewise).
-  const int b_col = min(n0 + tid, g.N - 1);
-  const uint32_t b_voff = (uint32_t)b_col * 4u;
+  for (int i = 0; i < CA; ++i)
+    a_voff[i] = (uint32_t)(min(m0 + a_row + (THREADS / 8) * i, g.M - 1) * g.K + 8 * a_chk) * 2u;
 
-  auto loadA = [&](u32x4 (&SA)[8], int ks_in) {
+  // B (weights) go straight to registers: each lane reads the words of its
+  // fragments. Columns beyond N are clamped to N - 1 (never stored).
+  uint32_t b_voff[TN];
+#pragma unroll
+  for (int t = 0; t < TN; ++t) b_voff[t] = (uint32_t)min(n0 + (BN / WN) * wn + 32 * t + (lane & 31), g.N - 1) * 4u;
+
+  auto loadA = [&](u32x4 (&SA)[CA], int ks_in) {
     const int ks = min(ks_in, nk - 1);  // slabs past the end reload the last one (never used)
     // Chunks past the end of K (second half of the last slab when K % 64 != 0)
     // read the chunk 32 halves before instead; they are zeroed when stored.
     const uint32_t adj = (KTAIL && ks * BK + 8 * a_chk >= g.K) ? 64u : 0u;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) SA[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, a_voff[i] - adj, ks * BK * 2, 0);
+    for (int i = 0; i < CA; ++i) SA[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, a_voff[i] - adj, ks * BK * 2, 0);
   };
-  auto loadB = [&](SB& S, int ks_in) {
-    const int ks = min(ks_in, nk - 1);
-    const int row0 = ks * (BK / EPS);
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      // word rows past the end of K read row 0 instead (zeroed when stored)
-      const int row = (!KTAIL || (row0 + r) * EPS < g.K) ? row0 + r : 0;
-      S.w[r] = __builtin_amdgcn_raw_buffer_load_b32(rw, b_voff, row * g.N * 4, kNonTemporal);
-    }
-    if constexpr (RLO > 0) {
-      const int lrow0 = ks * (BK / 32);
-#pragma unroll
-      for (int r = 0; r < RLO; ++r) {
-        const int row = (!KTAIL || (lrow0 + r) * 32 < g.K) ? lrow0 + r : 0;
-        S.l[r] = __builtin_amdgcn_raw_buffer_load_b32(rl, b_voff, row * g.N * 4, kNonTemporal);
-      }
-    }
-    if constexpr (!POST_SCALE) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int u = min(ks * 2 + h, g.K / 32 - 1);
-        const int grp = g.upg_log2 >= 0 ? (u >> g.upg_log2) : u / g.upg;
-        S.z[h] = __builtin_amdgcn_raw_buffer_load_b16(rz, (uint32_t)b_col * 2u, grp * g.N * 2, 0);
-        S.s[h] = __builtin_amdgcn_raw_buffer_load_b16(rs, (uint32_t)b_col * 2u, grp * g.N * 2, 0);
-      }
-    }
-  };
-
-  // Zero point of this thread's column when there is one group per column.
-  f16x2 zneg = f16x2{0, 0};
-  if constexpr (POST_SCALE) {
-    const f16 z = __builtin_bit_cast(f16, g.zeros[b_col]);
-    zneg = f16x2{(f16)-z, (f16)-z};
-  }
-
-  auto storeA = [&](const u32x4 (&SA)[8], int buf, int ks) {
-    f16* A = lds + buf * (BM + BN) * LDK;
+  auto storeA = [&](const u32x4 (&SA)[CA], int buf, int ks) {
+    f16* A = lds + buf * BM * LDK;
     const bool tail = KTAIL && (ks * BK + 32 >= g.K);  // only the first 32-k half is inside K
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < CA; ++i) {
       u32x4 v = SA[i];
       if (KTAIL && tail && a_chk >= 4) v = u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(A + (a_row + 32 * i) * LDK + 8 * a_chk) = v;
+      *reinterpret_cast<u32x4*>(A + (a_row + (THREADS / 8) * i) * LDK + 8 * a_chk) = v;
     }
   };
-  auto storeB = [&](const SB& S, int buf, int ks) {
-    f16* B = lds + buf * (BM + BN) * LDK + BM * LDK;
-    const bool tail = KTAIL && (ks * BK + 32 >= g.K);
-    const f16x2 m1024 = f16x2{(f16)(-1024.f), (f16)(-1024.f)};
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      uint32_t h[4], d[4];
-      codes8<BITS>(S.w, S.l, c, h);
-      if constexpr (POST_SCALE) {
-#pragma unroll
-        for (int p = 0; p < 4; ++p) d[p] = as_u32((as_f16x2(h[p]) + m1024) + zneg);
-      } else {
-        const f16 zh = __builtin_bit_cast(f16, S.z[c >> 2]);
-        const f16 sh = __builtin_bit_cast(f16, S.s[c >> 2]);
-        const f16x2 zz = f16x2{(f16)-zh, (f16)-zh}, ss = f16x2{sh, sh};
-#pragma unroll
-        for (int p = 0; p < 4; ++p) d[p] = as_u32(((as_f16x2(h[p]) + m1024) + zz) * ss);
-      }
-      u32x4 v = u32x4{d[0], d[1], d[2], d[3]};
-      if (KTAIL && tail && c >= 4) v = u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(B + tid * LDK + 8 * c) = v;
-    }
-  };
-
   auto frag_a = [&](int buf, int s, int t) {
-    const f16* A = lds + buf * (BM + BN) * LDK;
-    return *reinterpret_cast<const f16x8*>(A + (128 * wm + 16 * t + i16) * LDK + 32 * s + 8 * j4);
-  };
-  auto frag_b = [&](int buf, int s, int t) {
-    const f16* B = lds + buf * (BM + BN) * LDK + BM * LDK;
-    return *reinterpret_cast<const f16x8*>(B + (128 * wn + 16 * t + i16) * LDK + 32 * s + 8 * j4);
+    const f16* A = lds + buf * BM * LDK;
+    return *reinterpret_cast<const f16x8*>(A + ((BM / WM) * wm + 32 * t + (lane & 31)) * LDK + 16 * s + 8 * kc);
   };
 
-  f32x4 acc[8][8];
+  // Weight words of one k-step for all TN tiles, plus the step's zero point
+  // and scale (the pre-scaled path) per tile.
+  struct BStep {
+    uint32_t w[TN][NW];
+    uint32_t l[TN][NL > 0 ? NL : 1];
+  };
+  auto loadB = [&](BStep& S, int ks_in, int s) {
+    const int ks = min(ks_in, nk - 1);
+    const bool past = KTAIL && ks * BK + 16 * s >= g.K;  // this step is past the end of K: read row 0
 #pragma unroll
-  for (int a = 0; a < 8; ++a)
+    for (int t = 0; t < TN; ++t) {
 #pragma unroll
-    for (int b = 0; b < 8; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int w = 0; w < NW; ++w) {
+        // kc is a lane property: it goes in the per-lane offset
+        const int row0 = past ? 0 : frag_row<BITS>(ks, s, 0, w);
+        const uint32_t kcoff = (BITS == 8 ? 2u * kc : (BITS == 4 ? (uint32_t)kc : 0u)) * (uint32_t)g.N * 4u;
+        S.w[t][w] = __builtin_amdgcn_raw_buffer_load_b32(rw, b_voff[t] + (past ? 0u : kcoff), row0 * g.N * 4, kNonTemporal);
+      }
+      if constexpr (NL > 0) {
+        const int lrow = past ? 0 : ks * 2 + (s >> 1);
+        S.l[t][0] = __builtin_amdgcn_raw_buffer_load_b32(rl, b_voff[t], lrow * g.N * 4, kNonTemporal);
+      }
+    }
+  };
+  // Zero points and scales of this lane's TN columns: once (one group per
+  // column) or per 32-k unit.
+  struct ZS {
+    uint16_t z[TN][NG], s[TN][NG];
+  };
+  auto loadZS = [&](ZS& Z, int ks_in) {
+    const int ks = min(ks_in, nk - 1);
+#pragma unroll
+    for (int h = 0; h < NG; ++h) {
+      const int u = POST_SCALE ? 0 : min(ks * 2 + h, g.K / 32 - 1);
+      const int grp = POST_SCALE ? 0 : (g.upg_log2 >= 0 ? (u >> g.upg_log2) : u / g.upg);
+#pragma unroll
+      for (int t = 0; t < TN; ++t) {
+        Z.z[t][h] = __builtin_amdgcn_raw_buffer_load_b16(rz, b_voff[t] / 2u, grp * g.N * 2, 0);
+        Z.s[t][h] = __builtin_amdgcn_raw_buffer_load_b16(rs, b_voff[t] / 2u, grp * g.N * 2, 0);
+      }
+    }
+  };
+  auto frag_b = [&](const BStep& S, const ZS& Z, int t, int s, bool zero) {
+    uint32_t h[4], d[4];
+    frag_codes<BITS>(S.w[t], S.l[t], kc, s, h);
+    const f16x2 m1024 = f16x2{(f16)(-1024.f), (f16)(-1024.f)};
+    const f16 zh = __builtin_bit_cast(f16, Z.z[t][POST_SCALE ? 0 : (s >> 1)]);
+    const f16x2 zz = f16x2{(f16)-zh, (f16)-zh};
+    if constexpr (POST_SCALE) {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) d[p] = as_u32((as_f16x2(h[p]) + m1024) + zz);
+    } else {
+      const f16 sh = __builtin_bit_cast(f16, Z.s[t][s >> 1]);
+      const f16x2 ss = f16x2{sh, sh};
+#pragma unroll
+      for (int p = 0; p < 4; ++p) d[p] = as_u32(((as_f16x2(h[p]) + m1024) + zz) * ss);
+    }
+    if (KTAIL && zero) d[0] = d[1] = d[2] = d[3] = 0u;
+    return __builtin_bit_cast(f16x8, u32x4{d[0], d[1], d[2], d[3]});
+  };
 
-  u32x4 SA[8];
-  SB Pn1, Pn2;  // weight words of the next slab and of the one after it
-  f16x8 bf[8], af;
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int a = 0; a < TM; ++a)
+#pragma unroll
+    for (int b = 0; b < TN; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+
+  u32x4 SA[CA];
+  BStep Bc[4], Bn[4];  // weight words of the current and of the next slab, per k-step
+  ZS Zc, Zn;
+  f16x8 fa[TM], fa_next[TM];
 
   loadA(SA, 0);
-  loadB(Pn1, 0);
-  loadB(Pn2, 1);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) loadB(Bc[s], 0, s);
+  loadZS(Zc, 0);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) loadB(Bn[s], 1, s);
+  loadZS(Zn, 1);
   storeA(SA, 0, 0);
-  storeB(Pn1, 0, 0);
-  Pn1 = Pn2;
-  loadB(Pn2, 2);
   __syncthreads();
-  af = frag_a(0, 0, 0);
 #pragma unroll
-  for (int b = 0; b < 8; ++b) bf[b] = frag_b(0, 0, b);
+  for (int t = 0; t < TM; ++t) fa[t] = frag_a(0, 0, t);
 
-  // One slab per iteration: two sub-steps of 64 MFMAs each.
+  // One 64-k slab per iteration: four 16-k steps of TM x TN MFMAs. A
+  // fragments of the next step are read from LDS while the current step's
+  // MFMAs run; the weight words of each step are dequantized in registers and
+  // that register set is refilled with the same step of the slab after next.
+  // Activation slabs rotate through three LDS buffers: slab ks + 1 is stored
+  // during step 2 into a buffer last read two slabs ago, and the one barrier
+  // per slab sits before step 3, so the first fragments of the next slab are
+  // read while step 3's MFMAs run.
   for (int ks = 0; ks < nk; ++ks) {
-    const int cur = ks & 1;
+    const int cur = ks % 3, nxt = (ks + 1) % 3;
     loadA(SA, ks + 1);
-    // sub-step 0; A fragments are read one ahead of their MFMAs
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const f16x8 a_now = af;
-      af = frag_a(cur, t < 7 ? 0 : 1, t < 7 ? t + 1 : 0);
+    for (int s = 0; s < 4; ++s) {
+      // Scheduling fence: each step's instructions stay in their step.
+      __builtin_amdgcn_sched_barrier(0);
+      if (s == 3) __syncthreads();  // slab ks + 1 is in LDS
 #pragma unroll
-      for (int b = 0; b < 8; ++b) acc[t][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_now, bf[b], acc[t][b], 0, 0, 0);
+      for (int t = 0; t < TM; ++t) fa_next[t] = s < 3 ? frag_a(cur, s + 1, t) : frag_a(nxt, 0, t);
+      const bool past = KTAIL && ks * BK + 16 * s >= g.K;
+      f16x8 fb[TN];
+#pragma unroll
+      for (int t = 0; t < TN; ++t) fb[t] = frag_b(Bc[s], Zc, t, s, past);
+      Bc[s] = Bn[s];
+      loadB(Bn[s], ks + 2, s);
+      if (s == 3) {
+        Zc = Zn;
+        loadZS(Zn, ks + 2);
+      }
+      if (s == 2) storeA(SA, nxt, ks + 1);
+#pragma unroll
+      for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int b = 0; b < TN; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[a], fb[b], acc[a][b], 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < TM; ++t) fa[t] = fa_next[t];
     }
-    // the activation loads of the next slab go out first
-    __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 8, 0);
-#pragma unroll
-    for (int b = 0; b < 8; ++b) bf[b] = frag_b(cur, 1, b);
-    // sub-step 1, staging the next slab in the other buffer under it and
-    // requesting the weight words of the slab after the next
-    storeB(Pn1, cur ^ 1, ks + 1);
-    Pn1 = Pn2;
-    loadB(Pn2, ks + 3);
-    storeA(SA, cur ^ 1, ks + 1);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const f16x8 a_now = af;
-      if (t < 7) af = frag_a(cur, 1, t + 1);
-#pragma unroll
-      for (int b = 0; b < 8; ++b) acc[t][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_now, bf[b], acc[t][b], 0, 0, 0);
-    }
-    __syncthreads();
-    af = frag_a(cur ^ 1, 0, 0);
-#pragma unroll
-    for (int b = 0; b < 8; ++b) bf[b] = frag_b(cur ^ 1, 0, b);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // Epilogue: scale (one group per column), round to fp16, stage the tile in
-  // LDS, then write rows with 16-byte stores.
+  // LDS, then write rows with 16-byte stores. Accumulator register r of a
+  // 32 x 32 tile holds row 8 (r / 4) + 4 (lane / 32) + r % 4, column lane % 32.
   __syncthreads();
 #pragma unroll
-  for (int b = 0; b < 8; ++b) {
-    const int col = 128 * wn + 16 * b + i16;
-    float s = 1.f;
-    if constexpr (POST_SCALE) s = half_bits_to_float(g.scales[min(n0 + col, g.N - 1)]);
+  for (int b = 0; b < TN; ++b) {
+    const int col = (BN / WN) * wn + 32 * b + (lane & 31);
+    float sc = 1.f;
+    if constexpr (POST_SCALE) sc = half_bits_to_float(g.scales[min(n0 + col, g.N - 1)]);
 #pragma unroll
-    for (int a = 0; a < 8; ++a)
+    for (int a = 0; a < TM; ++a)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) lds[(128 * wm + 16 * a + 4 * j4 + r) * LDY + col] = (f16)(acc[a][b][r] * s);
+      for (int r = 0; r < 16; ++r)
+        lds[((BM / WM) * wm + 32 * a + 8 * (r >> 2) + 4 * kc + (r & 3)) * LDY + col] = (f16)(acc[a][b][r] * sc);
   }
   __syncthreads();
 #pragma unroll 4
-  for (int c = tid; c < BM * (BN / 8); c += kThreads) {
+  for (int c = tid; c < BM * (BN / 8); c += THREADS) {
     const int row = c / (BN / 8), chunk = c - row * (BN / 8);
     const int gr = m0 + row, gc = n0 + 8 * chunk;
     if (gr < g.M && gc < g.N)
@@ -328,16 +344,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   }
 }
 
-template <int BITS>
-hipError_t launch_bits(const GemmArgs& a, hipStream_t s) {
+template <int BITS, int WM, int WN>
+hipError_t launch_waves(const GemmArgs& a, hipStream_t s) {
   const int nblocks = a.mblocks * a.nblocks;
   const bool post = a.upg * 32 == a.K;
   const bool tail = a.K % BK != 0;
-  if (post && !tail) gemm_kernel<BITS, true, false><<<nblocks, kThreads, 0, s>>>(a);
-  else if (post) gemm_kernel<BITS, true, true><<<nblocks, kThreads, 0, s>>>(a);
-  else if (!tail) gemm_kernel<BITS, false, false><<<nblocks, kThreads, 0, s>>>(a);
-  else gemm_kernel<BITS, false, true><<<nblocks, kThreads, 0, s>>>(a);
+  constexpr int T = 64 * WM * WN;
+  if (post && !tail) gemm_kernel<BITS, true, false, WM, WN><<<nblocks, T, 0, s>>>(a);
+  else if (post) gemm_kernel<BITS, true, true, WM, WN><<<nblocks, T, 0, s>>>(a);
+  else if (!tail) gemm_kernel<BITS, false, false, WM, WN><<<nblocks, T, 0, s>>>(a);
+  else gemm_kernel<BITS, false, true, WM, WN><<<nblocks, T, 0, s>>>(a);
   return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t launch_bits(const GemmArgs& a, hipStream_t s) {
+  return launch_waves<BITS, 2, 4>(a, s);  // 8 waves: 2 along M x 4 along N
 }
 
 }  // namespace

@@ -47,6 +47,7 @@ namespace {
 
 constexpr int kMaxM = 16;
 constexpr int kMaxSplit = 16;  // blocks along K per column strip
+constexpr int kCUs = 256;      // compute units of an MI355X
 // Arrival counters live in a fixed header at the start of the workspace, one
 // per column strip, and partial sums start after it. The header never
 // overlaps any call's partial sums, so counters left at zero by one call are
@@ -62,8 +63,15 @@ template <> struct Bits<2> { static constexpr int NW = 1; };
 template <> struct Bits<3> { static constexpr int NW = 2; };
 
 template <int VEC> struct Vec;
+template <> struct Vec<1> { typedef uint32_t T; };
 template <> struct Vec<2> { typedef u32x2 T; };
 template <> struct Vec<4> { typedef u32x4 T; };
+
+template <int VEC>
+__device__ __forceinline__ uint32_t word_at(typename Vec<VEC>::T w, int v) {
+  if constexpr (VEC == 1) return w;
+  else return w[v];
+}
 
 template <int VEC>
 __device__ __forceinline__ typename Vec<VEC>::T load_words(const uint32_t* p) {
@@ -145,6 +153,7 @@ template <int BITS, int VEC, int WAVES> constexpr int chunk_units() {
 
 // Fp16 scale/zero values of a lane's VEC columns, as loaded.
 template <int VEC> struct Halves;
+template <> struct Halves<1> { typedef uint16_t T; };
 template <> struct Halves<2> { typedef uint32_t T; };
 template <> struct Halves<4> { typedef u32x2 T; };
 template <int VEC>
@@ -153,7 +162,8 @@ __device__ __forceinline__ typename Halves<VEC>::T load_halves(const uint16_t* p
 }
 template <int VEC>
 __device__ __forceinline__ uint16_t half_at(typename Halves<VEC>::T h, int v) {
-  if constexpr (VEC == 2) return (uint16_t)(h >> (16 * v));
+  if constexpr (VEC == 1) return h;
+  else if constexpr (VEC == 2) return (uint16_t)(h >> (16 * v));
   else return (uint16_t)(h[v >> 1] >> (16 * (v & 1)));
 }
 
@@ -285,7 +295,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs g) {
 #pragma unroll
       for (int v = 0; v < VEC; ++v) {
         uint32_t b[4];
-        decode8<BITS>(wv[c][0][v], NW > 1 ? wv[c][NW - 1][v] : 0u, j, b);
+        decode8<BITS>(word_at<VEC>(wv[c][0], v), NW > 1 ? word_at<VEC>(wv[c][NW - 1], v) : 0u, j, b);
         uint32_t d[4];
         if constexpr (FAST) {
 #pragma unroll
@@ -418,6 +428,7 @@ hipError_t launch_typed(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
 
 template <int BITS>
 hipError_t launch_bits(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
+  if (p.vec == 1) return p.waves == 16 ? launch_typed<BITS, 1, 16>(p, a, s) : launch_typed<BITS, 1, 8>(p, a, s);
   if (p.waves == 16) return p.vec == 2 ? launch_typed<BITS, 2, 16>(p, a, s) : launch_typed<BITS, 4, 16>(p, a, s);
   if (p.waves == 8) return p.vec == 2 ? launch_typed<BITS, 2, 8>(p, a, s) : launch_typed<BITS, 4, 8>(p, a, s);
   return p.vec == 2 ? launch_typed<BITS, 2, 4>(p, a, s) : launch_typed<BITS, 4, 4>(p, a, s);
@@ -426,15 +437,23 @@ hipError_t launch_bits(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
 }  // namespace
 
 GemvPlan gemv_plan(int M, int K, int N, int bits, int group_size) {
-  (void)bits;
   GemvPlan p{};
-  p.vec = QMM_GEMV_VEC != 0 ? QMM_GEMV_VEC : 2;
-  p.strip_cols = 16 * p.vec;
+  // Narrowest column strip whose blocks fit in one round on the 256 CUs
+  // (16, 32 or 64 columns per wave). Every block then covers a strip with
+  // 16 waves splitting K; blocks along K are added only when the strips
+  // alone leave too few waves in flight.
+  int vec = 4;
+  if ((N + 15) / 16 <= kCUs) vec = 1;
+  else if ((N + 31) / 32 <= kCUs) vec = 2;
+  if (QMM_GEMV_VEC != 0) vec = QMM_GEMV_VEC;
+  p.vec = vec;
+  p.strip_cols = 16 * vec;
   p.nstrips = (N + p.strip_cols - 1) / p.strip_cols;
-  // Wide problems: one block of 16 waves per strip splits K inside the block
-  // (no hand-over between blocks); narrow ones add blocks along K.
-  p.waves = QMM_GEMV_WAVES != 0 ? QMM_GEMV_WAVES : (p.nstrips >= 96 ? 16 : 4);
   const int U = K / 32;
+  // 16 waves per block, except where two words per lane per unit (3-bit,
+  // 8-bit) at 4 columns per lane need more registers than 16 waves allow.
+  p.waves = (vec == 4 && (bits == 3 || bits == 8)) ? 8 : 16;
+  if (QMM_GEMV_WAVES != 0) p.waves = QMM_GEMV_WAVES;
   const long long per_split = (long long)p.nstrips * p.waves;
   int ks = (int)((QMM_GEMV_TARGET_WAVES + per_split - 1) / per_split);
   int max_ks = U / p.waves;  // at least one unit per wave
