@@ -242,10 +242,14 @@ def main():
     ap.add_argument("--no-gemm", action="store_true")
     ap.add_argument("--only", choices=("gemv", "gemm"), default=None,
                     help="run one product only and print its own line (for profiling runs)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after the products, run 4 plain device copies of MIB MiB each (outside every timed "
+                         "region) so that a counter profile can scale FETCH_SIZE / WRITE_SIZE by a copy of "
+                         "known size")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (no sharding, no collectives); "
+        print("bench.py measures one GPU: the library has no multi-GPU path (no sharding, no collectives); "
               "run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
@@ -257,7 +261,27 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     w.library()  # fails loudly if the HIP library is missing
+    try:
+        run(args, torch, datagen, w)
+    finally:
+        if args.copy_calibration > 0:
+            copy_calibration(torch, args.copy_calibration)
 
+
+def copy_calibration(torch, mib: int):
+    """Four device-to-device copies of `mib` MiB: a reference kernel whose HBM bytes are known exactly."""
+    n = mib * 1024 * 1024
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n, "copies": 4}),
+          flush=True)
+
+
+def run(args, torch, datagen, w):
     if args.only == "gemm":
         gm = bench_gemm(w, torch, datagen, args.gemm_steps, args.gemm_warmup)
         print(json.dumps({"workload": gm["wl"].name, "ms_per_step": round(gm["ms_per_step"], 4),
@@ -294,7 +318,7 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": committed_traffic("gemv"),
-            "kernel": "gemv_kernel<4,4>", "mean_launch_us": round(gv["mean_launch_us"], 3),
+            "kernel": "gemv_kernel, 4-bit instance", "mean_launch_us": round(gv["mean_launch_us"], 3),
             "median_launch_us": round(gv["median_launch_us"], 3),
         },
     }
@@ -307,7 +331,7 @@ def main():
             "ms_per_step": round(gm["ms_per_step"], 4), "pct_of_fp16_dense_peak": round(100 * tflops / FP16_DENSE_PEAK_TFLOPS, 2),
             "roofline": {"bound": "mfma", "achieved": round(k_tflops, 2), "peak": FP16_DENSE_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(k_tflops / FP16_DENSE_PEAK_TFLOPS, 4),
-                         "traffic": committed_traffic("gemm"), "kernel": "gemm_kernel<8,true>",
+                         "traffic": committed_traffic("gemm"), "kernel": "gemm_kernel, 8-bit post-scale instance",
                          "mean_launch_ms": round(gm["mean_launch_ms"], 4)},
         }
     if not args.no_cpu_baseline:

@@ -41,6 +41,9 @@
 #ifndef QMM_GEMV_WAVES
 #define QMM_GEMV_WAVES 0  // 0: chosen per shape
 #endif
+#ifndef QMM_GEMV_XCD_REMAP
+#define QMM_GEMV_XCD_REMAP 1
+#endif
 
 namespace qmm {
 namespace {
@@ -231,7 +234,12 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs g) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int j = lane >> 4;       // lane group: which 8 k of a unit
   const int cl = lane & 15;      // column group within the wave
-  const int strip = blockIdx.x;
+  // Workgroups are dealt to the 8 XCDs round-robin by linear id, and each
+  // XCD has its own L2. Narrow strips share 128-byte lines with their
+  // neighbours, so each XCD is given a contiguous run of strips: a line is
+  // then fetched into one L2 only.
+  int strip = blockIdx.x;
+  if (QMM_GEMV_XCD_REMAP && (gridDim.x & 7) == 0) strip = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
   const int split = blockIdx.y;
   const int n0 = strip * COLS;
   const int nc = n0 + VEC * cl;  // first of this lane's VEC columns
