@@ -170,6 +170,29 @@ def test_non_integer_zero_points(gpu, path, bits):
 
 
 @pytest.mark.parametrize("path", ["gemv", "gemm"])
+@pytest.mark.parametrize("M,K,N,bits", [(70, 512, 800, 8), (300, 288, 800, 4), (260, 1024, 776, 2), (40, 544, 784, 3)])
+def test_one_group_zero_points_mixed(gpu, path, M, K, N, bits):
+    """group_size -1 with column blocks of integer zero points, non-integer ones, and integers above 1024
+    (where 1024 + z is not an fp16 integer of spacing 1). K = 288 and 544 leave a tail of a 64-row slab."""
+    if path == "gemv":
+        M = min(M, 16)
+    _say(f"{path} one-group mixed zeros M={M} K={K} N={N} bits={bits}")
+    d = datagen.small_case(M, K, N, bits, -1, seed=K + N + bits)
+    rng = np.random.default_rng(bits + 7)
+    z = d["zeros"].astype(np.float64)
+    z[:, 256:512] = rng.uniform(-2.0, (1 << bits) + 2.0, size=(1, 256))
+    z[:, 512:640] = rng.integers(1025, 1100, size=(1, 128))
+    z[:, 640:] = rng.uniform(1024.0, 1030.0, size=(1, N - 640))
+    d["zeros"] = z.astype(np.float16)
+    qw_ref, qlo_ref = oracle.pack(d["codes"], bits)
+    g = _to_gpu_case(d)
+    qw, qlo = _pack_gpu(gpu, d["codes"], bits)
+    y = _product(gpu, path, g["x"], qw, qlo, g["zeros"], g["scales"], bits, -1)
+    y_ref, a = oracle.quantized_matmul(d["x"], qw_ref, qlo_ref, d["zeros"], d["scales"], bits, -1)
+    _check(y.cpu().numpy(), y_ref, a, f"{path} one-group mixed zeros")
+
+
+@pytest.mark.parametrize("path", ["gemv", "gemm"])
 @pytest.mark.parametrize("bits,gs", [(2, 32), (3, 64), (4, 128), (8, -1), (4, 32)])
 def test_one_hot_rows_bit_exact(gpu, path, bits, gs):
     """x = e_k gives y = fp16(w[k, :]); probes every word slot and the first and last k of each group."""

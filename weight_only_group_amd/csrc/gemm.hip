@@ -6,31 +6,33 @@
 // dequantization is fused into the product instead of materialising W).
 //
 // Design:
-//  * Block tile 256 x 256, K in slabs of 64; 4 waves in a 2 x 2 arrangement,
-//    each wave a 128 x 128 sub-tile of 8 x 8 V_MFMA_F32_16X16X32_F16
-//    accumulators (256 fp32 accumulation registers per lane).
-//  * Both operands are staged in LDS as fp16 with k contiguous: A[m][k] and
-//    B[n][k], row pitch 72 halves, so the 16-byte fragment reads of 8 lanes
-//    touch 32 distinct banks. Two LDS buffers alternate between slabs.
-//  * Global loads run two slabs ahead into two register sets, so a slab's
-//    latency is covered by two slabs of matrix-core work.
-//  * Packed words are dequantized once per block on their way into LDS: each
-//    thread owns one column of the slab (64 codes), turns codes into halves
-//    with the 1024.0 mantissa trick (byte permute for 8-bit) and subtracts
-//    1024, then the zero point (exact for integer zero points). With one
-//    group per column
-//    (group_size -1) the scale is applied to the fp32 accumulator in the
-//    epilogue; otherwise each half is multiplied by its group's scale before
-//    it is stored (one fp16 rounding).
-//  * Each 64-k slab is two 32-k sub-steps. A fragments are read from LDS one
-//    step ahead of their MFMAs; during the second sub-step the next slab is
-//    dequantized into the other LDS buffer and the weights of the slab after
-//    it are requested from memory. The activation loads of the next slab are
-//    pinned to the start of the slab so their latency is covered.
+//  * Block tile 256 x 256, K in slabs of 64; 8 waves in a 2 (M) x 4 (N)
+//    arrangement, each wave a 128 x 64 sub-tile of 4 x 2
+//    V_MFMA_F32_32X32X16_F16 accumulators (128 fp32 registers per lane).
+//  * Activations go through LDS (row pitch 72 halves, so the 16-byte
+//    fragment reads of a wave spread over all banks): three buffers rotate,
+//    the next slab is stored during the third 16-k step of the current one,
+//    and one barrier per slab suffices.
+//  * Weights never touch LDS. Each lane loads exactly the packed words of its
+//    own B fragments (32 adjacent columns of one word row per half wave:
+//    128-byte segments) with buffer loads two slabs ahead, and dequantizes
+//    them in registers right before the MFMAs that use them.
+//  * Dequantization: codes are ORed into the mantissa of 1024.0 (a byte
+//    permute for 8-bit) and the zero point is subtracted in fp16. With one
+//    group per column, one packed add of c = -(1024 + z) rounded to fp16
+//    subtracts z rounded to an integer (for |z| < 1024; exactly); the
+//    remainder (zero for integer zero points) is removed in the epilogue with
+//    the row sums of x, and the scale is applied to the fp32 accumulator. With smaller groups each half
+//    is (q - z) * scale in fp16 (one rounding of an exact difference).
+//  * Register sets of two slabs in flight and of the A fragments of two steps
+//    are indexed by compile-time parity (two slabs per loop iteration), so no
+//    registers are copied between sets.
 //  * The epilogue stages the fp16 tile through LDS and writes rows with
 //    16-byte stores.
 //  * Block ids are remapped so that each of the 8 XCDs (own L2 each) works on
 //    a contiguous run of tiles that share weight and activation panels.
+#include <type_traits>
+
 #include "common.h"
 
 namespace qmm {
@@ -236,20 +238,31 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs g) {
       }
     }
   };
-  auto frag_b = [&](const BStep& S, const ZS& Z, int t, int s, bool zero) {
+  // One group per column: c = -(1024 + z) rounded to fp16, per column. For
+  // |z| < 1024 it is an integer, and 1024 + q + c = q - round(z) exactly, so
+  // codes dequantize with one packed add. The remainder z - round(z) (zero
+  // for integer zero points) is taken out in the epilogue.
+  f16x2 zc[TN];
+  auto frag_b = [&](auto fast_tag, const BStep& S, const ZS& Z, int t, int s, bool zero) {
+    constexpr bool FAST = decltype(fast_tag)::value;
     uint32_t h[4], d[4];
     frag_codes<BITS>(S.w[t], S.l[t], kc, s, h);
-    const f16x2 m1024 = f16x2{(f16)(-1024.f), (f16)(-1024.f)};
-    const f16 zh = __builtin_bit_cast(f16, Z.z[t][POST_SCALE ? 0 : (s >> 1)]);
-    const f16x2 zz = f16x2{(f16)-zh, (f16)-zh};
-    if constexpr (POST_SCALE) {
+    if constexpr (FAST) {
 #pragma unroll
-      for (int p = 0; p < 4; ++p) d[p] = as_u32((as_f16x2(h[p]) + m1024) + zz);
+      for (int p = 0; p < 4; ++p) d[p] = as_u32(as_f16x2(h[p]) + zc[t]);
     } else {
-      const f16 sh = __builtin_bit_cast(f16, Z.s[t][s >> 1]);
-      const f16x2 ss = f16x2{sh, sh};
+      const f16x2 m1024 = f16x2{(f16)(-1024.f), (f16)(-1024.f)};
+      const f16 zh = __builtin_bit_cast(f16, Z.z[t][POST_SCALE ? 0 : (s >> 1)]);
+      const f16x2 zz = f16x2{(f16)-zh, (f16)-zh};
+      if constexpr (POST_SCALE) {
 #pragma unroll
-      for (int p = 0; p < 4; ++p) d[p] = as_u32(((as_f16x2(h[p]) + m1024) + zz) * ss);
+        for (int p = 0; p < 4; ++p) d[p] = as_u32((as_f16x2(h[p]) + m1024) + zz);
+      } else {
+        const f16 sh = __builtin_bit_cast(f16, Z.s[t][s >> 1]);
+        const f16x2 ss = f16x2{sh, sh};
+#pragma unroll
+        for (int p = 0; p < 4; ++p) d[p] = as_u32(((as_f16x2(h[p]) + m1024) + zz) * ss);
+      }
     }
     if (KTAIL && zero) d[0] = d[1] = d[2] = d[3] = 0u;
     return __builtin_bit_cast(f16x8, u32x4{d[0], d[1], d[2], d[3]});
@@ -263,32 +276,23 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
+  // Register sets: weight words and zero/scale values of two slabs in flight
+  // (slab ks uses set ks % 2 and refills it with slab ks + 2), and the A
+  // fragments of the current and next 16-k step (set s % 2). Indices are
+  // compile-time constants throughout, so nothing is copied between sets.
   u32x4 SA[CA];
-  BStep Bc[4], Bn[4];  // weight words of the current and of the next slab, per k-step
-  ZS Zc, Zn;
-  f16x8 fa[TM], fa_next[TM];
+  BStep B0[4], B1[4];
+  ZS Z0, Z1;
+  f16x8 fa[2][TM];
 
-  loadA(SA, 0);
-#pragma unroll
-  for (int s = 0; s < 4; ++s) loadB(Bc[s], 0, s);
-  loadZS(Zc, 0);
-#pragma unroll
-  for (int s = 0; s < 4; ++s) loadB(Bn[s], 1, s);
-  loadZS(Zn, 1);
-  storeA(SA, 0, 0);
-  __syncthreads();
-#pragma unroll
-  for (int t = 0; t < TM; ++t) fa[t] = frag_a(0, 0, t);
-
-  // One 64-k slab per iteration: four 16-k steps of TM x TN MFMAs. A
-  // fragments of the next step are read from LDS while the current step's
-  // MFMAs run; the weight words of each step are dequantized in registers and
-  // that register set is refilled with the same step of the slab after next.
-  // Activation slabs rotate through three LDS buffers: slab ks + 1 is stored
-  // during step 2 into a buffer last read two slabs ago, and the one barrier
-  // per slab sits before step 3, so the first fragments of the next slab are
-  // read while step 3's MFMAs run.
-  for (int ks = 0; ks < nk; ++ks) {
+  // One 64-k slab: four 16-k steps of TM x TN MFMAs. A fragments of the next
+  // step are read from LDS while the current step's MFMAs run; each step's
+  // weight words are dequantized in registers and their registers refilled
+  // with the same step of slab ks + 2. Activation slabs rotate through three
+  // LDS buffers: slab ks + 1 is stored during step 2 into a buffer last read
+  // two slabs ago, and the one barrier per slab sits before step 3, so the
+  // first fragments of the next slab are read while step 3's MFMAs run.
+  auto slab = [&](auto fast_tag, int ks, BStep (&B)[4], ZS& Z) __attribute__((always_inline)) {
     const int cur = ks % 3, nxt = (ks + 1) % 3;
     loadA(SA, ks + 1);
 #pragma unroll
@@ -297,32 +301,96 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs g) {
       __builtin_amdgcn_sched_barrier(0);
       if (s == 3) __syncthreads();  // slab ks + 1 is in LDS
 #pragma unroll
-      for (int t = 0; t < TM; ++t) fa_next[t] = s < 3 ? frag_a(cur, s + 1, t) : frag_a(nxt, 0, t);
+      for (int t = 0; t < TM; ++t) fa[(s + 1) & 1][t] = s < 3 ? frag_a(cur, s + 1, t) : frag_a(nxt, 0, t);
       const bool past = KTAIL && ks * BK + 16 * s >= g.K;
       f16x8 fb[TN];
 #pragma unroll
-      for (int t = 0; t < TN; ++t) fb[t] = frag_b(Bc[s], Zc, t, s, past);
-      Bc[s] = Bn[s];
-      loadB(Bn[s], ks + 2, s);
-      if (s == 3) {
-        Zc = Zn;
-        loadZS(Zn, ks + 2);
-      }
+      for (int t = 0; t < TN; ++t) fb[t] = frag_b(fast_tag, B[s], Z, t, s, past);
+      loadB(B[s], ks + 2, s);
+      if (!POST_SCALE && s == 3) loadZS(Z, ks + 2);
       if (s == 2) storeA(SA, nxt, ks + 1);
 #pragma unroll
       for (int a = 0; a < TM; ++a)
 #pragma unroll
-        for (int b = 0; b < TN; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[a], fb[b], acc[a][b], 0, 0, 0);
-#pragma unroll
-      for (int t = 0; t < TM; ++t) fa[t] = fa_next[t];
+        for (int b = 0; b < TN; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[s & 1][a], fb[b], acc[a][b], 0, 0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
+  };
+  auto run = [&](auto fast_tag) __attribute__((always_inline)) {
+    int ks = 0;
+    for (; ks + 1 < nk; ks += 2) {
+      slab(fast_tag, ks, B0, Z0);
+      slab(fast_tag, ks + 1, B1, POST_SCALE ? Z0 : Z1);
+    }
+    if (ks < nk) slab(fast_tag, ks, B0, Z0);
+  };
+
+  loadA(SA, 0);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) loadB(B0[s], 0, s);
+  loadZS(Z0, 0);  // with one group per column: the only zero/scale load
+#pragma unroll
+  for (int s = 0; s < 4; ++s) loadB(B1[s], 1, s);
+  if (!POST_SCALE) loadZS(Z1, 1);
+  storeA(SA, 0, 0);
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < TM; ++t) fa[0][t] = frag_a(0, 0, t);
+
+  if constexpr (POST_SCALE) {
+#pragma unroll
+    for (int t = 0; t < TN; ++t) {
+      const f16 c = (f16)((f16)(-1024.f) - __builtin_bit_cast(f16, Z0.z[t][0]));
+      zc[t] = f16x2{c, c};
+    }
+  }
+  run(std::integral_constant<bool, POST_SCALE>{});
+
+  // Accumulator register r of a 32 x 32 tile holds row 8 (r / 4) + 4 (lane / 32)
+  // + r % 4, column lane % 32.
+  auto acc_row = [&](int a, int r) { return (BM / WM) * wm + 32 * a + 8 * (r >> 2) + 4 * kc + (r & 3); };
+
+  // One group per column: the loop subtracted c = -(1024 + z) rounded, so
+  // acc = sum_k x (q - z) + delta * sum_k x with delta = z + 1024 + c (exact in
+  // fp32). Blocks with a column whose delta is not zero (a zero point that is
+  // not an integer) subtract delta times the row sums of x, computed here in
+  // a fixed order. The barrier below also ends every read of the slab buffers.
+  bool off = false;
+  float delta[TN];
+#pragma unroll
+  for (int t = 0; t < TN; ++t) {
+    delta[t] = 0.f;
+    if constexpr (POST_SCALE) delta[t] = (half_bits_to_float(Z0.z[t][0]) + 1024.f) + (float)zc[t].x;
+    off = off || delta[t] != 0.f;
+  }
+  if (__syncthreads_or(off)) {
+    float* rsum = reinterpret_cast<float*>(lds);
+    for (int row = tid >> 3; row < BM; row += THREADS / 8) {
+      const uint16_t* xr = g.x + (size_t)min(m0 + row, g.M - 1) * g.K;
+      float sum = 0.f;
+      for (int k = 8 * (tid & 7); k < g.K; k += 64) {
+        const f16x8 v = *reinterpret_cast<const f16x8*>(xr + k);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sum += (float)v[e];
+      }
+      sum += __shfl_xor(sum, 1);
+      sum += __shfl_xor(sum, 2);
+      sum += __shfl_xor(sum, 4);
+      if ((tid & 7) == 0) rsum[row] = sum;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+      for (int b = 0; b < TN; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[a][b][r] -= delta[b] * rsum[acc_row(a, r)];
+    __syncthreads();
   }
 
   // Epilogue: scale (one group per column), round to fp16, stage the tile in
-  // LDS, then write rows with 16-byte stores. Accumulator register r of a
-  // 32 x 32 tile holds row 8 (r / 4) + 4 (lane / 32) + r % 4, column lane % 32.
-  __syncthreads();
+  // LDS, then write rows with 16-byte stores.
 #pragma unroll
   for (int b = 0; b < TN; ++b) {
     const int col = (BN / WN) * wn + 32 * b + (lane & 31);
@@ -332,7 +400,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs g) {
     for (int a = 0; a < TM; ++a)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        lds[((BM / WM) * wm + 32 * a + 8 * (r >> 2) + 4 * kc + (r & 3)) * LDY + col] = (f16)(acc[a][b][r] * sc);
+        lds[acc_row(a, r) * LDY + col] = (f16)(acc[a][b][r] * sc);
   }
   __syncthreads();
 #pragma unroll 4
