@@ -23,6 +23,9 @@ The JSON line also carries:
   cpu_baseline  the CPU oracle on the same workload on this host
   gemm          the prefill product M=2048, K=4096, N=14336, 8-bit, one group
                 per column: TFLOP/s against the 2.5 PFLOP/s fp16 dense peak
+  floors        reference kernels timed the same way: an empty kernel as a
+                graph node, a plain streaming read of the decode product's
+                byte count (cold), a long streaming read, a dense MFMA loop
 """
 from __future__ import annotations
 
@@ -184,6 +187,67 @@ def bench_gemm(w, torch, datagen, steps: int, warmup: int):
             "flops": flops, "bytes": algorithmic_bytes(wl), "d": d}
 
 
+def floors(torch, gemv_bytes: int):
+    """Reference kernels from libqmm_probes.so, timed like the products: the dispatch floor of a
+    graph node, a plain streaming read of the decode product's byte count (cold, best of a few
+    launch shapes), a long streaming read, and a dense MFMA loop."""
+    import ctypes
+    path = os.path.join(ROOT, "weight_only_group_amd", "libqmm_probes.so")
+    lib = ctypes.CDLL(path)
+    lib.qmm_probe_empty.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.qmm_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                   ctypes.c_void_p]
+    lib.qmm_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device=dev)
+    nbytes = gemv_bytes // 256 * 256
+    R = max(1, math.ceil(COLD_BYTES / nbytes))
+    buf = torch.empty(R * nbytes, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+
+    def graph_us(fn, n=400):
+        fn(0, torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            sp = torch.cuda.current_stream().cuda_stream
+            for i in range(n):
+                fn(i, sp)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    def ok(st):
+        if st != 0:
+            raise RuntimeError(f"probe failed with status {st}")
+
+    out = {}
+    out["empty_kernel_graph_node_us"] = round(graph_us(lambda i, sp: ok(lib.qmm_probe_empty(256, 1024, sp))), 3)
+    best = None
+    for blocks, threads in ((256, 1024), (512, 1024), (1024, 512), (2048, 256)):
+        us = graph_us(lambda i, sp: ok(lib.qmm_probe_read(buf.data_ptr() + (i % R) * nbytes, nbytes, blocks, threads,
+                                                          sink.data_ptr(), sp)))
+        if best is None or us < best[0]:
+            best = (us, blocks, threads)
+    out["read_same_bytes_as_decode"] = {"bytes": nbytes, "us": round(best[0], 3),
+                                        "GB/s": round(nbytes / best[0] / 1e3, 1), "blocks": best[1],
+                                        "threads": best[2], "cold": True}
+    big = R * nbytes
+    us = graph_us(lambda i, sp: ok(lib.qmm_probe_read(buf.data_ptr(), big, 8192, 512, sink.data_ptr(), sp)), n=20)
+    out["read_long"] = {"bytes": big, "us": round(us, 1), "GB/s": round(big / us / 1e3, 1)}
+    iters, blocks = 4000, 1024
+    us = graph_us(lambda i, sp: ok(lib.qmm_probe_mfma(blocks, iters, sink.data_ptr(), sp)), n=5)
+    flops = blocks * 4 * 4 * iters * 2.0 * 32 * 32 * 16
+    out["mfma_32x32x16_f16"] = {"TFLOP/s": round(flops / us / 1e6, 1), "blocks": blocks, "iters": iters}
+    del buf
+    return out
+
+
 def cpu_baseline_gemv(datagen, d, seconds: float):
     import oracle
     wl = datagen.WORKLOADS[datagen.HEADLINE_GEMV]
@@ -226,6 +290,8 @@ def main():
     ap.add_argument("--cpu-gemm-rows", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemm", action="store_true")
+    ap.add_argument("--no-floors", action="store_true", help="skip the reference kernels (empty launch, "
+                    "streaming read, MFMA loop)")
     ap.add_argument("--only", choices=("gemv", "gemm"), default=None,
                     help="run one product only and print its own line (for profiling runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -319,6 +385,8 @@ def run(args, torch, datagen, w):
                          "traffic": committed_traffic("gemm"), "kernel": "gemm_kernel, 8-bit post-scale instance",
                          "mean_launch_ms": round(gm["mean_launch_ms"], 4)},
         }
+    if not args.no_floors:
+        out["floors"] = floors(torch, gv["bytes"])
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_gemv(datagen, gv["d"], args.cpu_seconds)
         if not args.no_gemm:

@@ -17,6 +17,10 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 SOURCES = ("api.hip", "pack.hip", "gemv.hip", "gemm.hip")
 LIB_NAME = "libqmm.so"
+# Reference kernels for measurement (empty launch, streaming read, MFMA loop);
+# a library of their own, outside the qmm ABI.
+PROBE_SOURCES = ("probes.hip",)
+PROBE_LIB_NAME = "libqmm_probes.so"
 ARCH = "gfx950"
 
 
@@ -39,10 +43,8 @@ def compile_flags(defines=()) -> list[str]:
     return flags
 
 
-def build(out: str | None = None, defines=(), verbose: bool = False, jobs: int = 4) -> str:
-    """Compile every source and link the shared library; returns its path."""
+def _compile_and_link(sources, out: str, defines, verbose: bool, jobs: int) -> str:
     cc = hipcc()
-    out = out or os.path.join(HERE, LIB_NAME)
     tag = "default" if not defines else "_".join(str(d).replace("=", "-") for d in defines)
     objdir = os.path.join(HERE, "_build", tag)
     os.makedirs(objdir, exist_ok=True)
@@ -59,7 +61,7 @@ def build(out: str | None = None, defines=(), verbose: bool = False, jobs: int =
         return obj
 
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(one, SOURCES))
+        objs = list(ex.map(one, sources))
     tmp = out + ".tmp"
     cmd = [cc, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -69,6 +71,16 @@ def build(out: str | None = None, defines=(), verbose: bool = False, jobs: int =
     if verbose:
         print(f"built {out}")
     return out
+
+
+def build(out: str | None = None, defines=(), verbose: bool = False, jobs: int = 4) -> str:
+    """Compile every source and link libqmm.so (and, for the default build, the
+    measurement probes library); returns the path of libqmm.so."""
+    default = out is None and not defines
+    path = _compile_and_link(SOURCES, out or os.path.join(HERE, LIB_NAME), defines, verbose, jobs)
+    if default:
+        _compile_and_link(PROBE_SOURCES, os.path.join(HERE, PROBE_LIB_NAME), (), verbose, jobs)
+    return path
 
 
 if __name__ == "__main__":

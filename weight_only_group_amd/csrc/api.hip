@@ -51,6 +51,13 @@ qmm_status check_product(const uint16_t* x, int M, int K, const int32_t* qweight
     if (group_size <= 0 || group_size % 32 || K % group_size)
       return fail(QMM_ERR_GROUP, "group_size=%d must be -1 or a positive multiple of 32 dividing K=%d", group_size, K);
   }
+  // Kernels address x, the packed planes, scales and zero points with 32-bit
+  // byte offsets.
+  const unsigned long long lim = 1ull << 32;
+  const unsigned long long groups = group_size == -1 ? 1ull : (unsigned long long)(K / group_size);
+  if ((unsigned long long)M * K * 2 >= lim || (unsigned long long)K * N * (bits == 3 ? 2 : bits) / 8 >= lim ||
+      groups * N * 2 >= lim)
+    return fail(QMM_ERR_SHAPE, "x, qweight, zeros and scales must each be smaller than 4 GiB");
   if (!x || !qweight || !zeros || !scales || !y) return fail(QMM_ERR_NULL, "a required pointer is NULL");
   if (bits == 3 && !qweight_lo) return fail(QMM_ERR_NULL, "qweight_lo (1-bit plane) is NULL for 3-bit codes");
   if (!aligned16(x) || !aligned16(qweight) || !aligned16(zeros) || !aligned16(scales) || !aligned16(y) ||
@@ -119,6 +126,9 @@ qmm_status qmm_gemv(const uint16_t* x, int M, int K, const int32_t* qweight, con
   if (st != QMM_OK) return st;
   if (N > qmm::kGemvMaxN) return fail(QMM_ERR_SHAPE, "N=%d exceeds the decode product's limit of %d", N, qmm::kGemvMaxN);
   const qmm::GemvPlan plan = qmm::gemv_plan(M, K, N, bits, group_size);
+  if (!plan.valid)
+    return fail(QMM_ERR_SHAPE, "M=%d, K=%d, group_size=%d exceed the decode product's staging limits; use qmm_gemm",
+                M, K, group_size);
   if (plan.workspace_bytes > 0) {
     if (!workspace) return fail(QMM_ERR_WORKSPACE, "workspace is NULL but %zu bytes are needed", plan.workspace_bytes);
     if (workspace_bytes < plan.workspace_bytes)

@@ -30,8 +30,9 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t b) {
 inline int group_rows(int K, int group_size) { return group_size == -1 ? K : group_size; }
 
 // ---- decode GEMV (small M) ----------------------------------------------
-// Column strips of the decode product are at least 32 columns wide; the
-// workspace header has one arrival counter per strip.
+// The workspace header has one arrival counter per column strip. Strips are
+// 32 or 64 columns wide whenever there are more than 256 of them, so this
+// covers every N up to the limit.
 constexpr int kGemvMaxN = 1 << 20;
 constexpr int kGemvMaxStrips = kGemvMaxN / 32;
 struct GemvPlan {
@@ -43,8 +44,11 @@ struct GemvPlan {
   int units_per_block;  // 32-row units of K per block
   int upg;          // 32-row units per group
   int upg_log2;     // log2(upg) if upg is a power of two, else -1
+  int ubp_log2;     // log2 of the activation slots staged per row and lane group
+  int gp_log2;      // log2 of the rows of scales / zero points staged per block
   size_t counters_bytes;  // arrival counters (one per strip), padded
   size_t workspace_bytes; // counters + split-K partial sums
+  int valid;        // 0: the shape does not fit the decode product's staging limits
 };
 GemvPlan gemv_plan(int M, int K, int N, int bits, int group_size);
 hipError_t launch_gemv(const GemvPlan& p, const uint16_t* x, int M, int K, const uint32_t* qw,

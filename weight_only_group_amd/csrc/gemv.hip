@@ -9,19 +9,23 @@
 // replaces the rest:
 //
 //  * A wave owns 16 * VEC adjacent columns. Lane l loads VEC adjacent words of
-//    one word row (one 8- or 16-byte load; a wave row segment is 128 or 256
-//    contiguous bytes) with a non-temporal hint, since weights are streamed
-//    once.
+//    one word row with a non-temporal buffer load (the row offset of a unit is
+//    a scalar), since weights are streamed once.
+//  * A block first requests its activations (already in the operand order of
+//    the matrix cores, per row, unit and lane group) and its rows of scales
+//    and zero points, then every wave requests its weight words. Loads
+//    complete in order, so the block waits for the first two only, puts them
+//    in LDS, and each unit is computed as soon as its own weight words arrive.
 //  * Codes become halves with one AND-OR into the mantissa of 1024.0 (exact),
 //    then one packed subtract of (1024 + zero) when the zero point is an
 //    integer (exact), else two subtracts.
 //  * The multiply-accumulate runs on the matrix cores: V_MFMA_F32_16X16X32_F16
-//    with x as the 16 x 32 A operand (rows >= M are zero) and the dequantized
-//    codes as the 32 x 16 B operand. Lane group j = l / 16 of the wave feeds
-//    8 of the 32 k values of a "unit" (32 consecutive k), so a unit never
-//    straddles a group (group_size % 32 == 0) and the fp32 accumulator of a
-//    group is multiplied by that group's scale once (exact dequantized values
-//    up to the scale product).
+//    with x as the 16 x 32 A operand (rows >= M repeat row 0 and are never
+//    stored) and the dequantized codes as the 32 x 16 B operand. Lane group
+//    j = l / 16 of the wave feeds 8 of the 32 k values of a "unit" (32
+//    consecutive k), so a unit never straddles a group (group_size % 32 == 0)
+//    and the fp32 accumulator of a group is multiplied by that group's scale
+//    once (exact dequantized values up to the scale product).
 //  * Waves of a block take consecutive K ranges of the same column strip and
 //    are summed through LDS in wave order. Blocks along K write fp32 partial
 //    sums; the last block of a strip to arrive (an atomic ticket) adds the
@@ -74,20 +78,6 @@ template <int VEC>
 __device__ __forceinline__ uint32_t word_at(typename Vec<VEC>::T w, int v) {
   if constexpr (VEC == 1) return w;
   else return w[v];
-}
-
-template <int VEC>
-__device__ __forceinline__ typename Vec<VEC>::T load_words(const uint32_t* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const typename Vec<VEC>::T*>(p));
-}
-
-// Row (in its plane) of word w of unit u for lane group j.
-template <int BITS>
-__device__ __forceinline__ int word_row(int u, int j, int w) {
-  if constexpr (BITS == 4) return 4 * u + j;
-  else if constexpr (BITS == 8) return 8 * u + 2 * j + w;
-  else if constexpr (BITS == 2) return 2 * u + (j >> 1);
-  else return w == 0 ? 2 * u + (j >> 1) : u;  // 3-bit: plane2 row, plane1 row
 }
 
 // Four fp16 pairs 1024 + q for the 8 codes lane group j takes from its
@@ -146,6 +136,8 @@ struct GemvArgs {
   int upg_log2;  // log2(upg) when upg is a power of two, else -1
   int units_per_block;
   int ksplit;
+  int ubp_log2;  // log2 of the activation slots per row and lane group (>= units_per_block)
+  int gp_log2;   // log2 of the rows of scales / zero points staged per block
 };
 
 // Units (32 rows of K) per batch of loads issued together, bounded by the
@@ -154,15 +146,11 @@ template <int BITS, int VEC, int WAVES> constexpr int chunk_units() {
   return (Bits<BITS>::NW * VEC <= (WAVES >= 8 ? 2 : 4)) ? 8 : 4;
 }
 
-// Fp16 scale/zero values of a lane's VEC columns, as loaded.
+// Fp16 scale/zero values of a lane's VEC columns, as read from LDS.
 template <int VEC> struct Halves;
 template <> struct Halves<1> { typedef uint16_t T; };
 template <> struct Halves<2> { typedef uint32_t T; };
 template <> struct Halves<4> { typedef u32x2 T; };
-template <int VEC>
-__device__ __forceinline__ typename Halves<VEC>::T load_halves(const uint16_t* p) {
-  return *reinterpret_cast<const typename Halves<VEC>::T*>(p);
-}
 template <int VEC>
 __device__ __forceinline__ uint16_t half_at(typename Halves<VEC>::T h, int v) {
   if constexpr (VEC == 1) return h;
@@ -170,15 +158,33 @@ __device__ __forceinline__ uint16_t half_at(typename Halves<VEC>::T h, int v) {
   else return (uint16_t)(h[v >> 1] >> (16 * (v & 1)));
 }
 
-// Raw activation bytes of one unit for lane group j: 16 halves' worth of
-// registers, permuted into decode8's element order when used.
+// First k (within a unit) of the activations lane group j feeds: 8 consecutive
+// k for 4- and 8-bit codes; for 2- and 3-bit codes two runs of 4, 8 apart.
+template <int BITS> __device__ __forceinline__ int x_first(int j) {
+  return (BITS == 4 || BITS == 8) ? 8 * j : 16 * (j >> 1) + 4 * (j & 1);
+}
+
+// A raw buffer resource over `bytes` bytes at p (out-of-range reads return 0).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)(uint32_t)bytes, 0x00020000);
+}
+constexpr int kNonTemporal = 2;  // buffer-load cache policy: streamed data
+
+template <int VEC>
+__device__ __forceinline__ typename Vec<VEC>::T load_words(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  if constexpr (VEC == 1) return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kNonTemporal);
+  else if constexpr (VEC == 2) return __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kNonTemporal);
+  else return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kNonTemporal);
+}
+
+// Raw activation bytes of one (row, unit, lane group) slot: 8 halves.
 template <int BITS>
-__device__ __forceinline__ u32x4 load_x_raw(const uint16_t* ubase, uint32_t off) {
+__device__ __forceinline__ u32x4 load_x_slot(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   if constexpr (BITS == 4 || BITS == 8) {
-    return *reinterpret_cast<const u32x4*>(ubase + off);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
   } else {
-    const u32x2 e = *reinterpret_cast<const u32x2*>(ubase + off);
-    const u32x2 f = *reinterpret_cast<const u32x2*>(ubase + off + 8);
+    const u32x2 e = __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0);
+    const u32x2 f = __builtin_amdgcn_raw_buffer_load_b64(r, byte_off + 16, 0, 0);
     return u32x4{e.x, e.y, f.x, f.y};
   }
 }
@@ -186,20 +192,15 @@ __device__ __forceinline__ u32x4 load_x_raw(const uint16_t* ubase, uint32_t off)
 // The A operand (x[m, 32u + k] for the 8 k of lane group j, in decode8's
 // element order) from the raw registers.
 template <int BITS>
-__device__ __forceinline__ f16x8 x_operand(u32x4 d) {
-  uint32_t a0, a1, a2, a3;
+__device__ __forceinline__ u32x4 x_operand(u32x4 d) {
   if constexpr (BITS == 8) {
-    a0 = d.x; a1 = d.y; a2 = d.z; a3 = d.w;
+    return d;
   } else {
     // 4-bit: d = x[0..7], pairs (k, k + 4); 2/3-bit: d = x[o..o+3], x[o+8..o+11], pairs (k, k + 8)
-    const uint32_t lo0 = d.x, lo1 = d.y;
-    const uint32_t hi0 = (BITS == 4) ? d.z : d.z, hi1 = (BITS == 4) ? d.w : d.w;
-    a0 = (lo0 & 0xFFFFu) | (hi0 << 16);
-    a1 = (lo0 >> 16) | (hi0 & 0xFFFF0000u);
-    a2 = (lo1 & 0xFFFFu) | (hi1 << 16);
-    a3 = (lo1 >> 16) | (hi1 & 0xFFFF0000u);
+    const uint32_t lo0 = d.x, lo1 = d.y, hi0 = d.z, hi1 = d.w;
+    return u32x4{__builtin_amdgcn_perm(hi0, lo0, 0x05040100u), __builtin_amdgcn_perm(hi0, lo0, 0x07060302u),
+                 __builtin_amdgcn_perm(hi1, lo1, 0x05040100u), __builtin_amdgcn_perm(hi1, lo1, 0x07060302u)};
   }
-  return pack8(a0, a1, a2, a3);
 }
 
 // Word-row offset of lane group j's first word of plane w within a unit, and
@@ -219,21 +220,32 @@ __device__ __forceinline__ int unit_rows(int w) {
   else return w == 0 ? 2 : 1;
 }
 
+// LDS of a block: staged activations and scales / zero points (5 KiB per
+// wave: 80 KiB for 16 waves, so that blocks of fewer waves can share a CU),
+// and apart from them the per-wave partial sums.
+constexpr int stage_bytes(int waves) { return waves * 5 * 1024; }
+constexpr int kXPerThread = 4;  // activation slots one thread stages at most
+
 template <int BITS, int VEC, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs g) {
   constexpr int NW = Bits<BITS>::NW;
   constexpr int CH = chunk_units<BITS, VEC, WAVES>();
   constexpr int COLS = 16 * VEC;
+  constexpr int CP = COLS / 8;  // 16-byte pieces per staged row of scales or zero points
+  constexpr int CP_LOG2 = VEC == 1 ? 1 : (VEC == 2 ? 2 : 3);
   constexpr int THREADS = 64 * WAVES;
-  __shared__ float red[WAVES][kMaxM][COLS];
+  __shared__ __attribute__((aligned(16))) unsigned char lds[stage_bytes(WAVES)];
+  __shared__ float red[WAVES * kMaxM * COLS];  // [WAVES][M][COLS]
+  __shared__ int wave_exact[WAVES];
   __shared__ int last_flag;
 
-  const int lane = threadIdx.x & 63;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
   // The wave index is the same for every lane of a wave; saying so keeps all
   // unit bookkeeping below in scalar registers and scalar branches.
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int j = lane >> 4;       // lane group: which 8 k of a unit
-  const int cl = lane & 15;      // column group within the wave
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = lane >> 4;   // lane group: which 8 k of a unit
+  const int cl = lane & 15;  // column group within the wave
   // Workgroups are dealt to the 8 XCDs round-robin by linear id, and each
   // XCD has its own L2. Narrow strips share 128-byte lines with their
   // neighbours, so each XCD is given a contiguous run of strips: a line is
@@ -243,142 +255,198 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs g) {
   const int split = blockIdx.y;
   const int n0 = strip * COLS;
   const int nc = n0 + VEC * cl;  // first of this lane's VEC columns
-  const bool col_ok = nc < g.N;
-  const int ncc = col_ok ? nc : 0;  // clamped: every load below is in bounds
+  const int ncc = nc < g.N ? nc : 0;  // clamped: every load below is in bounds
   // A-operand row of this lane. Rows >= M read row 0: those MFMA rows only
-  // produce outputs that are never stored, so they need no zeroing.
+  // produce outputs that are never stored.
   const int m = cl < g.M ? cl : 0;
 
   const int U = g.K / 32;
   const int ub0 = split * g.units_per_block;
   const int ub1 = min(U, ub0 + g.units_per_block);
+  const int nub = ub1 - ub0;
   const int per_wave = (g.units_per_block + WAVES - 1) / WAVES;
   const int ua = min(ub1, ub0 + wave * per_wave);
   const int uz = min(ub1, ua + per_wave);
+  auto group_of = [&](int u) { return g.upg_log2 >= 0 ? (u >> g.upg_log2) : u / g.upg; };
+  const int gb0 = group_of(ub0);
+  const int ngb = group_of(ub1 - 1) - gb0 + 1;  // groups this block touches
+  const int G = U / g.upg;
 
-  // Per-lane parts of every address; the per-unit parts are uniform.
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(g.x, (size_t)g.M * g.K * 2);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(g.qw, (size_t)U * unit_rows<BITS>(0) * g.N * 4);
+  const __amdgpu_buffer_rsrc_t rl = make_rsrc(BITS == 3 ? g.qlo : g.qw, (size_t)U * unit_rows<BITS>(NW - 1) * g.N * 4);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(g.scales, (size_t)G * g.N * 2);
+  const __amdgpu_buffer_rsrc_t rz = make_rsrc(g.zeros, (size_t)G * g.N * 2);
+
+  // ---- 1. staging requests: activation slots (row, unit, lane group) of the
+  // block's K range, and 16-byte pieces of its rows of scales and zero points.
+  const int ubp_log2 = g.ubp_log2;
+  u32x4 xraw[kXPerThread];
+#pragma unroll
+  for (int i = 0; i < kXPerThread; ++i) {
+    const int sl = tid + THREADS * i;
+    const int mm = sl >> (ubp_log2 + 2), uu = (sl >> 2) & ((1 << ubp_log2) - 1), jj = sl & 3;
+    if (mm < g.M && uu < nub)
+      xraw[i] = load_x_slot<BITS>(rx, (uint32_t)(mm * g.K + 32 * (ub0 + uu) + x_first<BITS>(jj)) * 2u);
+  }
+  const int sz_row = tid >> CP_LOG2, sz_cp = tid & (CP - 1);
+  const bool sz_on = sz_row < ngb;
+  u32x4 sraw = u32x4{0u, 0u, 0u, 0u}, zraw = u32x4{0u, 0u, 0u, 0u};
+  if (sz_on) {
+    const uint32_t voff = ((uint32_t)(gb0 + sz_row) * (uint32_t)g.N + (uint32_t)min(n0 + 8 * sz_cp, g.N - 8)) * 2u;
+    sraw = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0);
+    zraw = __builtin_amdgcn_raw_buffer_load_b128(rz, voff, 0, 0);
+  }
+
+  // ---- 2. weight words of the wave's first batch of units (the only stream
+  // from HBM): per lane VEC adjacent columns of one word row per plane. Units
+  // past the wave's range repeat its last unit and are not used.
   uint32_t woff[NW];
 #pragma unroll
-  for (int w = 0; w < NW; ++w) woff[w] = (uint32_t)(lane_row<BITS>(j, w) * g.N + ncc);
-  const uint32_t xoff = (uint32_t)(m * g.K) +
-                        ((BITS == 4 || BITS == 8) ? 8 * j : 16 * (j >> 1) + 4 * (j & 1));
-
-  f32x4 total[VEC], acc[VEC];
-#pragma unroll
-  for (int v = 0; v < VEC; ++v) {
-    total[v] = f32x4{0.f, 0.f, 0.f, 0.f};
-    acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  float sc[VEC];
-  f16x2 zc[VEC];  // -(1024 + z) on the exact path, else -z (1024 removed separately)
-#pragma unroll
-  for (int v = 0; v < VEC; ++v) { sc[v] = 0.f; zc[v] = f16x2{0, 0}; }
-  int zfast = 1;
-  int cur_g = -1;
-
-  for (int base = ua; base < uz; base += CH) {
-    typename Vec<VEC>::T wv[CH][NW];
-    u32x4 xr[CH];
-    typename Halves<VEC>::T sr[CH], zr[CH];
-    // Issue every load of the batch (indices clamped into range) before any
-    // of them is used.
+  for (int w = 0; w < NW; ++w) woff[w] = (uint32_t)(lane_row<BITS>(j, w) * g.N + ncc) * 4u;
+  typename Vec<VEC>::T wv[CH][NW];
+  auto load_batch = [&](int base) {
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      const int u = min(base + c, uz - 1);
+      const int u = min(base + c, uz - 1);  // uz >= 1
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        const uint32_t* plane = (BITS == 3 && w == 1) ? g.qlo : g.qw;
-        const uint32_t* ubase = plane + (size_t)u * unit_rows<BITS>(w) * g.N;
-        wv[c][w] = load_words<VEC>(ubase + woff[w]);
+        const uint32_t soff = (uint32_t)(u * unit_rows<BITS>(w)) * (uint32_t)g.N * 4u;
+        wv[c][w] = load_words<VEC>((BITS == 3 && w == 1) ? rl : rw, woff[w], soff);
       }
-      xr[c] = load_x_raw<BITS>(g.x + 32 * u, xoff);
-      const int grp = g.upg_log2 >= 0 ? (u >> g.upg_log2) : u / g.upg;
-      const size_t gofs = (size_t)grp * g.N;
-      sr[c] = load_halves<VEC>(g.scales + gofs + ncc);
-      zr[c] = load_halves<VEC>(g.zeros + gofs + ncc);
     }
-    auto process = [&](auto fast_tag, int c) {
-      constexpr bool FAST = decltype(fast_tag)::value;
-      const f16x8 A = x_operand<BITS>(xr[c]);
+  };
+  load_batch(ua);
+
+  // ---- 3. staged data into LDS, waiting for the staging requests only. The
+  // barrier also tells every wave whether all of the block's zero points are
+  // integers (|z| <= 1024), for which one packed add dequantizes exactly.
+  u32x4* xs = reinterpret_cast<u32x4*>(lds);
+  const int xs_bytes = g.M << (ubp_log2 + 6);
+  uint16_t* szs = reinterpret_cast<uint16_t*>(lds + xs_bytes);  // [2][1 << gp_log2][COLS]
 #pragma unroll
-      for (int v = 0; v < VEC; ++v) {
-        uint32_t b[4];
-        decode8<BITS>(word_at<VEC>(wv[c][0], v), NW > 1 ? word_at<VEC>(wv[c][NW - 1], v) : 0u, j, b);
-        uint32_t d[4];
-        if constexpr (FAST) {
+  for (int i = 0; i < kXPerThread; ++i) {
+    const int sl = tid + THREADS * i;
+    const int mm = sl >> (ubp_log2 + 2), uu = (sl >> 2) & ((1 << ubp_log2) - 1);
+    if (mm < g.M && uu < nub) xs[sl] = x_operand<BITS>(xraw[i]);
+  }
+  bool exact = true;
+  if (sz_on) {
+    *reinterpret_cast<u32x4*>(szs + sz_row * COLS + 8 * sz_cp) = sraw;
+    *reinterpret_cast<u32x4*>(szs + ((1 << g.gp_log2) + sz_row) * COLS + 8 * sz_cp) = zraw;
 #pragma unroll
-          for (int p = 0; p < 4; ++p) d[p] = as_u32(as_f16x2(b[p]) + zc[v]);
-        } else {
-          const f16x2 m1024 = f16x2{(f16)(-1024.f), (f16)(-1024.f)};
+    for (int e = 0; e < 8; ++e) {
+      const float z = half_bits_to_float((uint16_t)(zraw[e >> 1] >> (16 * (e & 1))));
+      exact = exact && (z == __builtin_rintf(z)) && (__builtin_fabsf(z) <= 1024.f);
+    }
+  }
+  const bool wave_ok = __all(exact);
+  if (lane == 0) wave_exact[wave] = wave_ok;
+  __syncthreads();
+  int all_ok = 1;
 #pragma unroll
-          for (int p = 0; p < 4; ++p) d[p] = as_u32((as_f16x2(b[p]) + m1024) + zc[v]);
-        }
-        acc[v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, pack8(d[0], d[1], d[2], d[3]), acc[v], 0, 0, 0);
-      }
-    };
+  for (int w = 0; w < WAVES; ++w) all_ok &= wave_exact[w];
+  const int zfast = __builtin_amdgcn_readfirstlane(all_ok);
+
+  // ---- 4. the wave's units.
+  f32x4 total[VEC];
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int u = base + c;
-      if (u >= uz) break;  // scalar
-      const int grp = g.upg_log2 >= 0 ? (u >> g.upg_log2) : u / g.upg;
-      if (grp != cur_g) {  // scalar
-        if (cur_g >= 0) {
+  for (int v = 0; v < VEC; ++v) total[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const u32x4* xrow = xs + (m << ubp_log2) * 4 + j;  // slot of unit u: xrow[4 (u - ub0)]
+
+  auto run = [&](auto fast_tag) {
+    constexpr bool FAST = decltype(fast_tag)::value;
+    f32x4 acc[2][VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) acc[0][v] = acc[1][v] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float sc[VEC];
+    f16x2 zc[VEC];  // -(1024 + z) on the exact path, else -z (1024 removed separately)
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) { sc[v] = 0.f; zc[v] = f16x2{0, 0}; }
+    int cur_g = -1;
+    auto chunk = [&](int base) {
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const int u = base + c;
+        if (u >= uz) break;  // scalar
+        const int grp = group_of(u);
+        if (grp != cur_g) {  // scalar
+          if (cur_g >= 0) {
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) {
+              total[v] += sc[v] * (acc[0][v] + acc[1][v]);
+              acc[0][v] = acc[1][v] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+          }
+          cur_g = grp;
+          const uint16_t* srow = szs + (grp - gb0) * COLS + VEC * cl;
+          const typename Halves<VEC>::T sh = *reinterpret_cast<const typename Halves<VEC>::T*>(srow);
+          const typename Halves<VEC>::T zh =
+              *reinterpret_cast<const typename Halves<VEC>::T*>(srow + (COLS << g.gp_log2));
 #pragma unroll
           for (int v = 0; v < VEC; ++v) {
-            total[v] += sc[v] * acc[v];
-            acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+            sc[v] = half_bits_to_float(half_at<VEC>(sh, v));
+            const f16 zf = __builtin_bit_cast(f16, half_at<VEC>(zh, v));
+            // exact on the fast path: integer zero point, |z| <= 1024
+            const f16 t = FAST ? (f16)((f16)(-1024.f) - zf) : (f16)(-zf);
+            zc[v] = f16x2{t, t};
           }
         }
-        cur_g = grp;
-        bool exact = true;
+        const f16x8 A = __builtin_bit_cast(f16x8, xrow[4 * (u - ub0)]);
 #pragma unroll
         for (int v = 0; v < VEC; ++v) {
-          sc[v] = half_bits_to_float(half_at<VEC>(sr[c], v));
-          const uint16_t zb = half_at<VEC>(zr[c], v);
-          const float z = half_bits_to_float(zb);
-          exact = exact && (z == __builtin_rintf(z)) && (__builtin_fabsf(z) <= 1024.f);
-          const f16 zh = __builtin_bit_cast(f16, zb);
-          zc[v] = f16x2{zh, zh};
-        }
-        zfast = __builtin_amdgcn_readfirstlane(__all(exact));
+          uint32_t b[4];
+          decode8<BITS>(word_at<VEC>(wv[c][0], v), NW > 1 ? word_at<VEC>(wv[c][NW - 1], v) : 0u, j, b);
+          uint32_t d[4];
+          if constexpr (FAST) {
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) {
-          // exact when zfast: integer zero point, |z| <= 1024
-          const f16 t = zfast ? (f16)((f16)(-1024.f) - zc[v].x) : (f16)(-zc[v].x);
-          zc[v] = f16x2{t, t};
+            for (int p = 0; p < 4; ++p) d[p] = as_u32(as_f16x2(b[p]) + zc[v]);
+          } else {
+            const f16x2 m1024 = f16x2{(f16)(-1024.f), (f16)(-1024.f)};
+#pragma unroll
+            for (int p = 0; p < 4; ++p) d[p] = as_u32((as_f16x2(b[p]) + m1024) + zc[v]);
+          }
+          acc[c & 1][v] =
+              __builtin_amdgcn_mfma_f32_16x16x32_f16(A, pack8(d[0], d[1], d[2], d[3]), acc[c & 1][v], 0, 0, 0);
         }
       }
-      if (zfast) process(std::integral_constant<bool, true>{}, c);
-      else process(std::integral_constant<bool, false>{}, c);
+    };
+    chunk(ua);  // its words were requested before the staging barrier
+    for (int base = ua + CH; base < uz; base += CH) {
+      load_batch(base);
+      chunk(base);
     }
-  }
-  if (cur_g >= 0) {
+    if (cur_g >= 0) {
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) total[v] += sc[v] * acc[v];
-  }
+      for (int v = 0; v < VEC; ++v) total[v] += sc[v] * (acc[0][v] + acc[1][v]);
+    }
+  };
+  if (zfast) run(std::integral_constant<bool, true>{});
+  else run(std::integral_constant<bool, false>{});
 
+  // ---- 5. the block's waves are summed in wave order.
   // D layout: lane holds rows 4 j + i (i < 4) of column VEC * cl + v.
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = 4 * j + i;
     if (row < g.M) {
 #pragma unroll
-      for (int v = 0; v < VEC; ++v) red[wave][row][VEC * cl + v] = total[v][i];
+      for (int v = 0; v < VEC; ++v) red[(wave * g.M + row) * COLS + VEC * cl + v] = total[v][i];
     }
   }
   __syncthreads();
 
-  // Waves of the block are summed in wave order.
   const int entries = g.M * COLS;
-  if (g.ksplit == 1) {
-    for (int e = threadIdx.x; e < entries; e += THREADS) {
-      const int row = e / COLS, col = e - row * COLS;
-      if (n0 + col < g.N) {
-        float s = red[0][row][col];
+  auto block_sum = [&](int e) {
+    float sum = red[e];
 #pragma unroll
-        for (int w = 1; w < WAVES; ++w) s += red[w][row][col];
-        g.y[(size_t)row * g.N + n0 + col] = __builtin_bit_cast(uint16_t, (f16)s);
-      }
+    for (int w = 1; w < WAVES; ++w) sum += red[w * entries + e];
+    return sum;
+  };
+  if (g.ksplit == 1) {
+    for (int e = tid; e < entries; e += THREADS) {
+      const int row = e / COLS, col = e - row * COLS;
+      if (n0 + col < g.N) g.y[(size_t)row * g.N + n0 + col] = __builtin_bit_cast(uint16_t, (f16)block_sum(e));
     }
     return;
   }
@@ -389,24 +457,20 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs g) {
   // L2; each thread waits until its stores are acknowledged before the block
   // takes its ticket, so the last block to arrive sees every partial.
   float* mypart = g.part + (size_t)split * g.M * g.N;
-  for (int e = threadIdx.x; e < entries; e += THREADS) {
+  for (int e = tid; e < entries; e += THREADS) {
     const int row = e / COLS, col = e - row * COLS;
-    if (n0 + col < g.N) {
-      float s = red[0][row][col];
-#pragma unroll
-      for (int w = 1; w < WAVES; ++w) s += red[w][row][col];
-      __hip_atomic_store(mypart + (size_t)row * g.N + n0 + col, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    if (n0 + col < g.N)
+      __hip_atomic_store(mypart + (size_t)row * g.N + n0 + col, block_sum(e), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) expcnt(0) lgkmcnt(0): stores acknowledged
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     const uint32_t prev = __hip_atomic_fetch_add(&g.counters[strip], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     last_flag = (prev == (uint32_t)(g.ksplit - 1));
   }
   __syncthreads();
   if (!last_flag) return;
-  for (int e = threadIdx.x; e < entries; e += THREADS) {
+  for (int e = tid; e < entries; e += THREADS) {
     const int row = e / COLS, col = e - row * COLS;
     if (n0 + col < g.N) {
       const size_t off = (size_t)row * g.N + n0 + col;
@@ -418,13 +482,13 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs g) {
         const int spc = min(sp, g.ksplit - 1);
         pv[sp] = __hip_atomic_load(g.part + (size_t)spc * g.M * g.N + off, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      float s = pv[0];
+      float sum = pv[0];
 #pragma unroll
-      for (int sp = 1; sp < kMaxSplit; ++sp) s += (sp < g.ksplit) ? pv[sp] : 0.f;
-      g.y[off] = __builtin_bit_cast(uint16_t, (f16)s);
+      for (int sp = 1; sp < kMaxSplit; ++sp) sum += (sp < g.ksplit) ? pv[sp] : 0.f;
+      g.y[off] = __builtin_bit_cast(uint16_t, (f16)sum);
     }
   }
-  if (threadIdx.x == 0) __hip_atomic_store(&g.counters[strip], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) __hip_atomic_store(&g.counters[strip], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int BITS, int VEC, int WAVES>
@@ -442,6 +506,12 @@ hipError_t launch_bits(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
   return p.vec == 2 ? launch_typed<BITS, 2, 4>(p, a, s) : launch_typed<BITS, 4, 4>(p, a, s);
 }
 
+int ceil_log2(int v) {
+  int l = 0;
+  while ((1 << l) < v) ++l;
+  return l;
+}
+
 }  // namespace
 
 GemvPlan gemv_plan(int M, int K, int N, int bits, int group_size) {
@@ -449,7 +519,8 @@ GemvPlan gemv_plan(int M, int K, int N, int bits, int group_size) {
   // Narrowest column strip whose blocks fit in one round on the 256 CUs
   // (16, 32 or 64 columns per wave). Every block then covers a strip with
   // 16 waves splitting K; blocks along K are added only when the strips
-  // alone leave too few waves in flight.
+  // alone leave too few waves in flight, or when a block's activations and
+  // scales / zero points would not fit its staging area.
   int vec = 4;
   if ((N + 15) / 16 <= kCUs) vec = 1;
   else if ((N + 31) / 32 <= kCUs) vec = 2;
@@ -462,27 +533,50 @@ GemvPlan gemv_plan(int M, int K, int N, int bits, int group_size) {
   // 8-bit) at 4 columns per lane need more registers than 16 waves allow.
   p.waves = (vec == 4 && (bits == 3 || bits == 8)) ? 8 : 16;
   if (QMM_GEMV_WAVES != 0) p.waves = QMM_GEMV_WAVES;
+  p.upg = group_rows(K, group_size) / 32;
+  p.upg_log2 = -1;
+  for (int l = 0; l < 31; ++l)
+    if ((1 << l) == p.upg) p.upg_log2 = l;
   const long long per_split = (long long)p.nstrips * p.waves;
   int ks = (int)((QMM_GEMV_TARGET_WAVES + per_split - 1) / per_split);
   int max_ks = U / p.waves;  // at least one unit per wave
   max_ks = max_ks < 1 ? 1 : (max_ks > kMaxSplit ? kMaxSplit : max_ks);
   ks = ks < 1 ? 1 : (ks > max_ks ? max_ks : ks);
-  p.upg = group_rows(K, group_size) / 32;
-  p.upg_log2 = -1;
-  for (int l = 0; l < 31; ++l)
-    if ((1 << l) == p.upg) p.upg_log2 = l;
-  p.units_per_block = (U + ks - 1) / ks;
+  const int threads = 64 * p.waves, cols = p.strip_cols;
+  for (;; ++ks) {
+    if (ks > kMaxSplit) return GemvPlan{};  // no valid plan: valid == 0
+    const int upb = (U + ks - 1) / ks;
+    const int ubp_log2 = ceil_log2(upb);
+    int groups = 0;  // most groups one block touches
+    for (int s = 0; s * upb < U; ++s) {
+      const int u0 = s * upb, u1 = (U < u0 + upb ? U : u0 + upb) - 1;
+      const int gcount = u1 / p.upg - u0 / p.upg + 1;
+      groups = gcount > groups ? gcount : groups;
+    }
+    const int gp_log2 = ceil_log2(groups);
+    const long long x_slots = (long long)M << (ubp_log2 + 2);
+    const long long stage = (x_slots << 4) + (2LL << gp_log2) * cols * 2;
+    if (x_slots <= (long long)kXPerThread * threads && ((long long)(cols / 8) << gp_log2) <= threads &&
+        stage <= stage_bytes(p.waves)) {
+      p.units_per_block = upb;
+      p.ubp_log2 = ubp_log2;
+      p.gp_log2 = gp_log2;
+      break;
+    }
+  }
   p.ksplit = (U + p.units_per_block - 1) / p.units_per_block;
   if (p.ksplit > 1) {
     p.counters_bytes = kCounterHeaderBytes;
     p.workspace_bytes = p.counters_bytes + (size_t)p.ksplit * M * N * sizeof(float);
   }
+  p.valid = 1;
   return p;
 }
 
 hipError_t launch_gemv(const GemvPlan& p, const uint16_t* x, int M, int K, const uint32_t* qw,
                        const uint32_t* qlo, const uint16_t* zeros, const uint16_t* scales, int N,
                        int bits, int group_size, uint16_t* y, void* workspace, hipStream_t s) {
+  if (!p.valid) return hipErrorInvalidValue;
   GemvArgs a;
   a.x = x;
   a.qw = qw;
@@ -499,6 +593,8 @@ hipError_t launch_gemv(const GemvPlan& p, const uint16_t* x, int M, int K, const
   a.upg_log2 = p.upg_log2;
   a.units_per_block = p.units_per_block;
   a.ksplit = p.ksplit;
+  a.ubp_log2 = p.ubp_log2;
+  a.gp_log2 = p.gp_log2;
   switch (bits) {
     case 2: return launch_bits<2>(p, a, s);
     case 3: return launch_bits<3>(p, a, s);
