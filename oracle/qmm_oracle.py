@@ -13,7 +13,8 @@ What it computes, step by step, in the order the sources state it:
   docstring and ``_pack_kmajor`` / ``_unpack_kmajor``.)
 * 3-bit codes are two planes: a 2-bit plane holding ``q >> 1`` and a 1-bit
   plane holding ``q & 1``; ``q = (hi << 1) | lo``. (dashq_kernel.py, module
-  docstring, ``TritonQuantLinear.__init__`` and ``dequantize_weight``.)
+  docstring, ``TritonQuantLinear.__init__`` and ``dequantize_weight``.) Widths
+  1, 2, 3, 4 and 8 are supported (dashq_kernel.py, ``SUPPORTED_NBITS``).
 * Groups: row ``k`` of the weight belongs to group ``k // group_size``;
   ``group_size == -1`` means one group for the whole column.
   (GPTQModel-Compatible Triton Kernel README, "Group Quantization".)
@@ -21,7 +22,11 @@ What it computes, step by step, in the order the sources state it:
   (GPTQModel-Compatible Triton Kernel README, "Dequantization Formula";
   dashq_kernel.py, ``dequantize_weight``.)
 * Product: ``y = x @ w`` with x of shape (M, K). (GPTQModel-Compatible Triton
-  Kernel README, "API Reference", ``gptqmodel_quantized_matmul``.)
+  Kernel README, "API Reference", ``gptqmodel_quantized_matmul``.) An optional
+  bias row is added to every row of y (dashq_kernel.py, ``TritonQuantLinear``:
+  the accumulator starts from the bias).
+* The dequantized weight as fp16 (dashq_kernel.py, ``dequantize_weight``): the
+  exact product rounded once to the nearest half, ties to even.
 
 Arithmetic is float64 throughout. Every fp16 input is widened to float64
 exactly; for the workloads' integer zero points every product ``x * w`` is exact
@@ -39,7 +44,7 @@ import numpy as np
 # Bit widths whose codes pack into one plane of 32-bit words. 3 is handled as
 # two planes (2 + 1); 1 is the width of the low 3-bit plane.
 PLANE_BITS = (1, 2, 4, 8)
-SUPPORTED_BITS = (2, 3, 4, 8)
+SUPPORTED_BITS = (1, 2, 3, 4, 8)
 
 # Element-wise parity rule: |y - y_ref| <= REL_TOL * sum_k |x_k w_kn| + ABS_TOL.
 REL_TOL = 2e-3
@@ -154,28 +159,42 @@ def dequantize(q: np.ndarray, scales: np.ndarray, zeros: np.ndarray, group_size:
     return s[g] * (q.astype(np.float64) - z[g])
 
 
-def matmul(x: np.ndarray, w: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
-    """y = x @ w and the tolerance reference a = sum_k |x_k * w_kn|, both float64."""
+def dequantize_fp16(q: np.ndarray, scales: np.ndarray, zeros: np.ndarray, group_size: int) -> np.ndarray:
+    """(K, N) codes -> (K, N) fp16 weights: the float64 product rounded once to fp16 (nearest, ties to even).
+
+    With fp16 scales and zero points and codes below 256 the float64 product is
+    exact, so this is the correctly rounded fp16 value of s * (q - z).
+    """
+    return dequantize(q, scales, zeros, group_size).astype(np.float16)
+
+
+def matmul(x: np.ndarray, w: np.ndarray, bias: np.ndarray | None = None) -> tuple[np.ndarray, np.ndarray]:
+    """y = x @ w (+ bias) and the tolerance reference a = sum_k |x_k * w_kn| (+ |bias|), both float64."""
     x64 = np.asarray(x).astype(np.float64)
     w64 = np.asarray(w, dtype=np.float64)
-    return x64 @ w64, np.abs(x64) @ np.abs(w64)
+    y, a = x64 @ w64, np.abs(x64) @ np.abs(w64)
+    if bias is not None:
+        b = np.asarray(bias).astype(np.float64).reshape(1, -1)
+        y, a = y + b, a + np.abs(b)
+    return y, a
 
 
-def quantized_matmul(x, qweight, qweight_lo, zeros, scales, bits: int, group_size: int):
-    """Reference for ``y = x @ dequantize(qweight)`` from packed words.
+def quantized_matmul(x, qweight, qweight_lo, zeros, scales, bits: int, group_size: int, bias=None):
+    """Reference for ``y = x @ dequantize(qweight) (+ bias)`` from packed words.
 
     Arguments follow the functional statement of the problem (x, packed weight,
     zeros, scales, bits, group_size); ``qweight_lo`` is the 1-bit plane for
-    3-bit weights. Returns (y, a) in float64, a being the tolerance reference.
+    3-bit weights; ``bias`` is an optional (N,) row. Returns (y, a) in float64,
+    a being the tolerance reference.
     """
     K = np.asarray(x).shape[1]
     q = unpack(qweight, qweight_lo, bits, K)
-    return matmul(x, dequantize(q, scales, zeros, group_size))
+    return matmul(x, dequantize(q, scales, zeros, group_size), bias)
 
 
-def quantized_matmul_codes(x, codes, zeros, scales, group_size: int):
+def quantized_matmul_codes(x, codes, zeros, scales, group_size: int, bias=None):
     """Same product from unpacked codes (skips the packing step)."""
-    return matmul(x, dequantize(codes, scales, zeros, group_size))
+    return matmul(x, dequantize(codes, scales, zeros, group_size), bias)
 
 
 def parity_bound(a: np.ndarray) -> np.ndarray:

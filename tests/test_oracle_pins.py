@@ -110,13 +110,66 @@ def check_dequant_examples_hand_worked():
         s = np.array(case["scales_gn"], dtype=np.float16)
         z = np.array(case["zeros_gn"], dtype=np.float16)
         x = np.array(case["x"], dtype=np.float16)
+        bias = np.array(case["bias_n"], dtype=np.float16) if "bias_n" in case else None
         for gs in case["group_sizes"]:
             w = oracle.dequantize(codes, s, z, gs)
             assert np.array_equal(w, np.array(case["w_kn"], dtype=np.float64)), case["name"]
             qw, qlo = oracle.pack(codes, case["bits"])
-            y, a = oracle.quantized_matmul(x, qw, qlo, z, s, case["bits"], gs)
+            y, a = oracle.quantized_matmul(x, qw, qlo, z, s, case["bits"], gs, bias=bias)
             assert np.array_equal(y, np.array(case["y"])), (case["name"], y)
             assert np.array_equal(a, np.array(case["a"])), (case["name"], a)
+
+
+def check_dequant_fp16_hand_worked():
+    """fp16 weights of tests/golden/dequant_examples.json 'fp16_cases', ties included."""
+    for case in _load("dequant_examples.json")["fp16_cases"]:
+        s = np.array([[int(case["scale_bits"], 16)]], dtype=np.uint16).view(np.float16)
+        z = np.array([[case["zero"]]], dtype=np.float16)
+        q = np.array([[case["q"]]], dtype=np.uint8)
+        assert oracle.dequantize(q, s, z, -1)[0, 0] == case["exact"], case["name"]
+        got = oracle.dequantize_fp16(q, s, z, -1).view(np.uint16)[0, 0]
+        assert got == int(case["fp16_bits"], 16), (case["name"], hex(got))
+
+
+def _round_half_even_fp16(v: Fraction) -> float:
+    """The binary16 value nearest to v (ties to even), from the format's definition: 10 stored
+    fraction bits, exponents -14..15, subnormals below 2^-14, overflow to infinity."""
+    if v == 0:
+        return 0.0
+    sign = -1.0 if v < 0 else 1.0
+    v = abs(v)
+    e = -14
+    while v >= Fraction(2) ** (e + 1) and e < 15:
+        e += 1
+    step = Fraction(2) ** (e - 10)
+    n = v / step
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    out = fl * step
+    if out > 65504:
+        return sign * float("inf")
+    return sign * float(out)
+
+
+def check_dequant_fp16_against_exact_rounding(seed=11):
+    """dequantize_fp16 equals the correctly rounded exact product, non-integer zero points included."""
+    rng = np.random.default_rng(seed)
+    for bits, gs in ((4, 32), (8, -1), (3, 32), (1, 32), (2, 64)):
+        K, N = 64, 12
+        codes = rng.integers(0, 1 << bits, size=(K, N)).astype(np.uint8)
+        G = 1 if gs == -1 else K // gs
+        s = rng.uniform(0.001, 0.3, size=(G, N)).astype(np.float16)
+        z = rng.uniform(-2.0, (1 << bits) + 2.0, size=(G, N)).astype(np.float16)
+        z[:, ::2] = np.round(z[:, ::2])
+        w16 = oracle.dequantize_fp16(codes, s, z, gs)
+        rows = K if gs == -1 else gs
+        for k in range(0, K, 3):
+            for n in range(N):
+                g = k // rows
+                exact = Fraction(float(s[g, n])) * (int(codes[k, n]) - Fraction(float(z[g, n])))
+                assert float(w16[k, n]) == _round_half_even_fp16(exact), (bits, gs, k, n)
 
 
 def _exact_y(x, codes, s, z, gs):
@@ -142,7 +195,7 @@ def _exact_y(x, codes, s, z, gs):
 def check_rational_brute_force(seed=3):
     """Tiny random products, including non-integer zero points, against exact rationals."""
     rng = np.random.default_rng(seed)
-    for bits in (2, 3, 4, 8):
+    for bits in (1, 2, 3, 4, 8):
         for K, gs in ((32, 32), (64, 16), (64, -1), (96, 32)):
             M, N = 2, 3
             codes = rng.integers(0, 1 << bits, size=(K, N), dtype=np.uint8)
@@ -221,13 +274,34 @@ def check_group_minus_one_is_single_group(seed=2):
 
 
 def check_widths_agree_on_small_codes(seed=4):
-    """Codes in [0, 7] packed as 3-bit planes, as 4-bit and as 8-bit give bit-identical products."""
+    """Codes in [0, 7] packed as 3-bit planes, as 4-bit and as 8-bit give bit-identical products;
+    codes in [0, 1] packed at every width (1-bit included) do too."""
     d = datagen.small_case(2, 256, 24, 3, 64, seed=seed)
     ys = []
     for bits in (3, 4, 8):
         qw, qlo = oracle.pack(d["codes"], bits)
         ys.append(oracle.quantized_matmul(d["x"], qw, qlo, d["zeros"], d["scales"], bits, 64)[0])
     assert np.array_equal(ys[0], ys[1]) and np.array_equal(ys[0], ys[2])
+    d1 = datagen.small_case(2, 256, 24, 1, 64, seed=seed + 1)
+    assert d1["codes"].max() <= 1
+    ys = []
+    for bits in (1, 2, 3, 4, 8):
+        qw, qlo = oracle.pack(d1["codes"], bits)
+        ys.append(oracle.quantized_matmul(d1["x"], qw, qlo, d1["zeros"], d1["scales"], bits, 64)[0])
+    assert all(np.array_equal(ys[0], y) for y in ys[1:])
+
+
+def check_bias_row(seed=5):
+    """With x = 0 the product is the bias row exactly; otherwise y(bias) - bias == y (exact small values)."""
+    d = datagen.small_case(3, 64, 16, 4, 32, seed=seed)
+    qw, _ = oracle.pack(d["codes"], 4)
+    b = np.linspace(-2, 2, 16).astype(np.float16)
+    y0, a0 = oracle.quantized_matmul(np.zeros_like(d["x"]), qw, None, d["zeros"], d["scales"], 4, 32, bias=b)
+    assert np.array_equal(y0, np.tile(b.astype(np.float64), (3, 1))) and np.array_equal(a0, np.abs(y0))
+    y, a = oracle.quantized_matmul(d["x"], qw, None, d["zeros"], d["scales"], 4, 32)
+    yb, ab = oracle.quantized_matmul(d["x"], qw, None, d["zeros"], d["scales"], 4, 32, bias=b)
+    assert np.allclose(yb - b.astype(np.float64), y, rtol=0, atol=1e-12)
+    assert np.allclose(ab - np.abs(b.astype(np.float64)), a, rtol=0, atol=1e-12)
 
 
 def check_one_hot_rows(seed=9):
@@ -262,6 +336,7 @@ def check_parity_rule():
 CHECKS = [
     check_pack_words_hand_worked, check_ascending_nibbles, check_word_bijection,
     check_out_of_range_codes_masked, check_three_bit_identity, check_dequant_examples_hand_worked,
+    check_dequant_fp16_hand_worked, check_dequant_fp16_against_exact_rounding, check_bias_row,
     check_rational_brute_force, check_exact_integer_recomputation, check_closed_form_constant_scale_zero,
     check_group_minus_one_is_single_group, check_widths_agree_on_small_codes, check_one_hot_rows,
     check_parity_rule,
@@ -316,16 +391,35 @@ def _mut_dequant_sign(q, scales, zeros, group_size):
     return scales.astype(np.float64)[g] * (zeros.astype(np.float64)[g] - q.astype(np.float64))
 
 
-def _mut_matmul_transposed_x(x, w):
+def _mut_matmul_transposed_x(x, w, bias=None):
     x64 = np.asarray(x).astype(np.float64)
     w64 = np.asarray(w, dtype=np.float64)
     xr = x64[:, ::-1]  # k index reversed
-    return xr @ w64, np.abs(xr) @ np.abs(w64)
+    y, a = xr @ w64, np.abs(xr) @ np.abs(w64)
+    if bias is not None:
+        b = np.asarray(bias).astype(np.float64).reshape(1, -1)
+        y, a = y + b, a + np.abs(b)
+    return y, a
 
 
 def _mut_3bit_planes_swapped(codes):
     q = np.asarray(codes).astype(np.uint8) & 7
     return oracle.pack_kmajor(q & 1, 2), oracle.pack_kmajor(q >> 1, 1)
+
+
+def _mut_matmul_drops_bias(x, w, bias=None):
+    x64 = np.asarray(x).astype(np.float64)
+    w64 = np.asarray(w, dtype=np.float64)
+    return x64 @ w64, np.abs(x64) @ np.abs(w64)
+
+
+def _mut_fp16_truncates(q, scales, zeros, group_size):
+    w = oracle.dequantize(q, scales, zeros, group_size)
+    t = w.astype(np.float16)
+    # round toward zero instead of to nearest
+    over = np.abs(t.astype(np.float64)) > np.abs(w)
+    t[over] = np.nextafter(t[over], np.float16(0))
+    return t
 
 
 MUTATIONS = {
@@ -336,6 +430,8 @@ MUTATIONS = {
     "dequant_sign": ("dequantize", _mut_dequant_sign),
     "matmul_reversed_k": ("matmul", _mut_matmul_transposed_x),
     "three_bit_planes_swapped": ("pack_3bit", _mut_3bit_planes_swapped),
+    "matmul_drops_bias": ("matmul", _mut_matmul_drops_bias),
+    "fp16_truncates": ("dequantize_fp16", _mut_fp16_truncates),
 }
 
 
@@ -352,6 +448,6 @@ def test_planted_mistakes(name, monkeypatch):
             continue  # the slow one adds nothing the others miss here
         try:
             check()
-        except (AssertionError, ValueError, IndexError, TypeError):
+        except (AssertionError, ValueError, IndexError):
             caught.append(check.__name__)
     assert caught, f"planted mistake {name} was not caught by any pin"
