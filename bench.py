@@ -107,7 +107,7 @@ def bench_gemv(w, torch, datagen, steps: int, warmup: int):
     def launch(i: int, stream_ptr: int):
         qw, qlo, z, s = copies[i % R]
         st = lib.qmm_gemv(x.data_ptr(), wl.M, wl.K, qw.data_ptr(), None if qlo is None else qlo.data_ptr(),
-                          z.data_ptr(), s.data_ptr(), wl.N, wl.bits, wl.group_size, y.data_ptr(), ws.data_ptr(),
+                          z.data_ptr(), s.data_ptr(), None, wl.N, wl.bits, wl.group_size, y.data_ptr(), ws.data_ptr(),
                           ws.numel(), stream_ptr)
         if st != 0:
             raise RuntimeError(f"qmm_gemv failed: {lib.qmm_last_error().decode()}")
@@ -162,7 +162,7 @@ def bench_gemm(w, torch, datagen, steps: int, warmup: int):
 
     def launch(i: int):
         qw, z, s = copies[i % R]
-        st = lib.qmm_gemm(x.data_ptr(), wl.M, wl.K, qw.data_ptr(), None, z.data_ptr(), s.data_ptr(), wl.N, wl.bits,
+        st = lib.qmm_gemm(x.data_ptr(), wl.M, wl.K, qw.data_ptr(), None, z.data_ptr(), s.data_ptr(), None, wl.N, wl.bits,
                           wl.group_size, y.data_ptr(), torch.cuda.current_stream().cuda_stream)
         if st != 0:
             raise RuntimeError(f"qmm_gemm failed: {lib.qmm_last_error().decode()}")

@@ -12,7 +12,10 @@
  * weight layout is the K-major packing of dashq_kernel.py (module docstring,
  * _pack_kmajor / _unpack_kmajor): a (K / eps, N) int32 array, eps = 32 / bits,
  * code k of column n in word k / eps at bit offset (k % eps) * bits; 3-bit
- * codes are a 2-bit plane of q >> 1 plus a 1-bit plane of q & 1.
+ * codes are a 2-bit plane of q >> 1 plus a 1-bit plane of q & 1. Widths 1, 2,
+ * 3, 4 and 8 are supported (dashq_kernel.py, SUPPORTED_NBITS). An optional
+ * bias row is added to the fp32 result before its rounding to fp16
+ * (dashq_kernel.py, TritonQuantLinear: the accumulator starts from the bias).
  *
  * Conventions for every entry point:
  *  - Pointers to arrays are DEVICE pointers (memory of the current HIP
@@ -41,12 +44,12 @@
 extern "C" {
 #endif
 
-#define QMM_ABI_VERSION 1
+#define QMM_ABI_VERSION 2
 
 typedef enum qmm_status {
   QMM_OK = 0,
   QMM_ERR_NULL = 1,      /* a required pointer is NULL                              */
-  QMM_ERR_BITS = 2,      /* bits not in {2, 3, 4, 8}                                */
+  QMM_ERR_BITS = 2,      /* bits not in {1, 2, 3, 4, 8}                             */
   QMM_ERR_SHAPE = 3,     /* M, K or N out of range or not a required multiple      */
   QMM_ERR_GROUP = 4,     /* group_size neither -1 nor a positive multiple of 32 dividing K */
   QMM_ERR_ALIGN = 5,     /* a pointer is not 16-byte aligned                        */
@@ -68,7 +71,7 @@ const char* qmm_last_error(void);
  * qmm_pack -- codes (K, N) uint8, row-major -> K-major packed words.
  * Defined by dashq_kernel.py, _pack_kmajor and TritonQuantLinear.__init__
  * (3-bit planes).
- *   bits 2, 4, 8: qweight (K / eps, N) int32, eps = 32 / bits; qweight_lo unused (may be NULL).
+ *   bits 1, 2, 4, 8: qweight (K / eps, N) int32, eps = 32 / bits; qweight_lo unused (may be NULL).
  *   bits 3:       qweight = 2-bit plane of q >> 1, (K / 16, N); qweight_lo = 1-bit
  *                 plane of q & 1, (K / 32, N).
  * Requirements: K % eps == 0 (K % 32 == 0 for 3 bits), N >= 1, K >= 1.
@@ -90,6 +93,23 @@ qmm_status qmm_unpack(const int32_t* qweight, const int32_t* qweight_lo, int K, 
                       uint8_t* codes, hipStream_t stream);
 
 /*
+ * qmm_dequant -- the dequantized weight as fp16, K-major (K, N) row-major:
+ *   w[k, n] = fp16(scale[g, n] * (q[k, n] - zero[g, n])),  g = k / group_size
+ * dashq_kernel.py, TritonQuantLinear.dequantize_weight (the step its batched
+ * path runs before a dense product). The exact product is rounded once to
+ * fp16, nearest even.
+ *   qweight, qweight_lo   packed words as written by qmm_pack (qweight_lo only for 3 bits)
+ *   zeros, scales         (G, N) fp16, G = K / group_size, or 1 if group_size == -1
+ *   w                     (K, N) fp16 output
+ * Requirements: K % 32 == 0, N >= 1, group_size == -1 or (group_size % 32 == 0
+ * and K % group_size == 0). No alignment beyond the element size is needed.
+ */
+qmm_status qmm_dequant(const int32_t* qweight, const int32_t* qweight_lo,
+                       const uint16_t* zeros, const uint16_t* scales,
+                       int K, int N, int bits, int group_size,
+                       uint16_t* w, hipStream_t stream);
+
+/*
  * qmm_workspace_bytes -- device workspace qmm_gemv needs for this problem
  * (0 if it needs none; also 0 for invalid arguments). The workspace holds a
  * fixed 128 KiB header of per-column-strip arrival counters followed by
@@ -107,18 +127,22 @@ size_t qmm_workspace_bytes(int M, int K, int N, int bits, int group_size);
  *   x       (M, K) fp16
  *   qweight, qweight_lo   packed words as written by qmm_pack (qweight_lo only for 3 bits)
  *   zeros, scales         (G, N) fp16, G = K / group_size, or 1 if group_size == -1
+ *   bias    (N,) fp16 or NULL; added to the fp32 result before rounding
  *   y       (M, N) fp16 output, fp32 accumulation, rounded to nearest even
  *   workspace, workspace_bytes   see qmm_workspace_bytes
  * Requirements: K % 32 == 0, N % 8 == 0, N <= 1048576, group_size == -1 or
  * (group_size % 32 == 0 and K % group_size == 0); x, qweight, qweight_lo,
- * zeros, scales, y and workspace 16-byte aligned.
+ * zeros, scales, y and workspace 16-byte aligned; x, each packed plane,
+ * zeros and scales smaller than 4 GiB. Shapes whose activations or scales do
+ * not fit the kernel's on-chip staging (M * K large, e.g. K > 32768 at
+ * M = 16) are rejected with QMM_ERR_SHAPE; qmm_gemm takes them.
  * The summation order is fixed: two calls on the same inputs give the same bits.
  * One zero-filled workspace serves calls of any shape, as long as it is large
  * enough for each and calls sharing it do not overlap in time.
  */
 qmm_status qmm_gemv(const uint16_t* x, int M, int K,
                     const int32_t* qweight, const int32_t* qweight_lo,
-                    const uint16_t* zeros, const uint16_t* scales,
+                    const uint16_t* zeros, const uint16_t* scales, const uint16_t* bias,
                     int N, int bits, int group_size,
                     uint16_t* y, void* workspace, size_t workspace_bytes,
                     hipStream_t stream);
@@ -129,11 +153,12 @@ qmm_status qmm_gemv(const uint16_t* x, int M, int K,
  * with fp32 accumulation. dashq_kernel.py, TritonQuantLinear.forward (batched
  * path: dequantize, then a dense product); GPTQModel-Compatible Triton Kernel
  * README, overview (dequantization fused with the product).
- * Arguments and requirements as for qmm_gemv, without a workspace.
+ * Arguments and requirements as for qmm_gemv (bias included), without a
+ * workspace and without the staging limit.
  */
 qmm_status qmm_gemm(const uint16_t* x, int M, int K,
                     const int32_t* qweight, const int32_t* qweight_lo,
-                    const uint16_t* zeros, const uint16_t* scales,
+                    const uint16_t* zeros, const uint16_t* scales, const uint16_t* bias,
                     int N, int bits, int group_size,
                     uint16_t* y, hipStream_t stream);
 

@@ -31,7 +31,7 @@ def _declared():
 
 def test_header_declares_the_boundary():
     assert _declared() == sorted(
-        ["qmm_abi_version", "qmm_status_string", "qmm_last_error", "qmm_pack", "qmm_unpack",
+        ["qmm_abi_version", "qmm_status_string", "qmm_last_error", "qmm_pack", "qmm_unpack", "qmm_dequant",
          "qmm_workspace_bytes", "qmm_gemv", "qmm_gemm"])
 
 
@@ -49,7 +49,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = _lib()
-    assert lib.qmm_abi_version() == 1
+    assert lib.qmm_abi_version() == 2
     names = [lib.qmm_status_string(i).decode() for i in range(8)]
     assert names == ["QMM_OK", "QMM_ERR_NULL", "QMM_ERR_BITS", "QMM_ERR_SHAPE", "QMM_ERR_GROUP",
                      "QMM_ERR_ALIGN", "QMM_ERR_WORKSPACE", "QMM_ERR_HIP"]
@@ -76,22 +76,23 @@ MIS = 0x10004
 
 
 def _gemv(lib, **kw):
-    a = dict(x=A, M=1, K=256, qw=A, qlo=A, z=A, s=A, N=64, bits=4, gs=128, y=A, ws=A, wsb=1 << 30)
+    a = dict(x=A, M=1, K=256, qw=A, qlo=A, z=A, s=A, b=None, N=64, bits=4, gs=128, y=A, ws=A, wsb=1 << 30)
     a.update(kw)
-    return lib.qmm_gemv(a["x"], a["M"], a["K"], a["qw"], a["qlo"], a["z"], a["s"], a["N"], a["bits"], a["gs"],
-                        a["y"], a["ws"], a["wsb"], None)
+    return lib.qmm_gemv(a["x"], a["M"], a["K"], a["qw"], a["qlo"], a["z"], a["s"], a["b"], a["N"], a["bits"],
+                        a["gs"], a["y"], a["ws"], a["wsb"], None)
 
 
 def _gemm(lib, **kw):
-    a = dict(x=A, M=300, K=256, qw=A, qlo=A, z=A, s=A, N=64, bits=4, gs=128, y=A)
+    a = dict(x=A, M=300, K=256, qw=A, qlo=A, z=A, s=A, b=None, N=64, bits=4, gs=128, y=A)
     a.update(kw)
-    return lib.qmm_gemm(a["x"], a["M"], a["K"], a["qw"], a["qlo"], a["z"], a["s"], a["N"], a["bits"], a["gs"],
-                        a["y"], None)
+    return lib.qmm_gemm(a["x"], a["M"], a["K"], a["qw"], a["qlo"], a["z"], a["s"], a["b"], a["N"], a["bits"],
+                        a["gs"], a["y"], None)
 
 
 INVALID = [
     ("bits5", dict(bits=5), 2),
-    ("bits1", dict(bits=1), 2),
+    ("bits0", dict(bits=0), 2),
+    ("bits6", dict(bits=6), 2),
     ("M0", dict(M=0), 3),
     ("K_not_32", dict(K=48, gs=-1), 3),
     ("N_not_8", dict(N=60), 3),
@@ -130,6 +131,10 @@ def test_gemm_rejects_before_launch(host_only, name, kw, want):
 
 def test_gemv_limits(host_only):
     assert _gemv(host_only, M=17) == 3
+    # activations too large for the decode kernel's staging: refused (the GEMM takes them)
+    assert _gemv(host_only, M=16, K=65536, N=64, gs=-1) == 3
+    # arrays of 4 GiB or more are refused by both products
+    assert _gemm(host_only, M=1 << 17, K=16384, N=64, gs=-1) == 3
     # a deep, narrow product needs a workspace: too small or missing is refused
     assert host_only.qmm_workspace_bytes(1, 8192, 64, 4, 128) > 16
     assert _gemv(host_only, K=8192, N=64, wsb=16) == 6
@@ -148,6 +153,18 @@ def test_pack_rejects_before_launch(host_only):
     assert lib.qmm_unpack(A, None, 64, 8, 3, A, None) == 1
     assert lib.qmm_unpack(A, None, 64, 8, 4, None, None) == 1
     assert lib.qmm_unpack(A, None, 20, 8, 2, A, None) == 3
+    assert lib.qmm_pack(A, 48, 8, 1, A, None, None, None) == 3   # K % 32 for 1-bit
+
+
+def test_dequant_rejects_before_launch(host_only):
+    lib = host_only
+    assert lib.qmm_dequant(A, A, A, A, 256, 64, 5, 128, A, None) == 2
+    assert lib.qmm_dequant(A, A, A, A, 48, 64, 4, -1, A, None) == 3      # K % 32
+    assert lib.qmm_dequant(A, A, A, A, 256, 64, 4, 48, A, None) == 4     # group size
+    assert lib.qmm_dequant(A, None, A, A, 256, 64, 3, 128, A, None) == 1  # no 1-bit plane
+    assert lib.qmm_dequant(A, A, None, A, 256, 64, 4, 128, A, None) == 1
+    assert lib.qmm_dequant(A, A, A, A, 256, 64, 4, 128, None, None) == 1
+    assert lib.qmm_last_error().decode() != ""
 
 
 def test_binding_refuses_cpu_tensors():

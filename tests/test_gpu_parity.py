@@ -70,7 +70,7 @@ def _check(y_gpu, y_ref, a, label, max_ratio=0.35):
 PACK_SHAPES = [(32, 8), (64, 24), (96, 520), (512, 256), (256, 1000)]
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 8])
 @pytest.mark.parametrize("K,N", PACK_SHAPES)
 def test_pack_unpack_bit_exact(gpu, bits, K, N):
     if K % (32 if bits == 3 else 32 // bits):
@@ -135,6 +135,7 @@ SWEEP_GEMV = [
     (1, 512, 96, 2, 64), (8, 256, 264, 2, 32), (16, 2048, 40, 2, 128),
     (1, 512, 128, 3, 128), (2, 256, 200, 3, 32), (8, 1024, 520, 3, 64), (1, 96, 24, 3, -1),
     (1, 32, 8, 4, 32), (16, 32, 8, 8, -1),
+    (1, 256, 64, 1, 128), (4, 512, 200, 1, 32), (16, 1024, 136, 1, -1),
 ]
 
 
@@ -150,6 +151,7 @@ SWEEP_GEMM = [
     (100, 512, 136, 8, 128), (260, 1024, 264, 8, -1), (64, 96, 8, 8, 32),
     (33, 512, 96, 2, 64), (270, 256, 264, 2, 32),
     (40, 512, 128, 3, 128), (300, 256, 520, 3, 32), (8, 1024, 40, 3, -1),
+    (70, 512, 264, 1, 64), (260, 288, 520, 1, -1),
 ]
 
 
@@ -161,7 +163,7 @@ def test_gemm_sweep(gpu, M, K, N, bits, gs):
 
 
 @pytest.mark.parametrize("path", ["gemv", "gemm"])
-@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 8])
 def test_non_integer_zero_points(gpu, path, bits):
     _say(f"{path} non-integer zeros bits={bits}")
     M = 4 if path == "gemv" else 70
@@ -193,7 +195,7 @@ def test_one_group_zero_points_mixed(gpu, path, M, K, N, bits):
 
 
 @pytest.mark.parametrize("path", ["gemv", "gemm"])
-@pytest.mark.parametrize("bits,gs", [(2, 32), (3, 64), (4, 128), (8, -1), (4, 32)])
+@pytest.mark.parametrize("bits,gs", [(2, 32), (3, 64), (4, 128), (8, -1), (4, 32), (1, 32), (1, -1)])
 def test_one_hot_rows_bit_exact(gpu, path, bits, gs):
     """x = e_k gives y = fp16(w[k, :]); probes every word slot and the first and last k of each group."""
     K, N = 256, 136
@@ -295,11 +297,77 @@ def test_errors_on_device(gpu):
         w.qmm_gemm(x, qw, None, z, z, 5, 128, out=y)
     assert e.value.status == 2
     lib = w.library()
-    st = lib.qmm_gemv(x.data_ptr() + 2, 1, 256, qw.data_ptr(), None, z.data_ptr(), z.data_ptr(), 64, 4, 128,
+    st = lib.qmm_gemv(x.data_ptr() + 2, 1, 256, qw.data_ptr(), None, z.data_ptr(), z.data_ptr(), None, 64, 4, 128,
                       y.data_ptr(), None, 0, None)
     assert st == 5
     torch.cuda.synchronize()
     assert torch.all(y == 7.0)
+
+
+# ------------------------------------------------------------------ dequantize, bias
+
+DEQUANT_CASES = [(1, 256, 72, 32), (2, 512, 136, 64), (3, 256, 200, -1), (4, 1024, 264, 128), (8, 512, 520, 32),
+                 (4, 32, 8, -1)]
+
+
+@pytest.mark.parametrize("bits,K,N,gs", DEQUANT_CASES)
+@pytest.mark.parametrize("zkind", ["integer", "fractional"])
+def test_dequant_bit_exact(gpu, bits, K, N, gs, zkind):
+    """qmm_dequant returns fp16(s * (q - z)) rounded once: equal bit for bit to the oracle."""
+    _say(f"dequant bits={bits} K={K} N={N} gs={gs} zeros={zkind}")
+    d = datagen.small_case(1, K, N, bits, gs, seed=K + N + bits)
+    if zkind == "fractional":
+        rng = np.random.default_rng(bits)
+        d["zeros"] = rng.uniform(-1.5, (1 << bits) + 0.5, size=d["zeros"].shape).astype(np.float16)
+    want = oracle.dequantize_fp16(d["codes"], d["scales"], d["zeros"], gs)
+    qw, qlo = _pack_gpu(gpu, d["codes"], bits)
+    g = _to_gpu_case(d)
+    got = gpu.qmm_dequant(qw, qlo, g["zeros"], g["scales"], K, bits, gs).cpu().numpy()
+    mism = np.argwhere(got.view(np.uint16) != want.view(np.uint16))
+    assert mism.size == 0, [(k, n, float(got[k, n]), float(want[k, n])) for k, n in mism[:10]]
+
+
+def test_dequant_rounding_ties(gpu):
+    """The hand-worked ties of tests/golden/dequant_examples.json round to even on the GPU too."""
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "dequant_examples.json")) as f:
+        cases = json.load(f)["fp16_cases"]
+    K, N = 32, 8 * len(cases)
+    codes = np.zeros((K, N), dtype=np.uint8)
+    s = np.zeros((1, N), dtype=np.uint16)
+    z = np.zeros((1, N), dtype=np.float16)
+    for i, c in enumerate(cases):
+        codes[:, 8 * i:8 * i + 8] = c["q"]
+        s[0, 8 * i:8 * i + 8] = int(c["scale_bits"], 16)
+        z[0, 8 * i:8 * i + 8] = c["zero"]
+    qw, _ = _pack_gpu(gpu, codes, 8)
+    got = gpu.qmm_dequant(qw, None, _t(z), _t(s.view(np.float16)), K, 8, -1).cpu().numpy().view(np.uint16)
+    for i, c in enumerate(cases):
+        assert np.all(got[:, 8 * i:8 * i + 8] == int(c["fp16_bits"], 16)), c["name"]
+
+
+@pytest.mark.parametrize("path,M,K,N,bits,gs", [
+    ("gemv", 1, 512, 256, 4, 128),      # one block per strip
+    ("gemv", 3, 8192, 64, 4, 128),      # blocks along K hand over through the workspace
+    ("gemv", 8, 1024, 520, 1, -1),
+    ("gemm", 70, 288, 520, 8, -1),      # K tail, ragged N, scale after the accumulation
+    ("gemm", 300, 512, 264, 3, 64),     # scale inside the dequantization
+])
+def test_bias(gpu, path, M, K, N, bits, gs):
+    _say(f"bias {path} M={M} K={K} N={N} bits={bits} gs={gs}")
+    d = datagen.small_case(M, K, N, bits, gs, seed=M + K + N)
+    b = np.random.default_rng(M).uniform(-4, 4, size=N).astype(np.float16)
+    qw_ref, qlo_ref = oracle.pack(d["codes"], bits)
+    qw, qlo = _pack_gpu(gpu, d["codes"], bits)
+    g = _to_gpu_case(d)
+    fn = gpu.qmm_gemv if path == "gemv" else gpu.qmm_gemm
+    y = fn(g["x"], qw, qlo, g["zeros"], g["scales"], bits, gs, bias=_t(b)).cpu().numpy()
+    y_ref, a = oracle.quantized_matmul(d["x"], qw_ref, qlo_ref, d["zeros"], d["scales"], bits, gs, bias=b)
+    _check(y, y_ref, a, f"{path} bias")
+    # x = 0: the output is the bias row, exactly
+    y0 = fn(torch.zeros_like(g["x"]), qw, qlo, g["zeros"], g["scales"], bits, gs, bias=_t(b)).cpu().numpy()
+    assert np.array_equal(y0.view(np.uint16), np.tile(b, (M, 1)).view(np.uint16))
 
 
 # ------------------------------------------------------------------ the five workloads

@@ -9,10 +9,13 @@ Functions mirror the C ABI (include/qmm.h):
 
 * ``qmm_pack(codes, bits)`` -> ``(qweight, qweight_lo)``
 * ``qmm_unpack(qweight, qweight_lo, K, bits)`` -> codes
-* ``qmm_gemv(x, qweight, qweight_lo, zeros, scales, bits, group_size)`` (1 <= M <= 16)
-* ``qmm_gemm(x, qweight, qweight_lo, zeros, scales, bits, group_size)`` (any M)
-* ``quantized_matmul(x, qweight, qzeros, scales, bits, group_size, qweight_lo=None)``:
+* ``qmm_dequant(qweight, qweight_lo, zeros, scales, K, bits, group_size)`` -> (K, N) fp16
+* ``qmm_gemv(x, qweight, qweight_lo, zeros, scales, bits, group_size, bias=None)`` (1 <= M <= 16)
+* ``qmm_gemm(x, qweight, qweight_lo, zeros, scales, bits, group_size, bias=None)`` (any M)
+* ``quantized_matmul(x, qweight, qzeros, scales, bits, group_size, qweight_lo=None, bias=None)``:
   the functional form, M <= 16 to the GEMV, larger M to the GEMM.
+
+Bit widths 1, 2, 3, 4 and 8.
 """
 from __future__ import annotations
 
@@ -32,9 +35,11 @@ STATUS_NAMES = {
 }
 # Every symbol the header declares.
 EXPORTS = (
-    "qmm_abi_version", "qmm_status_string", "qmm_last_error", "qmm_pack", "qmm_unpack",
+    "qmm_abi_version", "qmm_status_string", "qmm_last_error", "qmm_pack", "qmm_unpack", "qmm_dequant",
     "qmm_workspace_bytes", "qmm_gemv", "qmm_gemm",
 )
+ABI_VERSION = 2
+BITS = (1, 2, 3, 4, 8)
 GEMV_MAX_M = 16
 
 _lib = None
@@ -59,12 +64,16 @@ def _declare(lib):
     lib.qmm_pack.argtypes = [P, I, I, I, P, P, P, P]
     lib.qmm_unpack.restype = I
     lib.qmm_unpack.argtypes = [P, P, I, I, I, P, P]
+    lib.qmm_dequant.restype = I
+    lib.qmm_dequant.argtypes = [P, P, P, P, I, I, I, I, P, P]
     lib.qmm_workspace_bytes.restype = SZ
     lib.qmm_workspace_bytes.argtypes = [I, I, I, I, I]
     lib.qmm_gemv.restype = I
-    lib.qmm_gemv.argtypes = [P, I, I, P, P, P, P, I, I, I, P, P, SZ, P]
+    lib.qmm_gemv.argtypes = [P, I, I, P, P, P, P, P, I, I, I, P, P, SZ, P]
     lib.qmm_gemm.restype = I
-    lib.qmm_gemm.argtypes = [P, I, I, P, P, P, P, I, I, I, P, P]
+    lib.qmm_gemm.argtypes = [P, I, I, P, P, P, P, P, I, I, I, P, P]
+    if lib.qmm_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"libqmm ABI version {lib.qmm_abi_version()} does not match the binding's {ABI_VERSION}")
     return lib
 
 
@@ -121,7 +130,7 @@ def qmm_pack(codes: torch.Tensor, bits: int, count_bad: bool = False):
     """(K, N) uint8 codes on the GPU -> (qweight, qweight_lo[, bad_count])."""
     _gpu(codes, "codes", torch.uint8)
     K, N = codes.shape
-    shp, shp_lo = packed_shapes(K, N, bits) if bits in (2, 3, 4, 8) else ((1, 1), None)
+    shp, shp_lo = packed_shapes(K, N, bits) if bits in BITS else ((1, 1), None)
     dev = codes.device
     qw = torch.empty(shp, dtype=torch.int32, device=dev)
     qlo = torch.empty(shp_lo, dtype=torch.int32, device=dev) if shp_lo else None
@@ -136,7 +145,7 @@ def qmm_unpack(qweight: torch.Tensor, qweight_lo: torch.Tensor | None, K: int, b
     if qweight_lo is not None:
         _gpu(qweight_lo, "qweight_lo", torch.int32)
     N = qweight.shape[1]
-    shp, shp_lo = packed_shapes(K, N, bits) if bits in (2, 3, 4, 8) else (None, None)
+    shp, shp_lo = packed_shapes(K, N, bits) if bits in BITS else (None, None)
     if shp is not None and tuple(qweight.shape) != shp:
         raise ValueError(f"qweight has shape {tuple(qweight.shape)}, expected {shp}")
     if shp_lo is not None and (qweight_lo is None or tuple(qweight_lo.shape) != shp_lo):
@@ -147,6 +156,30 @@ def qmm_unpack(qweight: torch.Tensor, qweight_lo: torch.Tensor | None, K: int, b
         _check(library().qmm_unpack(_ptr(qweight), _ptr(qweight_lo), K, N, bits, _ptr(codes), _stream(dev)),
                "qmm_unpack")
     return codes
+
+
+def qmm_dequant(qweight, qweight_lo, zeros, scales, K: int, bits: int, group_size: int, out=None):
+    """The dequantized weight as (K, N) fp16: fp16(scale * (q - zero)), rounded once."""
+    _gpu(qweight, "qweight", torch.int32)
+    if bits == 3:
+        if qweight_lo is None:
+            raise ValueError("3-bit weights need qweight_lo (the 1-bit plane)")
+        _gpu(qweight_lo, "qweight_lo", torch.int32)
+    _gpu(zeros, "zeros", torch.float16)
+    _gpu(scales, "scales", torch.float16)
+    N = qweight.shape[1]
+    if bits in BITS:
+        shp, shp_lo = packed_shapes(K, N, bits)
+        if tuple(qweight.shape) != shp or (shp_lo and tuple(qweight_lo.shape) != shp_lo):
+            raise ValueError(f"packed weight shapes {tuple(qweight.shape)} do not match K={K}, N={N}, bits={bits}")
+    if zeros.shape != scales.shape or zeros.shape[1] != N:
+        raise ValueError("zeros and scales must both be (G, N)")
+    dev = qweight.device
+    w = torch.empty((K, N), dtype=torch.float16, device=dev) if out is None else out
+    with torch.cuda.device(dev):
+        _check(library().qmm_dequant(_ptr(qweight), _ptr(qweight_lo), _ptr(zeros), _ptr(scales), K, N, bits,
+                                     group_size, _ptr(w), _stream(dev)), "qmm_dequant")
+    return w
 
 
 def workspace_bytes(M: int, K: int, N: int, bits: int, group_size: int) -> int:
@@ -171,6 +204,14 @@ def gemv_workspace(device, nbytes: int, stream=None) -> torch.Tensor | None:
     return ws
 
 
+def _check_bias(bias, N):
+    if bias is None:
+        return
+    _gpu(bias, "bias", torch.float16, ndim=1)
+    if bias.shape[0] != N:
+        raise ValueError(f"bias must have N={N} elements")
+
+
 def _check_product_args(x, qweight, qweight_lo, zeros, scales, bits):
     _gpu(x, "x", torch.float16)
     _gpu(qweight, "qweight", torch.int32)
@@ -182,7 +223,7 @@ def _check_product_args(x, qweight, qweight_lo, zeros, scales, bits):
     _gpu(scales, "scales", torch.float16)
     M, K = x.shape
     N = qweight.shape[1]
-    if bits in (2, 3, 4, 8):
+    if bits in BITS:
         shp, shp_lo = packed_shapes(K, N, bits)
         if tuple(qweight.shape) != shp or (shp_lo and tuple(qweight_lo.shape) != shp_lo):
             raise ValueError(f"packed weight shapes {tuple(qweight.shape)} do not match K={K}, N={N}, bits={bits}")
@@ -191,40 +232,49 @@ def _check_product_args(x, qweight, qweight_lo, zeros, scales, bits):
     return M, K, N
 
 
-def qmm_gemv(x, qweight, qweight_lo, zeros, scales, bits: int, group_size: int, out=None, workspace=None):
-    """y = x @ dequantize(W) for 1 <= M <= 16; returns (M, N) fp16."""
+def qmm_gemv(x, qweight, qweight_lo, zeros, scales, bits: int, group_size: int, out=None, workspace=None,
+             bias=None):
+    """y = x @ dequantize(W) (+ bias) for 1 <= M <= 16; returns (M, N) fp16."""
     M, K, N = _check_product_args(x, qweight, qweight_lo, zeros, scales, bits)
+    _check_bias(bias, N)
     dev = x.device
     y = torch.empty((M, N), dtype=torch.float16, device=dev) if out is None else out
     nbytes = workspace_bytes(M, K, N, bits, group_size) if M <= GEMV_MAX_M else 0
     ws = workspace if workspace is not None else gemv_workspace(dev, nbytes)
     with torch.cuda.device(dev):
-        _check(library().qmm_gemv(_ptr(x), M, K, _ptr(qweight), _ptr(qweight_lo), _ptr(zeros), _ptr(scales), N, bits,
-                                  group_size, _ptr(y), _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev)),
+        _check(library().qmm_gemv(_ptr(x), M, K, _ptr(qweight), _ptr(qweight_lo), _ptr(zeros), _ptr(scales),
+                                  _ptr(bias), N, bits, group_size, _ptr(y), _ptr(ws), 0 if ws is None else ws.numel(),
+                                  _stream(dev)),
                "qmm_gemv")
     return y
 
 
-def qmm_gemm(x, qweight, qweight_lo, zeros, scales, bits: int, group_size: int, out=None):
-    """y = x @ dequantize(W) for any M on the matrix cores; returns (M, N) fp16."""
+def qmm_gemm(x, qweight, qweight_lo, zeros, scales, bits: int, group_size: int, out=None, bias=None):
+    """y = x @ dequantize(W) (+ bias) for any M on the matrix cores; returns (M, N) fp16."""
     M, K, N = _check_product_args(x, qweight, qweight_lo, zeros, scales, bits)
+    _check_bias(bias, N)
     dev = x.device
     y = torch.empty((M, N), dtype=torch.float16, device=dev) if out is None else out
     with torch.cuda.device(dev):
-        _check(library().qmm_gemm(_ptr(x), M, K, _ptr(qweight), _ptr(qweight_lo), _ptr(zeros), _ptr(scales), N, bits,
-                                  group_size, _ptr(y), _stream(dev)),
+        _check(library().qmm_gemm(_ptr(x), M, K, _ptr(qweight), _ptr(qweight_lo), _ptr(zeros), _ptr(scales),
+                                  _ptr(bias), N, bits, group_size, _ptr(y), _stream(dev)),
                "qmm_gemm")
     return y
 
 
-def quantized_matmul(x, qweight, qzeros, scales, bits: int, group_size: int, qweight_lo=None):
-    """output = x @ dequantize(qweight), in the argument order of the functional API.
+def quantized_matmul(x, qweight, qzeros, scales, bits: int, group_size: int, qweight_lo=None, bias=None):
+    """output = x @ dequantize(qweight) (+ bias), in the argument order of the functional API.
 
-    ``qzeros`` are the (G, N) fp16 zero points; M <= 16 runs the decode GEMV,
-    larger M the prefill GEMM.
+    ``qzeros`` are the (G, N) fp16 zero points; M <= 16 runs the decode GEMV
+    (the GEMM when the GEMV's staging limits reject the shape), larger M the
+    prefill GEMM.
     """
     if x.dim() != 2:
         raise ValueError("x must be (M, K)")
     if x.shape[0] <= GEMV_MAX_M:
-        return qmm_gemv(x, qweight, qweight_lo, qzeros, scales, bits, group_size)
-    return qmm_gemm(x, qweight, qweight_lo, qzeros, scales, bits, group_size)
+        try:
+            return qmm_gemv(x, qweight, qweight_lo, qzeros, scales, bits, group_size, bias=bias)
+        except QmmError as e:
+            if e.status != 3:  # QMM_ERR_SHAPE: shape beyond the decode kernel's staging limits
+                raise
+    return qmm_gemm(x, qweight, qweight_lo, qzeros, scales, bits, group_size, bias=bias)

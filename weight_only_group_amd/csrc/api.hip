@@ -26,13 +26,13 @@ qmm_status ok() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-bool bits_ok(int bits) { return bits == 2 || bits == 3 || bits == 4 || bits == 8; }
+bool bits_ok(int bits) { return bits == 1 || bits == 2 || bits == 3 || bits == 4 || bits == 8; }
 
 // Codes per word of the plane that sets the K granularity.
 int k_multiple(int bits) { return bits == 3 ? 32 : 32 / bits; }
 
 qmm_status check_packing(int K, int N, int bits, const void* qweight, const void* qweight_lo) {
-  if (!bits_ok(bits)) return fail(QMM_ERR_BITS, "bits=%d is not one of 2, 3, 4, 8", bits);
+  if (!bits_ok(bits)) return fail(QMM_ERR_BITS, "bits=%d is not one of 1, 2, 3, 4, 8", bits);
   if (K < 1 || N < 1) return fail(QMM_ERR_SHAPE, "K=%d and N=%d must be >= 1", K, N);
   if (K % k_multiple(bits)) return fail(QMM_ERR_SHAPE, "K=%d must be a multiple of %d for %d-bit codes", K, k_multiple(bits), bits);
   if (qweight == nullptr) return fail(QMM_ERR_NULL, "qweight is NULL");
@@ -40,16 +40,22 @@ qmm_status check_packing(int K, int N, int bits, const void* qweight, const void
   return QMM_OK;
 }
 
+qmm_status check_group(int K, int group_size) {
+  if (group_size != -1 && (group_size <= 0 || group_size % 32 || K % group_size))
+    return fail(QMM_ERR_GROUP, "group_size=%d must be -1 or a positive multiple of 32 dividing K=%d", group_size, K);
+  return QMM_OK;
+}
+
 qmm_status check_product(const uint16_t* x, int M, int K, const int32_t* qweight, const int32_t* qweight_lo,
                          const uint16_t* zeros, const uint16_t* scales, int N, int bits, int group_size,
                          const uint16_t* y, int max_m) {
-  if (!bits_ok(bits)) return fail(QMM_ERR_BITS, "bits=%d is not one of 2, 3, 4, 8", bits);
+  if (!bits_ok(bits)) return fail(QMM_ERR_BITS, "bits=%d is not one of 1, 2, 3, 4, 8", bits);
   if (M < 1 || M > max_m) return fail(QMM_ERR_SHAPE, "M=%d must be in [1, %d]", M, max_m);
   if (K < 32 || K % 32) return fail(QMM_ERR_SHAPE, "K=%d must be a positive multiple of 32", K);
   if (N < 8 || N % 8) return fail(QMM_ERR_SHAPE, "N=%d must be a positive multiple of 8", N);
-  if (group_size != -1) {
-    if (group_size <= 0 || group_size % 32 || K % group_size)
-      return fail(QMM_ERR_GROUP, "group_size=%d must be -1 or a positive multiple of 32 dividing K=%d", group_size, K);
+  {
+    const qmm_status gs = check_group(K, group_size);
+    if (gs != QMM_OK) return gs;
   }
   // Kernels address x, the packed planes, scales and zero points with 32-bit
   // byte offsets.
@@ -113,6 +119,21 @@ qmm_status qmm_unpack(const int32_t* qweight, const int32_t* qweight_lo, int K, 
                   "qmm_unpack launch");
 }
 
+qmm_status qmm_dequant(const int32_t* qweight, const int32_t* qweight_lo, const uint16_t* zeros,
+                       const uint16_t* scales, int K, int N, int bits, int group_size, uint16_t* w,
+                       hipStream_t stream) {
+  qmm_status st = check_packing(K, N, bits, qweight, qweight_lo);
+  if (st != QMM_OK) return st;
+  if (K % 32) return fail(QMM_ERR_SHAPE, "K=%d must be a multiple of 32", K);
+  st = check_group(K, group_size);
+  if (st != QMM_OK) return st;
+  if (!zeros || !scales || !w) return fail(QMM_ERR_NULL, "zeros, scales and w must not be NULL");
+  return from_hip(qmm::launch_dequant(reinterpret_cast<const uint32_t*>(qweight),
+                                      reinterpret_cast<const uint32_t*>(qweight_lo), zeros, scales, K, N, bits,
+                                      group_size, w, stream),
+                  "qmm_dequant launch");
+}
+
 size_t qmm_workspace_bytes(int M, int K, int N, int bits, int group_size) {
   if (!bits_ok(bits) || M < 1 || M > 16 || K < 32 || K % 32 || N < 8 || N % 8 || N > qmm::kGemvMaxN) return 0;
   if (group_size != -1 && (group_size <= 0 || group_size % 32 || K % group_size)) return 0;
@@ -120,8 +141,8 @@ size_t qmm_workspace_bytes(int M, int K, int N, int bits, int group_size) {
 }
 
 qmm_status qmm_gemv(const uint16_t* x, int M, int K, const int32_t* qweight, const int32_t* qweight_lo,
-                    const uint16_t* zeros, const uint16_t* scales, int N, int bits, int group_size, uint16_t* y,
-                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                    const uint16_t* zeros, const uint16_t* scales, const uint16_t* bias, int N, int bits,
+                    int group_size, uint16_t* y, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   qmm_status st = check_product(x, M, K, qweight, qweight_lo, zeros, scales, N, bits, group_size, y, 16);
   if (st != QMM_OK) return st;
   if (N > qmm::kGemvMaxN) return fail(QMM_ERR_SHAPE, "N=%d exceeds the decode product's limit of %d", N, qmm::kGemvMaxN);
@@ -136,18 +157,18 @@ qmm_status qmm_gemv(const uint16_t* x, int M, int K, const int32_t* qweight, con
     if (!aligned16(workspace)) return fail(QMM_ERR_ALIGN, "workspace must be 16-byte aligned");
   }
   return from_hip(qmm::launch_gemv(plan, x, M, K, reinterpret_cast<const uint32_t*>(qweight),
-                                   reinterpret_cast<const uint32_t*>(qweight_lo), zeros, scales, N, bits,
+                                   reinterpret_cast<const uint32_t*>(qweight_lo), zeros, scales, bias, N, bits,
                                    group_size, y, workspace, stream),
                   "qmm_gemv launch");
 }
 
 qmm_status qmm_gemm(const uint16_t* x, int M, int K, const int32_t* qweight, const int32_t* qweight_lo,
-                    const uint16_t* zeros, const uint16_t* scales, int N, int bits, int group_size, uint16_t* y,
-                    hipStream_t stream) {
+                    const uint16_t* zeros, const uint16_t* scales, const uint16_t* bias, int N, int bits,
+                    int group_size, uint16_t* y, hipStream_t stream) {
   qmm_status st = check_product(x, M, K, qweight, qweight_lo, zeros, scales, N, bits, group_size, y, 1 << 30);
   if (st != QMM_OK) return st;
   return from_hip(qmm::launch_gemm(x, M, K, reinterpret_cast<const uint32_t*>(qweight),
-                                   reinterpret_cast<const uint32_t*>(qweight_lo), zeros, scales, N, bits,
+                                   reinterpret_cast<const uint32_t*>(qweight_lo), zeros, scales, bias, N, bits,
                                    group_size, y, stream),
                   "qmm_gemm launch");
 }

@@ -52,13 +52,19 @@ struct GemvPlan {
 };
 GemvPlan gemv_plan(int M, int K, int N, int bits, int group_size);
 hipError_t launch_gemv(const GemvPlan& p, const uint16_t* x, int M, int K, const uint32_t* qw,
-                       const uint32_t* qlo, const uint16_t* zeros, const uint16_t* scales, int N,
-                       int bits, int group_size, uint16_t* y, void* workspace, hipStream_t stream);
+                       const uint32_t* qlo, const uint16_t* zeros, const uint16_t* scales,
+                       const uint16_t* bias, int N, int bits, int group_size, uint16_t* y,
+                       void* workspace, hipStream_t stream);
 
 // ---- prefill GEMM ---------------------------------------------------------
 hipError_t launch_gemm(const uint16_t* x, int M, int K, const uint32_t* qw, const uint32_t* qlo,
-                       const uint16_t* zeros, const uint16_t* scales, int N, int bits,
-                       int group_size, uint16_t* y, hipStream_t stream);
+                       const uint16_t* zeros, const uint16_t* scales, const uint16_t* bias, int N,
+                       int bits, int group_size, uint16_t* y, hipStream_t stream);
+
+// ---- dequantize to fp16 -------------------------------------------------------
+hipError_t launch_dequant(const uint32_t* qw, const uint32_t* qlo, const uint16_t* zeros,
+                          const uint16_t* scales, int K, int N, int bits, int group_size, uint16_t* w,
+                          hipStream_t stream);
 
 // ---- pack / unpack ----------------------------------------------------------
 hipError_t launch_pack(const uint8_t* codes, int K, int N, int bits, uint32_t* qw, uint32_t* qlo,

@@ -51,6 +51,7 @@ struct GemmArgs {
   const uint32_t* qlo;
   const uint16_t* zeros;
   const uint16_t* scales;
+  const uint16_t* bias;  // (N,) or null
   uint16_t* y;
   int M, K, N;
   int upg;       // 32-row units per group
@@ -67,6 +68,7 @@ template <> struct Frag<8> { static constexpr int NW = 2, NL = 0, EPS = 4; };
 template <> struct Frag<4> { static constexpr int NW = 1, NL = 0, EPS = 8; };
 template <> struct Frag<2> { static constexpr int NW = 1, NL = 0, EPS = 16; };
 template <> struct Frag<3> { static constexpr int NW = 1, NL = 1, EPS = 16; };
+template <> struct Frag<1> { static constexpr int NW = 1, NL = 0, EPS = 32; };
 
 // Word row (within the plane) of word w of k-step s of slab ks, for lane
 // chunk kc; and the bit offset of the lane's first code in that word.
@@ -74,6 +76,7 @@ template <int BITS>
 __device__ __forceinline__ int frag_row(int ks, int s, int kc, int w) {
   if constexpr (BITS == 8) return ks * 16 + 4 * s + 2 * kc + w;
   else if constexpr (BITS == 4) return ks * 8 + 2 * s + kc;
+  else if constexpr (BITS == 1) return ks * 2 + (s >> 1);  // 32 codes per word: two steps
   else return ks * 4 + s;  // 2-bit and the 2-bit plane of 3-bit codes
 }
 
@@ -93,6 +96,13 @@ __device__ __forceinline__ void frag_codes(const uint32_t* w, const uint32_t* l,
     for (int p = 0; p < 4; ++p) {
       const uint32_t t = w[0] >> (8 * p);
       h[p] = (t & 0xFu) | ((t << 12) & 0xF0000u) | kMagic1024x2;
+    }
+  } else if constexpr (BITS == 1) {
+    const uint32_t u = w[0] >> (16 * (s & 1) + 8 * kc);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t t = u >> (2 * p);
+      h[p] = (t & 0x1u) | ((t << 15) & 0x10000u) | kMagic1024x2;
     }
   } else if constexpr (BITS == 2) {
     const uint32_t u = w[0] >> (16 * kc);
@@ -394,13 +404,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs g) {
 #pragma unroll
   for (int b = 0; b < TN; ++b) {
     const int col = (BN / WN) * wn + 32 * b + (lane & 31);
-    float sc = 1.f;
+    float sc = 1.f, bv = 0.f;  // the bias joins the fp32 value before its one rounding to fp16
     if constexpr (POST_SCALE) sc = half_bits_to_float(g.scales[min(n0 + col, g.N - 1)]);
+    if (g.bias) bv = half_bits_to_float(g.bias[min(n0 + col, g.N - 1)]);
 #pragma unroll
     for (int a = 0; a < TM; ++a)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        lds[acc_row(a, r) * LDY + col] = (f16)(acc[a][b][r] * sc);
+        lds[acc_row(a, r) * LDY + col] = (f16)(acc[a][b][r] * sc + bv);
   }
   __syncthreads();
 #pragma unroll 4
@@ -433,14 +444,15 @@ hipError_t launch_bits(const GemmArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gemm(const uint16_t* x, int M, int K, const uint32_t* qw, const uint32_t* qlo,
-                       const uint16_t* zeros, const uint16_t* scales, int N, int bits, int group_size,
-                       uint16_t* y, hipStream_t s) {
+                       const uint16_t* zeros, const uint16_t* scales, const uint16_t* bias, int N, int bits,
+                       int group_size, uint16_t* y, hipStream_t s) {
   GemmArgs a;
   a.x = x;
   a.qw = qw;
   a.qlo = qlo;
   a.zeros = zeros;
   a.scales = scales;
+  a.bias = bias;
   a.y = y;
   a.M = M;
   a.K = K;
@@ -452,6 +464,7 @@ hipError_t launch_gemm(const uint16_t* x, int M, int K, const uint32_t* qw, cons
   a.mblocks = (M + BM - 1) / BM;
   a.nblocks = (N + BN - 1) / BN;
   switch (bits) {
+    case 1: return launch_bits<1>(a, s);
     case 2: return launch_bits<2>(a, s);
     case 3: return launch_bits<3>(a, s);
     case 4: return launch_bits<4>(a, s);

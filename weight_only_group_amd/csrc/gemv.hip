@@ -68,6 +68,7 @@ template <> struct Bits<4> { static constexpr int NW = 1; };
 template <> struct Bits<8> { static constexpr int NW = 2; };
 template <> struct Bits<2> { static constexpr int NW = 1; };
 template <> struct Bits<3> { static constexpr int NW = 2; };
+template <> struct Bits<1> { static constexpr int NW = 1; };
 
 template <int VEC> struct Vec;
 template <> struct Vec<1> { typedef uint32_t T; };
@@ -83,6 +84,7 @@ __device__ __forceinline__ uint32_t word_at(typename Vec<VEC>::T w, int v) {
 // Four fp16 pairs 1024 + q for the 8 codes lane group j takes from its
 // word(s) of one column. Element order (pair p = elements 2p, 2p+1):
 //  4-bit: slots (p, p + 4) of the word          -> k = 8j + {p, p+4}
+//  1-bit: slots (8j + p, 8j + p + 4) of the word -> k = 8j + {p, p+4}
 //  8-bit: slots (0,1),(2,3) of word 0, then of 1 -> k = 8j + e
 //  2/3-bit: slots (i0 + p, i0 + p + 8), i0 = 4 (j & 1), of the plane-2 word
 //           -> k = 16 (j >> 1) + i0 + {p, p + 8}
@@ -91,6 +93,13 @@ __device__ __forceinline__ void decode8(uint32_t w0, uint32_t w1, int j, uint32_
   if constexpr (BITS == 4) {
 #pragma unroll
     for (int p = 0; p < 4; ++p) b[p] = ((w0 >> (4 * p)) & 0x000F000Fu) | kMagic1024x2;
+  } else if constexpr (BITS == 1) {
+    const uint32_t t = w0 >> (8 * j);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t u = (t >> p) & 0x11u;  // codes p and p + 4 at bits 0 and 4
+      b[p] = ((u | (u << 12)) & 0x00010001u) | kMagic1024x2;
+    }
   } else if constexpr (BITS == 8) {
     // byte permute: (byte0, 0x64, byte1, 0x64) = halves (1024 + q0, 1024 + q1)
     b[0] = __builtin_amdgcn_perm(0x64646464u, w0, 0x04010400u);
@@ -128,6 +137,7 @@ struct GemvArgs {
   const uint32_t* qlo;
   const uint16_t* zeros;
   const uint16_t* scales;
+  const uint16_t* bias;  // (N,) or null
   uint16_t* y;
   float* part;
   uint32_t* counters;
@@ -161,7 +171,7 @@ __device__ __forceinline__ uint16_t half_at(typename Halves<VEC>::T h, int v) {
 // First k (within a unit) of the activations lane group j feeds: 8 consecutive
 // k for 4- and 8-bit codes; for 2- and 3-bit codes two runs of 4, 8 apart.
 template <int BITS> __device__ __forceinline__ int x_first(int j) {
-  return (BITS == 4 || BITS == 8) ? 8 * j : 16 * (j >> 1) + 4 * (j & 1);
+  return (BITS == 1 || BITS == 4 || BITS == 8) ? 8 * j : 16 * (j >> 1) + 4 * (j & 1);
 }
 
 // A raw buffer resource over `bytes` bytes at p (out-of-range reads return 0).
@@ -180,7 +190,7 @@ __device__ __forceinline__ typename Vec<VEC>::T load_words(__amdgpu_buffer_rsrc_
 // Raw activation bytes of one (row, unit, lane group) slot: 8 halves.
 template <int BITS>
 __device__ __forceinline__ u32x4 load_x_slot(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
-  if constexpr (BITS == 4 || BITS == 8) {
+  if constexpr (BITS == 1 || BITS == 4 || BITS == 8) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
   } else {
     const u32x2 e = __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0);
@@ -196,7 +206,7 @@ __device__ __forceinline__ u32x4 x_operand(u32x4 d) {
   if constexpr (BITS == 8) {
     return d;
   } else {
-    // 4-bit: d = x[0..7], pairs (k, k + 4); 2/3-bit: d = x[o..o+3], x[o+8..o+11], pairs (k, k + 8)
+    // 1/4-bit: d = x[0..7], pairs (k, k + 4); 2/3-bit: d = x[o..o+3], x[o+8..o+11], pairs (k, k + 8)
     const uint32_t lo0 = d.x, lo1 = d.y, hi0 = d.z, hi1 = d.w;
     return u32x4{__builtin_amdgcn_perm(hi0, lo0, 0x05040100u), __builtin_amdgcn_perm(hi0, lo0, 0x07060302u),
                  __builtin_amdgcn_perm(hi1, lo1, 0x05040100u), __builtin_amdgcn_perm(hi1, lo1, 0x07060302u)};
@@ -207,14 +217,16 @@ __device__ __forceinline__ u32x4 x_operand(u32x4 d) {
 // the rows a unit spans in that plane.
 template <int BITS>
 __device__ __forceinline__ int lane_row(int j, int w) {
-  if constexpr (BITS == 4) return j;
+  if constexpr (BITS == 1) return 0;
+  else if constexpr (BITS == 4) return j;
   else if constexpr (BITS == 8) return 2 * j + w;
   else if constexpr (BITS == 2) return j >> 1;
   else return w == 0 ? (j >> 1) : 0;
 }
 template <int BITS>
 __device__ __forceinline__ int unit_rows(int w) {
-  if constexpr (BITS == 4) return 4;
+  if constexpr (BITS == 1) return 1;
+  else if constexpr (BITS == 4) return 4;
   else if constexpr (BITS == 8) return 8;
   else if constexpr (BITS == 2) return 2;
   else return w == 0 ? 2 : 1;
@@ -443,10 +455,13 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs g) {
     for (int w = 1; w < WAVES; ++w) sum += red[w * entries + e];
     return sum;
   };
+  // The bias joins the fp32 sum before its one rounding to fp16.
+  auto bias_at = [&](int n) { return g.bias ? half_bits_to_float(g.bias[n]) : 0.f; };
   if (g.ksplit == 1) {
     for (int e = tid; e < entries; e += THREADS) {
       const int row = e / COLS, col = e - row * COLS;
-      if (n0 + col < g.N) g.y[(size_t)row * g.N + n0 + col] = __builtin_bit_cast(uint16_t, (f16)block_sum(e));
+      if (n0 + col < g.N)
+        g.y[(size_t)row * g.N + n0 + col] = __builtin_bit_cast(uint16_t, (f16)(block_sum(e) + bias_at(n0 + col)));
     }
     return;
   }
@@ -485,7 +500,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs g) {
       float sum = pv[0];
 #pragma unroll
       for (int sp = 1; sp < kMaxSplit; ++sp) sum += (sp < g.ksplit) ? pv[sp] : 0.f;
-      g.y[off] = __builtin_bit_cast(uint16_t, (f16)sum);
+      g.y[off] = __builtin_bit_cast(uint16_t, (f16)(sum + bias_at(n0 + col)));
     }
   }
   if (tid == 0) __hip_atomic_store(&g.counters[strip], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -574,8 +589,9 @@ GemvPlan gemv_plan(int M, int K, int N, int bits, int group_size) {
 }
 
 hipError_t launch_gemv(const GemvPlan& p, const uint16_t* x, int M, int K, const uint32_t* qw,
-                       const uint32_t* qlo, const uint16_t* zeros, const uint16_t* scales, int N,
-                       int bits, int group_size, uint16_t* y, void* workspace, hipStream_t s) {
+                       const uint32_t* qlo, const uint16_t* zeros, const uint16_t* scales,
+                       const uint16_t* bias, int N, int bits, int group_size, uint16_t* y,
+                       void* workspace, hipStream_t s) {
   if (!p.valid) return hipErrorInvalidValue;
   GemvArgs a;
   a.x = x;
@@ -583,6 +599,7 @@ hipError_t launch_gemv(const GemvPlan& p, const uint16_t* x, int M, int K, const
   a.qlo = qlo;
   a.zeros = zeros;
   a.scales = scales;
+  a.bias = bias;
   a.y = y;
   a.counters = p.ksplit > 1 ? static_cast<uint32_t*>(workspace) : nullptr;
   a.part = p.ksplit > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + p.counters_bytes) : nullptr;
@@ -596,6 +613,7 @@ hipError_t launch_gemv(const GemvPlan& p, const uint16_t* x, int M, int K, const
   a.ubp_log2 = p.ubp_log2;
   a.gp_log2 = p.gp_log2;
   switch (bits) {
+    case 1: return launch_bits<1>(p, a, s);
     case 2: return launch_bits<2>(p, a, s);
     case 3: return launch_bits<3>(p, a, s);
     case 4: return launch_bits<4>(p, a, s);

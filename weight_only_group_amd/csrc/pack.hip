@@ -4,7 +4,7 @@
 // codes (K, N) row-major; words (K / eps, N), eps = 32 / bits; code k of
 // column n sits in word k / eps of column n at bit offset (k % eps) * bits.
 // 3-bit codes are two planes (TritonQuantLinear.__init__): a 2-bit plane of
-// q >> 1 and a 1-bit plane of q & 1.
+// q >> 1 and a 1-bit plane of q & 1. Widths 1, 2, 3, 4 and 8 (SUPPORTED_NBITS).
 //
 // One thread per output word (pack) or per input word (unpack); consecutive
 // threads take consecutive columns, so every global access is coalesced along
@@ -105,6 +105,7 @@ hipError_t unpack_plane(const uint32_t* words, int K, int N, uint8_t* codes, hip
 hipError_t launch_pack(const uint8_t* codes, int K, int N, int bits, uint32_t* qw, uint32_t* qlo,
                        int32_t* bad_count, hipStream_t s) {
   switch (bits) {
+    case 1: return pack_plane<1>(codes, K, N, 0, 1, qw, bad_count, s);
     case 2: return pack_plane<2>(codes, K, N, 0, 2, qw, bad_count, s);
     case 4: return pack_plane<4>(codes, K, N, 0, 4, qw, bad_count, s);
     case 8: return pack_plane<8>(codes, K, N, 0, 8, qw, bad_count, s);
@@ -121,6 +122,7 @@ hipError_t launch_pack(const uint8_t* codes, int K, int N, int bits, uint32_t* q
 hipError_t launch_unpack(const uint32_t* qw, const uint32_t* qlo, int K, int N, int bits, uint8_t* codes,
                          hipStream_t s) {
   switch (bits) {
+    case 1: return unpack_plane<1>(qw, K, N, codes, s);
     case 2: return unpack_plane<2>(qw, K, N, codes, s);
     case 4: return unpack_plane<4>(qw, K, N, codes, s);
     case 8: return unpack_plane<8>(qw, K, N, codes, s);
