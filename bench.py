@@ -23,6 +23,8 @@ The JSON line also carries:
   cpu_baseline  the CPU oracle on the same workload on this host
   gemm          the prefill product M=2048, K=4096, N=14336, 8-bit, one group
                 per column: TFLOP/s against the 2.5 PFLOP/s fp16 dense peak
+  readme_shapes the prefill kernel at the README's own benchmark shapes
+                (128x512x1024, 256x1024x2048, 512x2048x4096; 4-bit g128), cold
   floors        reference kernels timed the same way: an empty kernel as a
                 graph node, a plain streaming read of the decode product's
                 byte count (cold), a long streaming read, a dense MFMA loop
@@ -185,6 +187,56 @@ def bench_gemm(w, torch, datagen, steps: int, warmup: int):
     mean_ms = total_ms / steps
     return {"wl": wl, "total_ms": total_ms, "ms_per_step": total_ms / steps, "mean_launch_ms": mean_ms,
             "flops": flops, "bytes": algorithmic_bytes(wl), "d": d}
+
+
+# The README's benchmark shapes (M, N, K) and the latencies it quotes for them on
+# an A100 (4-bit, group size 128 assumed from its quick start; context only: other
+# hardware, and the page's latencies and TOPS figures disagree with each other).
+README_SHAPES = ((128, 512, 1024, 2.5), (256, 1024, 2048, 8.2), (512, 2048, 4096, 31.5))
+
+
+def bench_readme_shapes(w, torch, datagen, steps: int = 200):
+    """The prefill kernel at the README's own shapes, 4-bit g128, cold weights, graph replay."""
+    dev = torch.device("cuda:0")
+    lib = w.library()
+    out = []
+    for M, N, K, page_ms in README_SHAPES:
+        d = datagen.small_case(M, K, N, 4, 128, seed=M + N + K)
+        x = torch.from_numpy(d["x"]).to(dev)
+        z0 = torch.from_numpy(d["zeros"]).to(dev)
+        s0 = torch.from_numpy(d["scales"]).to(dev)
+        qw0, _ = w.qmm_pack(torch.from_numpy(d["codes"]).to(dev), 4)
+        R = max(1, math.ceil(COLD_BYTES / (qw0.nbytes + z0.nbytes + s0.nbytes)))
+        copies = [(qw0, z0, s0)] + [(qw0.clone(), z0.clone(), s0.clone()) for _ in range(R - 1)]
+        y = torch.empty((M, N), dtype=torch.float16, device=dev)
+
+        def launch(i, sp):
+            qw, z, s = copies[i % R]
+            st = lib.qmm_gemm(x.data_ptr(), M, K, qw.data_ptr(), None, z.data_ptr(), s.data_ptr(), None, N, 4, 128,
+                              y.data_ptr(), sp)
+            if st != 0:
+                raise RuntimeError(f"qmm_gemm failed: {lib.qmm_last_error().decode()}")
+
+        for i in range(3):
+            launch(i, torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            sp = torch.cuda.current_stream().cuda_stream
+            for i in range(steps):
+                launch(i, sp)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        out.append({"M": M, "N": N, "K": K, "bits": 4, "group_size": 128, "us": round(us, 3),
+                    "TFLOP/s": round(2.0 * M * N * K / us / 1e6, 2), "page_context_a100_ms": page_ms})
+        del copies, g
+    return out
 
 
 def floors(torch, gemv_bytes: int):
@@ -385,6 +437,8 @@ def run(args, torch, datagen, w):
                          "traffic": committed_traffic("gemm"), "kernel": "gemm_kernel, 8-bit post-scale instance",
                          "mean_launch_ms": round(gm["mean_launch_ms"], 4)},
         }
+    if not args.no_gemm:
+        out["readme_shapes"] = bench_readme_shapes(w, torch, datagen)
     if not args.no_floors:
         out["floors"] = floors(torch, gv["bytes"])
     if not args.no_cpu_baseline:

@@ -162,6 +162,18 @@ def test_gemm_sweep(gpu, M, K, N, bits, gs):
     _check(y, y_ref, a, "gemm")
 
 
+# The README's benchmark shapes (M, N, K) with its quick-start format (4-bit,
+# group size 128), and a shape that takes the 128 x 128 block tile.
+README_SHAPES = [(128, 512, 1024), (256, 1024, 2048), (512, 2048, 4096), (1024, 4096, 256)]
+
+
+@pytest.mark.parametrize("M,N,K", README_SHAPES)
+def test_gemm_mid_m_shapes(gpu, M, N, K):
+    _say(f"gemm mid-M M={M} N={N} K={K} 4-bit g128")
+    y, y_ref, a = _run(gpu, "gemm", M, K, N, 4, 128, seed=M + N + K)
+    _check(y, y_ref, a, "gemm mid-M")
+
+
 @pytest.mark.parametrize("path", ["gemv", "gemm"])
 @pytest.mark.parametrize("bits", [1, 2, 3, 4, 8])
 def test_non_integer_zero_points(gpu, path, bits):

@@ -9,6 +9,9 @@
 //  * Block tile 256 x 256, K in slabs of 64; 8 waves in a 2 (M) x 4 (N)
 //    arrangement, each wave a 128 x 64 sub-tile of 4 x 2
 //    V_MFMA_F32_32X32X16_F16 accumulators (128 fp32 registers per lane).
+//    Products too small to give every CU such a tile take 128 x 128 or
+//    64 x 64 tiles of 4 waves (the README's own benchmark shapes are of this
+//    kind).
 //  * Activations go through LDS (row pitch 72 halves, so the 16-byte
 //    fragment reads of a wave spread over all banks): three buffers rotate,
 //    the next slab is stored during the third 16-k step of the current one,
@@ -38,12 +41,9 @@
 namespace qmm {
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int BK = 64;
 constexpr int LDK = BK + 8;  // halves per LDS row of a staged activation slab
-constexpr int LDY = BN + 8;  // halves per LDS row of the staged output tile
-constexpr int kLdsHalves = BM * LDY;  // the output tile; the three activation buffers fit inside
-static_assert(3 * BM * LDK <= kLdsHalves, "activation buffers must fit in the LDS allocation");
-static_assert(BM * LDY <= kLdsHalves, "output tile must fit in the slab buffers");
+constexpr int kCUs = 256;
 
 struct GemmArgs {
   const uint16_t* x;
@@ -135,14 +135,22 @@ __device__ __forceinline__ int remap_block(int pid, int nblocks) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, size_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)(uint32_t)bytes, 0x00020000);
 }
-constexpr int kNonTemporal = 2;  // buffer-load cache policy: streamed data
+// Cache policy of the weight loads: the scope bit only (no non-temporal
+// hint), which measured fastest; a weight panel is reused by the row tiles
+// that run beside each other on one XCD.
+constexpr int kWeightPolicy = 1;
 
-template <int BITS, bool POST_SCALE, bool KTAIL, int WM, int WN>
+// Block tile BM x BN = (32 TM WM) x (32 TN WN): WM x WN waves, each TM x TN
+// MFMA tiles of 32 x 32.
+template <int BITS, bool POST_SCALE, bool KTAIL, int WM, int WN, int TM, int TN>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs g) {
+  constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN;
+  constexpr int LDY = BN + 8;  // halves per LDS row of the staged output tile
+  // The three activation buffers, then (reusing them) the output tile.
+  constexpr int kLdsHalves = 3 * BM * LDK > BM * LDY ? 3 * BM * LDK : BM * LDY;
   __shared__ __attribute__((aligned(16))) f16 lds[kLdsHalves];
+  __shared__ float rsum[BM];  // row sums of x, for zero points that are not integers
   constexpr int THREADS = 64 * WM * WN;
-  constexpr int TM = BM / WM / 32;           // 32-row MFMA tiles per wave
-  constexpr int TN = BN / WN / 32;           // 32-column MFMA tiles per wave
   constexpr int CA = BM * BK / 8 / THREADS;  // 16-byte activation chunks per thread per slab
   constexpr int NW = Frag<BITS>::NW, NL = Frag<BITS>::NL;
   constexpr int NG = POST_SCALE ? 1 : 2;     // zero/scale pairs per column per slab (one per 32 k)
@@ -193,11 +201,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs g) {
   };
   auto storeA = [&](const u32x4 (&SA)[CA], int buf, int ks) {
     f16* A = lds + buf * BM * LDK;
-    const bool tail = KTAIL && (ks * BK + 32 >= g.K);  // only the first 32-k half is inside K
+    // Chunks at or past the end of K are stored as zeros: the second half of a
+    // final 32-k slab, and the whole slab that pads an odd slab count.
+    const bool zero = ks * BK + 8 * a_chk >= g.K;
 #pragma unroll
     for (int i = 0; i < CA; ++i) {
       u32x4 v = SA[i];
-      if (KTAIL && tail && a_chk >= 4) v = u32x4{0u, 0u, 0u, 0u};
+      if (zero) v = u32x4{0u, 0u, 0u, 0u};
       *reinterpret_cast<u32x4*>(A + (a_row + (THREADS / 8) * i) * LDK + 8 * a_chk) = v;
     }
   };
@@ -222,11 +232,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs g) {
         // kc is a lane property: it goes in the per-lane offset
         const int row0 = past ? 0 : frag_row<BITS>(ks, s, 0, w);
         const uint32_t kcoff = (BITS == 8 ? 2u * kc : (BITS == 4 ? (uint32_t)kc : 0u)) * (uint32_t)g.N * 4u;
-        S.w[t][w] = __builtin_amdgcn_raw_buffer_load_b32(rw, b_voff[t] + (past ? 0u : kcoff), row0 * g.N * 4, kNonTemporal);
+        S.w[t][w] = __builtin_amdgcn_raw_buffer_load_b32(rw, b_voff[t] + (past ? 0u : kcoff), row0 * g.N * 4, kWeightPolicy);
       }
       if constexpr (NL > 0) {
         const int lrow = past ? 0 : ks * 2 + (s >> 1);
-        S.l[t][0] = __builtin_amdgcn_raw_buffer_load_b32(rl, b_voff[t], lrow * g.N * 4, kNonTemporal);
+        S.l[t][0] = __builtin_amdgcn_raw_buffer_load_b32(rl, b_voff[t], lrow * g.N * 4, kWeightPolicy);
       }
     }
   };
@@ -253,7 +263,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs g) {
   // codes dequantize with one packed add. The remainder z - round(z) (zero
   // for integer zero points) is taken out in the epilogue.
   f16x2 zc[TN];
-  auto frag_b = [&](auto fast_tag, const BStep& S, const ZS& Z, int t, int s, bool zero) {
+  // Steps past the end of K (and the padding slab) need no masking here:
+  // their activations are stored as zeros, and the weights they meet are
+  // finite values of row 0 or of the last slab.
+  auto frag_b = [&](auto fast_tag, const BStep& S, const ZS& Z, int t, int s) {
     constexpr bool FAST = decltype(fast_tag)::value;
     uint32_t h[4], d[4];
     frag_codes<BITS>(S.w[t], S.l[t], kc, s, h);
@@ -274,7 +287,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs g) {
         for (int p = 0; p < 4; ++p) d[p] = as_u32(((as_f16x2(h[p]) + m1024) + zz) * ss);
       }
     }
-    if (KTAIL && zero) d[0] = d[1] = d[2] = d[3] = 0u;
     return __builtin_bit_cast(f16x8, u32x4{d[0], d[1], d[2], d[3]});
   };
 
@@ -299,12 +311,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs g) {
   // step are read from LDS while the current step's MFMAs run; each step's
   // weight words are dequantized in registers and their registers refilled
   // with the same step of slab ks + 2. Activation slabs rotate through three
-  // LDS buffers: slab ks + 1 is stored during step 2 into a buffer last read
-  // two slabs ago, and the one barrier per slab sits before step 3, so the
-  // first fragments of the next slab are read while step 3's MFMAs run.
+  // LDS buffers: slab ks + 1, requested during step 3 of the slab before, is
+  // stored during step 2 into a buffer last read two slabs ago, and the one
+  // barrier per slab sits before step 3, so the first fragments of the next
+  // slab are read while step 3's MFMAs run.
   auto slab = [&](auto fast_tag, int ks, BStep (&B)[4], ZS& Z) __attribute__((always_inline)) {
     const int cur = ks % 3, nxt = (ks + 1) % 3;
-    loadA(SA, ks + 1);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       // Scheduling fence: each step's instructions stay in their step.
@@ -312,13 +324,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs g) {
       if (s == 3) __syncthreads();  // slab ks + 1 is in LDS
 #pragma unroll
       for (int t = 0; t < TM; ++t) fa[(s + 1) & 1][t] = s < 3 ? frag_a(cur, s + 1, t) : frag_a(nxt, 0, t);
-      const bool past = KTAIL && ks * BK + 16 * s >= g.K;
       f16x8 fb[TN];
 #pragma unroll
-      for (int t = 0; t < TN; ++t) fb[t] = frag_b(fast_tag, B[s], Z, t, s, past);
+      for (int t = 0; t < TN; ++t) fb[t] = frag_b(fast_tag, B[s], Z, t, s);
       loadB(B[s], ks + 2, s);
       if (!POST_SCALE && s == 3) loadZS(Z, ks + 2);
       if (s == 2) storeA(SA, nxt, ks + 1);
+      if (s == 3) loadA(SA, ks + 2);  // three steps before it is stored
 #pragma unroll
       for (int a = 0; a < TM; ++a)
 #pragma unroll
@@ -327,13 +339,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs g) {
     }
     __builtin_amdgcn_sched_barrier(0);
   };
+  // Slabs run in pairs; an odd count is padded with a slab whose activations
+  // and weights are zero (it adds nothing), so that the loop keeps one shape
+  // and the accumulators one place.
   auto run = [&](auto fast_tag) __attribute__((always_inline)) {
-    int ks = 0;
-    for (; ks + 1 < nk; ks += 2) {
+    for (int ks = 0; ks < nk; ks += 2) {
       slab(fast_tag, ks, B0, Z0);
       slab(fast_tag, ks + 1, B1, POST_SCALE ? Z0 : Z1);
     }
-    if (ks < nk) slab(fast_tag, ks, B0, Z0);
   };
 
   loadA(SA, 0);
@@ -344,6 +357,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs g) {
   for (int s = 0; s < 4; ++s) loadB(B1[s], 1, s);
   if (!POST_SCALE) loadZS(Z1, 1);
   storeA(SA, 0, 0);
+  loadA(SA, 1);
   __syncthreads();
 #pragma unroll
   for (int t = 0; t < TM; ++t) fa[0][t] = frag_a(0, 0, t);
@@ -365,7 +379,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs g) {
   // acc = sum_k x (q - z) + delta * sum_k x with delta = z + 1024 + c (exact in
   // fp32). Blocks with a column whose delta is not zero (a zero point that is
   // not an integer) subtract delta times the row sums of x, computed here in
-  // a fixed order. The barrier below also ends every read of the slab buffers.
+  // a fixed order. The barrier of the vote also ends every read of the slab
+  // buffers.
   bool off = false;
   float delta[TN];
 #pragma unroll
@@ -374,8 +389,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs g) {
     if constexpr (POST_SCALE) delta[t] = (half_bits_to_float(Z0.z[t][0]) + 1024.f) + (float)zc[t].x;
     off = off || delta[t] != 0.f;
   }
-  if (__syncthreads_or(off)) {
-    float* rsum = reinterpret_cast<float*>(lds);
+  const bool need = __syncthreads_or(off);
+  if (need) {
     for (int row = tid >> 3; row < BM; row += THREADS / 8) {
       const uint16_t* xr = g.x + (size_t)min(m0 + row, g.M - 1) * g.K;
       float sum = 0.f;
@@ -390,29 +405,31 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs g) {
       if ((tid & 7) == 0) rsum[row] = sum;
     }
     __syncthreads();
-#pragma unroll
-    for (int a = 0; a < TM; ++a)
-#pragma unroll
-      for (int b = 0; b < TN; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[a][b][r] -= delta[b] * rsum[acc_row(a, r)];
-    __syncthreads();
   }
 
-  // Epilogue: scale (one group per column), round to fp16, stage the tile in
-  // LDS, then write rows with 16-byte stores.
+  // Epilogue: remainder correction, scale (one group per column) and bias in
+  // fp32, one rounding to fp16, the tile staged in LDS, rows written with
+  // 16-byte stores. The accumulators are only read.
+  auto emit = [&](auto need_tag) __attribute__((always_inline)) {
+    constexpr bool NEED = decltype(need_tag)::value;
 #pragma unroll
-  for (int b = 0; b < TN; ++b) {
-    const int col = (BN / WN) * wn + 32 * b + (lane & 31);
-    float sc = 1.f, bv = 0.f;  // the bias joins the fp32 value before its one rounding to fp16
-    if constexpr (POST_SCALE) sc = half_bits_to_float(g.scales[min(n0 + col, g.N - 1)]);
-    if (g.bias) bv = half_bits_to_float(g.bias[min(n0 + col, g.N - 1)]);
+    for (int b = 0; b < TN; ++b) {
+      const int col = (BN / WN) * wn + 32 * b + (lane & 31);
+      float sc = 1.f, bv = 0.f;
+      if constexpr (POST_SCALE) sc = half_bits_to_float(g.scales[min(n0 + col, g.N - 1)]);
+      if (g.bias) bv = half_bits_to_float(g.bias[min(n0 + col, g.N - 1)]);
 #pragma unroll
-    for (int a = 0; a < TM; ++a)
+      for (int a = 0; a < TM; ++a)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        lds[acc_row(a, r) * LDY + col] = (f16)(acc[a][b][r] * sc + bv);
-  }
+        for (int r = 0; r < 16; ++r) {
+          float v = acc[a][b][r];
+          if constexpr (NEED) v -= delta[b] * rsum[acc_row(a, r)];
+          lds[acc_row(a, r) * LDY + col] = (f16)(v * sc + bv);
+        }
+    }
+  };
+  if (need) emit(std::integral_constant<bool, true>{});
+  else emit(std::integral_constant<bool, false>{});
   __syncthreads();
 #pragma unroll 4
   for (int c = tid; c < BM * (BN / 8); c += THREADS) {
@@ -423,22 +440,31 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs g) {
   }
 }
 
-template <int BITS, int WM, int WN>
-hipError_t launch_waves(const GemmArgs& a, hipStream_t s) {
+template <int BITS, int WM, int WN, int TM, int TN>
+hipError_t launch_tiles(GemmArgs a, hipStream_t s) {
+  constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN;
+  a.mblocks = (a.M + BM - 1) / BM;
+  a.nblocks = (a.N + BN - 1) / BN;
   const int nblocks = a.mblocks * a.nblocks;
   const bool post = a.upg * 32 == a.K;
   const bool tail = a.K % BK != 0;
   constexpr int T = 64 * WM * WN;
-  if (post && !tail) gemm_kernel<BITS, true, false, WM, WN><<<nblocks, T, 0, s>>>(a);
-  else if (post) gemm_kernel<BITS, true, true, WM, WN><<<nblocks, T, 0, s>>>(a);
-  else if (!tail) gemm_kernel<BITS, false, false, WM, WN><<<nblocks, T, 0, s>>>(a);
-  else gemm_kernel<BITS, false, true, WM, WN><<<nblocks, T, 0, s>>>(a);
+  if (post && !tail) gemm_kernel<BITS, true, false, WM, WN, TM, TN><<<nblocks, T, 0, s>>>(a);
+  else if (post) gemm_kernel<BITS, true, true, WM, WN, TM, TN><<<nblocks, T, 0, s>>>(a);
+  else if (!tail) gemm_kernel<BITS, false, false, WM, WN, TM, TN><<<nblocks, T, 0, s>>>(a);
+  else gemm_kernel<BITS, false, true, WM, WN, TM, TN><<<nblocks, T, 0, s>>>(a);
   return hipGetLastError();
 }
 
+// The largest block tile whose grid still gives every CU a block: 256 x 256
+// (8 waves of 128 x 64), else 128 x 128 (4 waves of 64 x 64), else 64 x 64
+// (4 waves of 32 x 32).
 template <int BITS>
 hipError_t launch_bits(const GemmArgs& a, hipStream_t s) {
-  return launch_waves<BITS, 2, 4>(a, s);  // 8 waves: 2 along M x 4 along N
+  auto blocks = [&](int bm, int bn) { return (long long)((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn); };
+  if (blocks(256, 256) >= kCUs) return launch_tiles<BITS, 2, 4, 4, 2>(a, s);
+  if (blocks(128, 128) >= kCUs) return launch_tiles<BITS, 2, 2, 2, 2>(a, s);
+  return launch_tiles<BITS, 2, 2, 1, 1>(a, s);
 }
 
 }  // namespace
@@ -461,8 +487,6 @@ hipError_t launch_gemm(const uint16_t* x, int M, int K, const uint32_t* qw, cons
   a.upg_log2 = -1;
   for (int l = 0; l < 31; ++l)
     if ((1 << l) == a.upg) a.upg_log2 = l;
-  a.mblocks = (M + BM - 1) / BM;
-  a.nblocks = (N + BN - 1) / BN;
   switch (bits) {
     case 1: return launch_bits<1>(a, s);
     case 2: return launch_bits<2>(a, s);
