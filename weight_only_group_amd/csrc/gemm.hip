@@ -140,25 +140,36 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, size_
 // that run beside each other on one XCD.
 constexpr int kWeightPolicy = 1;
 
-// Block tile BM x BN = (32 TM WM) x (32 TN WN): WM x WN waves, each TM x TN
-// MFMA tiles of 32 x 32.
-template <int BITS, bool POST_SCALE, bool KTAIL, int WM, int WN, int TM, int TN>
-__global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs g) {
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
+// Block tile BM x BN = (32 TM WM) x (32 TN WN), computed by KG groups of
+// WM x WN waves, each wave TM x TN MFMA tiles of 32 x 32. Group j takes the
+// 64-k slabs j, j + KG, j + 2 KG, ... with LDS buffers of its own; the groups'
+// fp32 sums are added in group order at the end.
+template <int BITS, bool POST_SCALE, bool KTAIL, int WM, int WN, int TM, int TN, int KG>
+__global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) {
   constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN;
   constexpr int LDY = BN + 8;  // halves per LDS row of the staged output tile
-  // The three activation buffers, then (reusing them) the output tile.
-  constexpr int kLdsHalves = 3 * BM * LDK > BM * LDY ? 3 * BM * LDK : BM * LDY;
+  constexpr int GW = WM * WN;  // waves per group
+  constexpr int ACC = TM * TN * 16;  // accumulators per lane
+  // Each group's three activation buffers; then, reusing them, the other
+  // groups' partial sums and the output tile.
+  constexpr int kLdsHalves = cmax(cmax(KG * 3 * BM * LDK, BM * LDY), (KG - 1) * GW * ACC * 64 * 2);
   __shared__ __attribute__((aligned(16))) f16 lds[kLdsHalves];
   __shared__ float rsum[BM];  // row sums of x, for zero points that are not integers
-  constexpr int THREADS = 64 * WM * WN;
-  constexpr int CA = BM * BK / 8 / THREADS;  // 16-byte activation chunks per thread per slab
+  constexpr int GT = 64 * GW;  // threads per group
+  constexpr int THREADS = GT * KG;
+  constexpr int CA = BM * BK / 8 / GT;  // 16-byte activation chunks per thread per slab
   constexpr int NW = Frag<BITS>::NW, NL = Frag<BITS>::NL;
   constexpr int NG = POST_SCALE ? 1 : 2;     // zero/scale pairs per column per slab (one per 32 k)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / WN, wn = wave % WN;
+  const int kg = wave / GW;        // K group
+  const int gwave = wave - kg * GW;  // wave within the group
+  const int gtid = tid - kg * GT;    // thread within the group
+  const int wm = gwave / WN, wn = gwave % WN;
   const int kc = lane >> 5;  // k chunk of the lane in a fragment
 
   const int tile = remap_block(blockIdx.x, g.mblocks * g.nblocks);
@@ -166,6 +177,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs g) {
   const int mb = tile - nb * g.mblocks;
   const int m0 = mb * BM, n0 = nb * BN;
   const int nk = (g.K + BK - 1) / BK;
+  const int ni = (nk + KG - 1) / KG;  // slabs per group (the last ones may pad)
+  auto gslab = [&](int i) { return kg + KG * i; };  // global slab of the group's i-th
 
   // Buffer resources: every global load below is a 32-bit per-lane offset
   // plus a scalar offset, which keeps address arithmetic out of the vector
@@ -176,14 +189,15 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs g) {
   const __amdgpu_buffer_rsrc_t rz = make_rsrc(g.zeros, (size_t)(g.K / 32 / g.upg) * g.N * 2);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(g.scales, (size_t)(g.K / 32 / g.upg) * g.N * 2);
 
-  // A (activations) go through LDS: rows a_row + (THREADS / 8) i, clamped to
+  // A (activations) go through LDS: rows a_row + (GT / 8) i, clamped to
   // M - 1 (rows beyond M only feed outputs that are never stored), 8 halves
   // at column chunk a_chk.
-  const int a_row = tid >> 3, a_chk = tid & 7;
+  const int a_row = gtid >> 3, a_chk = gtid & 7;
   uint32_t a_voff[CA];
 #pragma unroll
   for (int i = 0; i < CA; ++i)
-    a_voff[i] = (uint32_t)(min(m0 + a_row + (THREADS / 8) * i, g.M - 1) * g.K + 8 * a_chk) * 2u;
+    a_voff[i] = (uint32_t)(min(m0 + a_row + (GT / 8) * i, g.M - 1) * g.K + 8 * a_chk) * 2u;
+  f16* const glds = lds + kg * 3 * BM * LDK;  // the group's activation buffers
 
   // B (weights) go straight to registers: each lane reads the words of its
   // fragments. Columns beyond N are clamped to N - 1 (never stored).
@@ -200,7 +214,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs g) {
     for (int i = 0; i < CA; ++i) SA[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, a_voff[i] - adj, ks * BK * 2, 0);
   };
   auto storeA = [&](const u32x4 (&SA)[CA], int buf, int ks) {
-    f16* A = lds + buf * BM * LDK;
+    f16* A = glds + buf * BM * LDK;
     // Chunks at or past the end of K are stored as zeros: the second half of a
     // final 32-k slab, and the whole slab that pads an odd slab count.
     const bool zero = ks * BK + 8 * a_chk >= g.K;
@@ -208,11 +222,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs g) {
     for (int i = 0; i < CA; ++i) {
       u32x4 v = SA[i];
       if (zero) v = u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(A + (a_row + (THREADS / 8) * i) * LDK + 8 * a_chk) = v;
+      *reinterpret_cast<u32x4*>(A + (a_row + (GT / 8) * i) * LDK + 8 * a_chk) = v;
     }
   };
   auto frag_a = [&](int buf, int s, int t) {
-    const f16* A = lds + buf * BM * LDK;
+    const f16* A = glds + buf * BM * LDK;
     return *reinterpret_cast<const f16x8*>(A + ((BM / WM) * wm + 32 * t + (lane & 31)) * LDK + 16 * s + 8 * kc);
   };
 
@@ -315,8 +329,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs g) {
   // stored during step 2 into a buffer last read two slabs ago, and the one
   // barrier per slab sits before step 3, so the first fragments of the next
   // slab are read while step 3's MFMAs run.
-  auto slab = [&](auto fast_tag, int ks, BStep (&B)[4], ZS& Z) __attribute__((always_inline)) {
-    const int cur = ks % 3, nxt = (ks + 1) % 3;
+  auto slab = [&](auto fast_tag, int i, BStep (&B)[4], ZS& Z) __attribute__((always_inline)) {
+    const int cur = i % 3, nxt = (i + 1) % 3;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       // Scheduling fence: each step's instructions stay in their step.
@@ -327,10 +341,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs g) {
       f16x8 fb[TN];
 #pragma unroll
       for (int t = 0; t < TN; ++t) fb[t] = frag_b(fast_tag, B[s], Z, t, s);
-      loadB(B[s], ks + 2, s);
-      if (!POST_SCALE && s == 3) loadZS(Z, ks + 2);
-      if (s == 2) storeA(SA, nxt, ks + 1);
-      if (s == 3) loadA(SA, ks + 2);  // three steps before it is stored
+      loadB(B[s], gslab(i + 2), s);
+      if (!POST_SCALE && s == 3) loadZS(Z, gslab(i + 2));
+      if (s == 2) storeA(SA, nxt, gslab(i + 1));
+      if (s == 3) loadA(SA, gslab(i + 2));  // three steps before it is stored
 #pragma unroll
       for (int a = 0; a < TM; ++a)
 #pragma unroll
@@ -343,21 +357,21 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs g) {
   // and weights are zero (it adds nothing), so that the loop keeps one shape
   // and the accumulators one place.
   auto run = [&](auto fast_tag) __attribute__((always_inline)) {
-    for (int ks = 0; ks < nk; ks += 2) {
-      slab(fast_tag, ks, B0, Z0);
-      slab(fast_tag, ks + 1, B1, POST_SCALE ? Z0 : Z1);
+    for (int i = 0; i < ni; i += 2) {
+      slab(fast_tag, i, B0, Z0);
+      slab(fast_tag, i + 1, B1, POST_SCALE ? Z0 : Z1);
     }
   };
 
-  loadA(SA, 0);
+  loadA(SA, gslab(0));
 #pragma unroll
-  for (int s = 0; s < 4; ++s) loadB(B0[s], 0, s);
-  loadZS(Z0, 0);  // with one group per column: the only zero/scale load
+  for (int s = 0; s < 4; ++s) loadB(B0[s], gslab(0), s);
+  loadZS(Z0, gslab(0));  // with one group per column: the only zero/scale load
 #pragma unroll
-  for (int s = 0; s < 4; ++s) loadB(B1[s], 1, s);
-  if (!POST_SCALE) loadZS(Z1, 1);
-  storeA(SA, 0, 0);
-  loadA(SA, 1);
+  for (int s = 0; s < 4; ++s) loadB(B1[s], gslab(1), s);
+  if (!POST_SCALE) loadZS(Z1, gslab(1));
+  storeA(SA, 0, gslab(0));
+  loadA(SA, gslab(1));
   __syncthreads();
 #pragma unroll
   for (int t = 0; t < TM; ++t) fa[0][t] = frag_a(0, 0, t);
@@ -389,7 +403,34 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs g) {
     if constexpr (POST_SCALE) delta[t] = (half_bits_to_float(Z0.z[t][0]) + 1024.f) + (float)zc[t].x;
     off = off || delta[t] != 0.f;
   }
-  const bool need = __syncthreads_or(off);
+  const bool need = __syncthreads_or(off);  // every group is past its last slab
+  if constexpr (KG > 1) {
+    // Groups 1.. hand their sums to group 0 through LDS (over the activation
+    // buffers); group 0 adds them in group order.
+    float* part = reinterpret_cast<float*>(lds);
+    if (kg > 0) {
+#pragma unroll
+      for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int b = 0; b < TN; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            part[(((kg - 1) * GW + gwave) * ACC + (a * TN + b) * 16 + r) * 64 + lane] = acc[a][b][r];
+    }
+    __syncthreads();
+    if (kg == 0) {
+#pragma unroll
+      for (int j = 1; j < KG; ++j)
+#pragma unroll
+        for (int a = 0; a < TM; ++a)
+#pragma unroll
+          for (int b = 0; b < TN; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              acc[a][b][r] += part[(((j - 1) * GW + gwave) * ACC + (a * TN + b) * 16 + r) * 64 + lane];
+    }
+    __syncthreads();  // the output tile reuses the same LDS
+  }
   if (need) {
     for (int row = tid >> 3; row < BM; row += THREADS / 8) {
       const uint16_t* xr = g.x + (size_t)min(m0 + row, g.M - 1) * g.K;
@@ -428,8 +469,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs g) {
         }
     }
   };
-  if (need) emit(std::integral_constant<bool, true>{});
-  else emit(std::integral_constant<bool, false>{});
+  if (kg == 0) {  // scalar
+    if (need) emit(std::integral_constant<bool, true>{});
+    else emit(std::integral_constant<bool, false>{});
+  }
   __syncthreads();
 #pragma unroll 4
   for (int c = tid; c < BM * (BN / 8); c += THREADS) {
@@ -440,7 +483,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs g) {
   }
 }
 
-template <int BITS, int WM, int WN, int TM, int TN>
+template <int BITS, int WM, int WN, int TM, int TN, int KG>
 hipError_t launch_tiles(GemmArgs a, hipStream_t s) {
   constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN;
   a.mblocks = (a.M + BM - 1) / BM;
@@ -448,23 +491,24 @@ hipError_t launch_tiles(GemmArgs a, hipStream_t s) {
   const int nblocks = a.mblocks * a.nblocks;
   const bool post = a.upg * 32 == a.K;
   const bool tail = a.K % BK != 0;
-  constexpr int T = 64 * WM * WN;
-  if (post && !tail) gemm_kernel<BITS, true, false, WM, WN, TM, TN><<<nblocks, T, 0, s>>>(a);
-  else if (post) gemm_kernel<BITS, true, true, WM, WN, TM, TN><<<nblocks, T, 0, s>>>(a);
-  else if (!tail) gemm_kernel<BITS, false, false, WM, WN, TM, TN><<<nblocks, T, 0, s>>>(a);
-  else gemm_kernel<BITS, false, true, WM, WN, TM, TN><<<nblocks, T, 0, s>>>(a);
+  constexpr int T = 64 * WM * WN * KG;
+  if (post && !tail) gemm_kernel<BITS, true, false, WM, WN, TM, TN, KG><<<nblocks, T, 0, s>>>(a);
+  else if (post) gemm_kernel<BITS, true, true, WM, WN, TM, TN, KG><<<nblocks, T, 0, s>>>(a);
+  else if (!tail) gemm_kernel<BITS, false, false, WM, WN, TM, TN, KG><<<nblocks, T, 0, s>>>(a);
+  else gemm_kernel<BITS, false, true, WM, WN, TM, TN, KG><<<nblocks, T, 0, s>>>(a);
   return hipGetLastError();
 }
 
 // The largest block tile whose grid still gives every CU a block: 256 x 256
-// (8 waves of 128 x 64), else 128 x 128 (4 waves of 64 x 64), else 64 x 64
-// (4 waves of 32 x 32).
+// (8 waves of 128 x 64), else 128 x 128 (two K groups of 4 waves of 64 x 64),
+// else 64 x 64 (four K groups of 4 waves of 32 x 32). Smaller tiles have
+// short slabs, so their blocks split K to keep more loads in flight.
 template <int BITS>
 hipError_t launch_bits(const GemmArgs& a, hipStream_t s) {
   auto blocks = [&](int bm, int bn) { return (long long)((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn); };
-  if (blocks(256, 256) >= kCUs) return launch_tiles<BITS, 2, 4, 4, 2>(a, s);
-  if (blocks(128, 128) >= kCUs) return launch_tiles<BITS, 2, 2, 2, 2>(a, s);
-  return launch_tiles<BITS, 2, 2, 1, 1>(a, s);
+  if (blocks(256, 256) >= kCUs) return launch_tiles<BITS, 2, 4, 4, 2, 1>(a, s);
+  if (blocks(128, 128) >= kCUs) return launch_tiles<BITS, 2, 2, 2, 2, 2>(a, s);
+  return launch_tiles<BITS, 2, 2, 1, 1, 4>(a, s);
 }
 
 }  // namespace
