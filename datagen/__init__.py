@@ -86,21 +86,32 @@ def draw_zeros(G: int, N: int, lo: int, hi: int, seed: int = 0) -> np.ndarray:
     return z.astype(np.float16)
 
 
+def draw_scales_f32(G: int, N: int, lo: float, hi: float, seed: int = 0) -> np.ndarray:
+    """(G, N) float32 draws of a uniform real on [lo, hi)."""
+    return _rng(seed, _TAG_SCALES).uniform(lo, hi, size=(G, N)).astype(np.float32)
+
+
 def draw_scales(G: int, N: int, lo: float, hi: float, seed: int = 0) -> np.ndarray:
     """(G, N) fp16 scales, a uniform real on [lo, hi) rounded to fp16."""
     return _rng(seed, _TAG_SCALES).uniform(lo, hi, size=(G, N)).astype(np.float16)
 
 
+def draw_x_f32(M: int, K: int, seed: int = 0) -> np.ndarray:
+    """(M, K) float32 draws of N(0, 1)."""
+    return _rng(seed, _TAG_X).standard_normal(size=(M, K), dtype=np.float32)
+
+
 def draw_x(M: int, K: int, seed: int = 0) -> np.ndarray:
     """(M, K) fp16 activations, N(0, 1) rounded to fp16."""
-    return _rng(seed, _TAG_X).standard_normal(size=(M, K), dtype=np.float32).astype(np.float16)
+    return draw_x_f32(M, K, seed).astype(np.float16)
 
 
 def generate(w: Workload | str, seed: int | None = None, M: int | None = None) -> dict:
     """All inputs of one workload as numpy arrays.
 
     Returns ``codes`` (K, N) uint8, ``zeros`` and ``scales`` (G, N) float16 and
-    ``x`` (M, K) float16. ``M`` overrides the workload's row count (used for
+    ``x`` (M, K) float16, plus ``scales_f32`` and ``x_f32``, the same draws
+    before their rounding to fp16. ``M`` overrides the workload's row count (used for
     row-sampled checks of large products).
     """
     if isinstance(w, str):
@@ -108,11 +119,34 @@ def generate(w: Workload | str, seed: int | None = None, M: int | None = None) -
     s = w.seed if seed is None else seed
     m = w.M if M is None else M
     G = w.groups
+    x32 = draw_x_f32(m, w.K, s)
+    s32 = draw_scales_f32(G, w.N, w.scale_range[0], w.scale_range[1], s)
     return {
         "codes": draw_codes(w.K, w.N, w.bits, s),
         "zeros": draw_zeros(G, w.N, w.zero_range[0], w.zero_range[1], s),
         "scales": draw_scales(G, w.N, w.scale_range[0], w.scale_range[1], s),
-        "x": draw_x(m, w.K, s),
+        "x": x32.astype(np.float16),
+        # the same draws before their rounding to fp16 (for bf16 cases)
+        "scales_f32": s32,
+        "x_f32": x32,
+    }
+
+
+def round_to_bf16(values) -> np.ndarray:
+    """float32 values -> bf16 bit patterns (uint16), nearest even (the inputs' storage format)."""
+    u = np.asarray(values, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))
+    return (u >> np.uint64(16)).astype(np.uint16)
+
+
+def as_bf16_case(d: dict) -> dict:
+    """The same draws stored as bf16: x, scales and zero points re-rounded from the draws'
+    float32 values (integer zero points stay exact up to 256)."""
+    return {
+        "codes": d["codes"],
+        "zeros": round_to_bf16(d["zeros"].astype(np.float32)),
+        "scales": round_to_bf16(d["scales_f32"]),
+        "x": round_to_bf16(d["x_f32"]),
     }
 
 

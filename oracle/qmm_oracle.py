@@ -27,6 +27,13 @@ What it computes, step by step, in the order the sources state it:
   the accumulator starts from the bias).
 * The dequantized weight as fp16 (dashq_kernel.py, ``dequantize_weight``): the
   exact product rounded once to the nearest half, ties to even.
+* bf16 activations, scales, zero points and output (dashq_kernel.py: the module
+  keeps scales and zeros in its output dtype and returns the product in the
+  activations' dtype). bf16 values travel as uint16 bit patterns (numpy has no
+  bf16 type); they are decoded exactly and the same float64 reference applies.
+  The bf16 tolerance is re-derived from the format: one bf16 rounding of a
+  dequantized weight (2^-9) plus the bf16 output rounding (2^-9) plus fp32
+  accumulation (K 2^-24) stays below 5e-3 * sum_k |x_k w_kn| up to K = 16384.
 
 Arithmetic is float64 throughout. Every fp16 input is widened to float64
 exactly; for the workloads' integer zero points every product ``x * w`` is exact
@@ -49,6 +56,8 @@ SUPPORTED_BITS = (1, 2, 3, 4, 8)
 # Element-wise parity rule: |y - y_ref| <= REL_TOL * sum_k |x_k w_kn| + ABS_TOL.
 REL_TOL = 2e-3
 ABS_TOL = 1e-3
+# The same rule for bf16 data (see the module docstring for the derivation).
+REL_TOL_BF16 = 5e-3
 
 
 def elements_per_word(bits: int) -> int:
@@ -197,20 +206,51 @@ def quantized_matmul_codes(x, codes, zeros, scales, group_size: int, bias=None):
     return matmul(x, dequantize(codes, scales, zeros, group_size), bias)
 
 
-def parity_bound(a: np.ndarray) -> np.ndarray:
-    return REL_TOL * np.asarray(a, dtype=np.float64) + ABS_TOL
+def bf16_to_f64(bits) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float64, exactly: a bf16 value is the upper half of a binary32."""
+    b = np.asarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
 
 
-def parity_report(y_dev: np.ndarray, y_ref: np.ndarray, a: np.ndarray) -> dict:
-    """Compare a device result (any float dtype, decoded exactly) with the reference.
+def f64_to_bf16(v) -> np.ndarray:
+    """float64 -> bf16 bit patterns, rounded once to nearest, ties to even (finite values of the
+    bf16 normal range; larger magnitudes become infinities).
+
+    bf16 keeps 8 significant bits, so the float64 significand (53 bits) loses its low 45 bits:
+    they are rounded half to even on the integer bit pattern, which carries into the exponent
+    when the significand overflows.
+    """
+    d = np.asarray(v, dtype=np.float64)
+    u = d.view(np.uint64)
+    low = u & np.uint64((1 << 45) - 1)
+    q = u >> np.uint64(45)
+    half = np.uint64(1 << 44)
+    up = (low > half) | ((low == half) & ((q & np.uint64(1)) == np.uint64(1)))
+    q = q + up.astype(np.uint64)
+    r = (q << np.uint64(45)).view(np.float64)  # exactly representable in bf16 (and binary32)
+    return (r.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def dequantize_bf16(q: np.ndarray, scales_bf16, zeros_bf16, group_size: int) -> np.ndarray:
+    """(K, N) codes -> (K, N) bf16 bit patterns: the exact s * (q - z) rounded once to bf16."""
+    return f64_to_bf16(dequantize(q, bf16_to_f64(scales_bf16), bf16_to_f64(zeros_bf16), group_size))
+
+
+def parity_bound(a: np.ndarray, rel_tol: float = REL_TOL) -> np.ndarray:
+    return rel_tol * np.asarray(a, dtype=np.float64) + ABS_TOL
+
+
+def parity_report(y_dev: np.ndarray, y_ref: np.ndarray, a: np.ndarray, rel_tol: float = REL_TOL) -> dict:
+    """Compare a device result (float values, decoded exactly) with the reference.
 
     ``ok`` holds iff every element is finite and within the bound.
     ``max_ratio`` is the largest |err| / bound; the bound alone is loose, so a
-    healthy kernel sits far below 1.
+    healthy kernel sits far below 1. ``rel_tol`` is REL_TOL for fp16 data and
+    REL_TOL_BF16 for bf16 data.
     """
     yd = np.asarray(y_dev).astype(np.float64)
     err = np.abs(yd - y_ref)
-    bound = parity_bound(a)
+    bound = parity_bound(a, rel_tol)
     finite = np.isfinite(yd)
     ratio = np.where(finite, err / bound, np.inf)
     bad = ~finite | (err > bound)

@@ -47,3 +47,13 @@ def test_workload_shapes_and_ranges():
         assert abs(xs.mean()) < 0.1 and 0.9 < xs.std() < 1.1, name
         # every code value occurs
         assert len(np.unique(d["codes"][:64])) == 1 << w.bits, name
+
+
+def test_bf16_inputs_are_nearest_even_roundings():
+    """bf16 inputs are the draws rounded once to bf16 (compared with the oracle's own rounding)."""
+    import oracle
+    d = datagen.small_case(2, 64, 16, 4, 32, seed=3)
+    b = datagen.as_bf16_case(d)
+    assert np.array_equal(b["x"], oracle.f64_to_bf16(d["x_f32"].astype(np.float64)))
+    assert np.array_equal(b["scales"], oracle.f64_to_bf16(d["scales_f32"].astype(np.float64)))
+    assert np.array_equal(oracle.bf16_to_f64(b["zeros"]), d["zeros"].astype(np.float64))  # small integers: exact

@@ -42,7 +42,7 @@ def _t(a, dtype=None):
 
 
 def _to_gpu_case(d):
-    return {k: _t(v) for k, v in d.items()}
+    return {k: _t(v) for k, v in d.items() if not k.endswith("_f32")}
 
 
 def _pack_gpu(w, codes_np, bits):

@@ -131,6 +131,67 @@ def check_dequant_fp16_hand_worked():
         assert got == int(case["fp16_bits"], 16), (case["name"], hex(got))
 
 
+def check_bf16_decode_every_pattern():
+    """bf16_to_f64 agrees with the format's definition (sign, 8-bit exponent biased by 127, 7
+    fraction bits, subnormals) on every finite bit pattern."""
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    exp = (bits >> 7) & 0xFF
+    finite = exp != 0xFF
+    b = bits[finite]
+    e = ((b >> 7) & 0xFF).astype(np.int64)
+    f = (b & 0x7F).astype(np.float64)
+    sign = np.where(b >> 15, -1.0, 1.0)
+    want = np.where(e == 0, sign * f / 128.0 * 2.0 ** -126, sign * (1.0 + f / 128.0) * np.ldexp(1.0, e - 127))
+    got = oracle.bf16_to_f64(b.astype(np.uint16))
+    assert np.array_equal(got, want)
+
+
+def check_bf16_encode_hand_worked():
+    """f64_to_bf16 on the hand-worked values of tests/golden/dequant_examples.json, ties included."""
+    d = _load("dequant_examples.json")
+    for case in d["bf16_encode_cases"]:
+        got = int(oracle.f64_to_bf16(np.array([case["value"]]))[0])
+        assert got == int(case["bf16_bits"], 16), (case["name"], hex(got))
+    for case in d["bf16_dequant_cases"]:
+        s = np.array([[int(case["scale_bits"], 16)]], dtype=np.uint16)
+        z = oracle.f64_to_bf16(np.array([[float(case["zero"])]]))
+        q = np.array([[case["q"]]], dtype=np.uint8)
+        assert oracle.dequantize(q, oracle.bf16_to_f64(s), oracle.bf16_to_f64(z), -1)[0, 0] == case["exact"]
+        got = int(oracle.dequantize_bf16(q, s, z, -1)[0, 0])
+        assert got == int(case["bf16_bits"], 16), (case["name"], hex(got))
+
+
+def _round_half_even_bits(v: Fraction, frac_bits: int, emin: int) -> Fraction:
+    """v rounded to frac_bits fraction bits (nearest, ties to even), exponents down to emin."""
+    if v == 0:
+        return Fraction(0)
+    sign = -1 if v < 0 else 1
+    v = abs(v)
+    e = emin
+    while v >= Fraction(2) ** (e + 1):
+        e += 1
+    step = Fraction(2) ** (e - frac_bits)
+    n = v / step
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return sign * fl * step
+
+
+def check_bf16_encode_against_exact_rounding(seed=12):
+    """f64_to_bf16 equals exact rounding to 7 fraction bits on products of bf16 scales and codes."""
+    rng = np.random.default_rng(seed)
+    s = oracle.f64_to_bf16(rng.uniform(1e-4, 2.0, size=400))
+    z = oracle.f64_to_bf16(rng.uniform(-3.0, 260.0, size=400))
+    q = rng.integers(0, 256, size=400)
+    v = oracle.bf16_to_f64(s) * (q - oracle.bf16_to_f64(z))
+    got = oracle.bf16_to_f64(oracle.f64_to_bf16(v))
+    for i in range(400):
+        want = _round_half_even_bits(Fraction(float(v[i])), 7, -126)
+        assert got[i] == float(want), (i, v[i], got[i], float(want))
+
+
 def _round_half_even_fp16(v: Fraction) -> float:
     """The binary16 value nearest to v (ties to even), from the format's definition: 10 stored
     fraction bits, exponents -14..15, subnormals below 2^-14, overflow to infinity."""
@@ -337,6 +398,7 @@ CHECKS = [
     check_pack_words_hand_worked, check_ascending_nibbles, check_word_bijection,
     check_out_of_range_codes_masked, check_three_bit_identity, check_dequant_examples_hand_worked,
     check_dequant_fp16_hand_worked, check_dequant_fp16_against_exact_rounding, check_bias_row,
+    check_bf16_decode_every_pattern, check_bf16_encode_hand_worked, check_bf16_encode_against_exact_rounding,
     check_rational_brute_force, check_exact_integer_recomputation, check_closed_form_constant_scale_zero,
     check_group_minus_one_is_single_group, check_widths_agree_on_small_codes, check_one_hot_rows,
     check_parity_rule,
@@ -422,6 +484,11 @@ def _mut_fp16_truncates(q, scales, zeros, group_size):
     return t
 
 
+def _mut_bf16_truncates(v):
+    d = np.asarray(v, dtype=np.float64)
+    return (d.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
 MUTATIONS = {
     "pack_slot_reversed": ("pack_kmajor", _mut_pack_slot_reversed),
     "unpack_arith_shift": ("unpack_kmajor", _mut_unpack_arith_shift),
@@ -432,6 +499,7 @@ MUTATIONS = {
     "three_bit_planes_swapped": ("pack_3bit", _mut_3bit_planes_swapped),
     "matmul_drops_bias": ("matmul", _mut_matmul_drops_bias),
     "fp16_truncates": ("dequantize_fp16", _mut_fp16_truncates),
+    "bf16_truncates": ("f64_to_bf16", _mut_bf16_truncates),
 }
 
 
