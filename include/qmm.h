@@ -16,6 +16,10 @@
  * 3, 4 and 8 are supported (dashq_kernel.py, SUPPORTED_NBITS). An optional
  * bias row is added to the fp32 result before its rounding to fp16
  * (dashq_kernel.py, TritonQuantLinear: the accumulator starts from the bias).
+ * The _bf16 entry points take and return bfloat16 data instead of fp16 (x,
+ * zeros, scales, bias, y, w as bf16 bit patterns; dashq_kernel.py keeps
+ * scales and zeros in the module's output dtype and returns the product in
+ * the activations' dtype); everything else is the same.
  *
  * Conventions for every entry point:
  *  - Pointers to arrays are DEVICE pointers (memory of the current HIP
@@ -44,7 +48,7 @@
 extern "C" {
 #endif
 
-#define QMM_ABI_VERSION 2
+#define QMM_ABI_VERSION 3
 
 typedef enum qmm_status {
   QMM_OK = 0,
@@ -52,7 +56,7 @@ typedef enum qmm_status {
   QMM_ERR_BITS = 2,      /* bits not in {1, 2, 3, 4, 8}                             */
   QMM_ERR_SHAPE = 3,     /* M, K or N out of range or not a required multiple      */
   QMM_ERR_GROUP = 4,     /* group_size neither -1 nor a positive multiple of 32 dividing K */
-  QMM_ERR_ALIGN = 5,     /* a pointer is not 16-byte aligned                        */
+  QMM_ERR_ALIGN = 5,     /* a pointer is not aligned as its argument requires        */
   QMM_ERR_WORKSPACE = 6, /* workspace missing or smaller than qmm_workspace_bytes() */
   QMM_ERR_HIP = 7        /* the HIP runtime reported an error                       */
 } qmm_status;
@@ -102,12 +106,20 @@ qmm_status qmm_unpack(const int32_t* qweight, const int32_t* qweight_lo, int K, 
  *   zeros, scales         (G, N) fp16, G = K / group_size, or 1 if group_size == -1
  *   w                     (K, N) fp16 output
  * Requirements: K % 32 == 0, N >= 1, group_size == -1 or (group_size % 32 == 0
- * and K % group_size == 0). No alignment beyond the element size is needed.
+ * and K % group_size == 0). No alignment beyond the element size is needed
+ * (4 bytes for the packed words, 2 for zeros, scales and w; QMM_ERR_ALIGN).
  */
 qmm_status qmm_dequant(const int32_t* qweight, const int32_t* qweight_lo,
                        const uint16_t* zeros, const uint16_t* scales,
                        int K, int N, int bits, int group_size,
                        uint16_t* w, hipStream_t stream);
+
+/* qmm_dequant for bf16 scales and zero points; w is bf16, the exact product
+ * rounded once to bf16, nearest even. */
+qmm_status qmm_dequant_bf16(const int32_t* qweight, const int32_t* qweight_lo,
+                            const uint16_t* zeros, const uint16_t* scales,
+                            int K, int N, int bits, int group_size,
+                            uint16_t* w, hipStream_t stream);
 
 /*
  * qmm_workspace_bytes -- device workspace qmm_gemv needs for this problem
@@ -132,7 +144,7 @@ size_t qmm_workspace_bytes(int M, int K, int N, int bits, int group_size);
  *   workspace, workspace_bytes   see qmm_workspace_bytes
  * Requirements: K % 32 == 0, N % 8 == 0, N <= 1048576, group_size == -1 or
  * (group_size % 32 == 0 and K % group_size == 0); x, qweight, qweight_lo,
- * zeros, scales, y and workspace 16-byte aligned; x, each packed plane,
+ * zeros, scales, y and workspace 16-byte aligned, bias 2-byte aligned; x, each packed plane,
  * zeros and scales smaller than 4 GiB. Shapes whose activations or scales do
  * not fit the kernel's on-chip staging (M * K large, e.g. K > 32768 at
  * M = 16) are rejected with QMM_ERR_SHAPE; qmm_gemm takes them.
@@ -146,6 +158,16 @@ qmm_status qmm_gemv(const uint16_t* x, int M, int K,
                     int N, int bits, int group_size,
                     uint16_t* y, void* workspace, size_t workspace_bytes,
                     hipStream_t stream);
+
+/* qmm_gemv with bf16 x, zeros, scales, bias and y (the same workspace). The
+ * dequantized codes are formed in fp32 and rounded once to bf16 for the
+ * matrix cores; accumulation stays fp32 and y is rounded to nearest even. */
+qmm_status qmm_gemv_bf16(const uint16_t* x, int M, int K,
+                         const int32_t* qweight, const int32_t* qweight_lo,
+                         const uint16_t* zeros, const uint16_t* scales, const uint16_t* bias,
+                         int N, int bits, int group_size,
+                         uint16_t* y, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
 
 /*
  * qmm_gemm -- the same product for any M >= 1, the prefill product: packed
@@ -161,6 +183,13 @@ qmm_status qmm_gemm(const uint16_t* x, int M, int K,
                     const uint16_t* zeros, const uint16_t* scales, const uint16_t* bias,
                     int N, int bits, int group_size,
                     uint16_t* y, hipStream_t stream);
+
+/* qmm_gemm with bf16 x, zeros, scales, bias and y (as qmm_gemv_bf16). */
+qmm_status qmm_gemm_bf16(const uint16_t* x, int M, int K,
+                         const int32_t* qweight, const int32_t* qweight_lo,
+                         const uint16_t* zeros, const uint16_t* scales, const uint16_t* bias,
+                         int N, int bits, int group_size,
+                         uint16_t* y, hipStream_t stream);
 
 #ifdef __cplusplus
 }

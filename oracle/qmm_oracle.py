@@ -31,9 +31,11 @@ What it computes, step by step, in the order the sources state it:
   keeps scales and zeros in its output dtype and returns the product in the
   activations' dtype). bf16 values travel as uint16 bit patterns (numpy has no
   bf16 type); they are decoded exactly and the same float64 reference applies.
-  The bf16 tolerance is re-derived from the format: one bf16 rounding of a
-  dequantized weight (2^-9) plus the bf16 output rounding (2^-9) plus fp32
-  accumulation (K 2^-24) stays below 5e-3 * sum_k |x_k w_kn| up to K = 16384.
+  The bf16 tolerance is re-derived from the format: bf16 keeps 8 significant
+  bits, so one rounding to nearest errs by up to 2^-8 relative. One rounding
+  of each dequantized weight (2^-8), the output rounding (2^-8) and fp32
+  accumulation (K 2^-24) stay below 9e-3 * sum_k |x_k w_kn| up to K = 16384,
+  as the fp16 rule's 2e-3 covers 2 * 2^-11 + K 2^-24.
 
 Arithmetic is float64 throughout. Every fp16 input is widened to float64
 exactly; for the workloads' integer zero points every product ``x * w`` is exact
@@ -57,7 +59,7 @@ SUPPORTED_BITS = (1, 2, 3, 4, 8)
 REL_TOL = 2e-3
 ABS_TOL = 1e-3
 # The same rule for bf16 data (see the module docstring for the derivation).
-REL_TOL_BF16 = 5e-3
+REL_TOL_BF16 = 9e-3
 
 
 def elements_per_word(bits: int) -> int:

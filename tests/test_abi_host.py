@@ -26,13 +26,13 @@ def _lib():
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(qmm_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(qmm_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_boundary():
     assert _declared() == sorted(
         ["qmm_abi_version", "qmm_status_string", "qmm_last_error", "qmm_pack", "qmm_unpack", "qmm_dequant",
-         "qmm_workspace_bytes", "qmm_gemv", "qmm_gemm"])
+         "qmm_workspace_bytes", "qmm_gemv", "qmm_gemm", "qmm_dequant_bf16", "qmm_gemv_bf16", "qmm_gemm_bf16"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -49,7 +49,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = _lib()
-    assert lib.qmm_abi_version() == 2
+    assert lib.qmm_abi_version() == 3
     names = [lib.qmm_status_string(i).decode() for i in range(8)]
     assert names == ["QMM_OK", "QMM_ERR_NULL", "QMM_ERR_BITS", "QMM_ERR_SHAPE", "QMM_ERR_GROUP",
                      "QMM_ERR_ALIGN", "QMM_ERR_WORKSPACE", "QMM_ERR_HIP"]
@@ -75,17 +75,17 @@ A = 0x10000
 MIS = 0x10004
 
 
-def _gemv(lib, **kw):
+def _gemv(lib, suffix="", **kw):
     a = dict(x=A, M=1, K=256, qw=A, qlo=A, z=A, s=A, b=None, N=64, bits=4, gs=128, y=A, ws=A, wsb=1 << 30)
     a.update(kw)
-    return lib.qmm_gemv(a["x"], a["M"], a["K"], a["qw"], a["qlo"], a["z"], a["s"], a["b"], a["N"], a["bits"],
+    return getattr(lib, "qmm_gemv" + suffix)(a["x"], a["M"], a["K"], a["qw"], a["qlo"], a["z"], a["s"], a["b"], a["N"], a["bits"],
                         a["gs"], a["y"], a["ws"], a["wsb"], None)
 
 
-def _gemm(lib, **kw):
+def _gemm(lib, suffix="", **kw):
     a = dict(x=A, M=300, K=256, qw=A, qlo=A, z=A, s=A, b=None, N=64, bits=4, gs=128, y=A)
     a.update(kw)
-    return lib.qmm_gemm(a["x"], a["M"], a["K"], a["qw"], a["qlo"], a["z"], a["s"], a["b"], a["N"], a["bits"],
+    return getattr(lib, "qmm_gemm" + suffix)(a["x"], a["M"], a["K"], a["qw"], a["qlo"], a["z"], a["s"], a["b"], a["N"], a["bits"],
                         a["gs"], a["y"], None)
 
 
@@ -106,7 +106,10 @@ INVALID = [
     ("y_null", dict(y=None), 1),
     ("x_misaligned", dict(x=MIS), 5),
     ("zeros_misaligned", dict(z=MIS), 5),
+    ("bias_misaligned", dict(b=A + 1), 5),
 ]
+# fp16 and bf16 entry points validate alike.
+SUFFIXES = ("", "_bf16")
 
 
 @pytest.fixture
@@ -117,16 +120,18 @@ def host_only():
     return _lib()
 
 
+@pytest.mark.parametrize("suffix", SUFFIXES)
 @pytest.mark.parametrize("name,kw,want", INVALID, ids=[c[0] for c in INVALID])
-def test_gemv_rejects_before_launch(host_only, name, kw, want):
-    st = _gemv(host_only, **kw)
+def test_gemv_rejects_before_launch(host_only, name, kw, want, suffix):
+    st = _gemv(host_only, suffix, **kw)
     assert st == want, (name, st, host_only.qmm_last_error())
     assert host_only.qmm_last_error().decode() != ""
 
 
+@pytest.mark.parametrize("suffix", SUFFIXES)
 @pytest.mark.parametrize("name,kw,want", INVALID, ids=[c[0] for c in INVALID])
-def test_gemm_rejects_before_launch(host_only, name, kw, want):
-    assert _gemm(host_only, **kw) == want
+def test_gemm_rejects_before_launch(host_only, name, kw, want, suffix):
+    assert _gemm(host_only, suffix, **kw) == want
 
 
 def test_gemv_limits(host_only):
@@ -156,14 +161,17 @@ def test_pack_rejects_before_launch(host_only):
     assert lib.qmm_pack(A, 48, 8, 1, A, None, None, None) == 3   # K % 32 for 1-bit
 
 
-def test_dequant_rejects_before_launch(host_only):
+@pytest.mark.parametrize("suffix", SUFFIXES)
+def test_dequant_rejects_before_launch(host_only, suffix):
     lib = host_only
-    assert lib.qmm_dequant(A, A, A, A, 256, 64, 5, 128, A, None) == 2
-    assert lib.qmm_dequant(A, A, A, A, 48, 64, 4, -1, A, None) == 3      # K % 32
-    assert lib.qmm_dequant(A, A, A, A, 256, 64, 4, 48, A, None) == 4     # group size
-    assert lib.qmm_dequant(A, None, A, A, 256, 64, 3, 128, A, None) == 1  # no 1-bit plane
-    assert lib.qmm_dequant(A, A, None, A, 256, 64, 4, 128, A, None) == 1
-    assert lib.qmm_dequant(A, A, A, A, 256, 64, 4, 128, None, None) == 1
+    dq = getattr(lib, "qmm_dequant" + suffix)
+    assert dq(A, A, A, A, 256, 64, 5, 128, A, None) == 2
+    assert dq(A, A, A, A, 48, 64, 4, -1, A, None) == 3      # K % 32
+    assert dq(A, A, A, A, 256, 64, 4, 48, A, None) == 4     # group size
+    assert dq(A, None, A, A, 256, 64, 3, 128, A, None) == 1  # no 1-bit plane
+    assert dq(A, A, None, A, 256, 64, 4, 128, A, None) == 1
+    assert dq(A, A, A, A, 256, 64, 4, 128, None, None) == 1
+    assert dq(A, A, A, A, 256, 64, 4, 128, A + 1, None) == 5  # w not 2-byte aligned
     assert lib.qmm_last_error().decode() != ""
 
 

@@ -394,6 +394,51 @@ def check_parity_rule():
     assert not r["ok"] and r["nonfinite"] == 1
 
 
+def _two_roundings_worst(fmt):
+    """Largest relative error of the kernels' rounding model on one term: the
+    dequantized weight s * d rounded once to the format, its product with x
+    (exact in float64, exact in fp32) rounded once to the format. Brute force
+    over every significand of s and x in [1, 2) (every third one of s for fp16)
+    and every integer code difference d in 1..255."""
+    d = np.arange(1, 256, dtype=np.float64)
+    if fmt == "bf16":
+        sig = oracle.bf16_to_f64(np.arange(0x3F80, 0x4000, dtype=np.uint16))
+        s_vals, x_vals = sig, sig
+
+        def rnd(v):
+            return oracle.bf16_to_f64(oracle.f64_to_bf16(v))
+    else:
+        sig = np.arange(0x3C00, 0x4000, dtype=np.uint16).view(np.float16).astype(np.float64)
+        s_vals, x_vals = sig[::3], sig
+
+        def rnd(v):
+            return np.asarray(v, dtype=np.float64).astype(np.float16).astype(np.float64)
+    worst = 0.0
+    for s in s_vals:
+        w = s * d                      # exact
+        wq = rnd(w)
+        exact = x_vals[:, None] * w[None, :]
+        y = rnd(x_vals[:, None] * wq[None, :])
+        worst = max(worst, float(np.max(np.abs(y - exact) / exact)))
+    return worst
+
+
+def check_tolerance_covers_the_rounding_model():
+    """REL_TOL (fp16) and REL_TOL_BF16 must cover two roundings to the format
+    (weight and output) plus fp32 accumulation over up to K = 16384 terms
+    (K * 2^-24). A format with p significant bits rounds with relative error up
+    to 2^-p: 2^-11 for fp16, 2^-8 for bf16 (7 stored fraction bits plus the
+    implicit one)."""
+    acc = 16384 * 2.0 ** -24
+    for fmt, tol, p in (("fp16", oracle.REL_TOL, 11), ("bf16", oracle.REL_TOL_BF16, 8)):
+        worst = _two_roundings_worst(fmt)
+        u = 2.0 ** -p
+        assert worst <= 2 * u + u * u, (fmt, worst)   # the model's own bound
+        assert worst + acc <= tol, (fmt, worst, tol)
+    # the brute force reaches the bf16 worst case: both roundings at close to 2^-8
+    assert _two_roundings_worst("bf16") > 1.9 * 2.0 ** -8
+
+
 CHECKS = [
     check_pack_words_hand_worked, check_ascending_nibbles, check_word_bijection,
     check_out_of_range_codes_masked, check_three_bit_identity, check_dequant_examples_hand_worked,
@@ -401,7 +446,7 @@ CHECKS = [
     check_bf16_decode_every_pattern, check_bf16_encode_hand_worked, check_bf16_encode_against_exact_rounding,
     check_rational_brute_force, check_exact_integer_recomputation, check_closed_form_constant_scale_zero,
     check_group_minus_one_is_single_group, check_widths_agree_on_small_codes, check_one_hot_rows,
-    check_parity_rule,
+    check_parity_rule, check_tolerance_covers_the_rounding_model,
 ]
 
 

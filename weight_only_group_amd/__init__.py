@@ -9,13 +9,15 @@ Functions mirror the C ABI (include/qmm.h):
 
 * ``qmm_pack(codes, bits)`` -> ``(qweight, qweight_lo)``
 * ``qmm_unpack(qweight, qweight_lo, K, bits)`` -> codes
-* ``qmm_dequant(qweight, qweight_lo, zeros, scales, K, bits, group_size)`` -> (K, N) fp16
+* ``qmm_dequant(qweight, qweight_lo, zeros, scales, K, bits, group_size)`` -> (K, N)
 * ``qmm_gemv(x, qweight, qweight_lo, zeros, scales, bits, group_size, bias=None)`` (1 <= M <= 16)
 * ``qmm_gemm(x, qweight, qweight_lo, zeros, scales, bits, group_size, bias=None)`` (any M)
 * ``quantized_matmul(x, qweight, qzeros, scales, bits, group_size, qweight_lo=None, bias=None)``:
   the functional form, M <= 16 to the GEMV, larger M to the GEMM.
 
-Bit widths 1, 2, 3, 4 and 8.
+Bit widths 1, 2, 3, 4 and 8. The floating-point data (x, zeros, scales, bias,
+the result) are all float16 or all bfloat16; bfloat16 calls the ``_bf16``
+entry points of the ABI.
 """
 from __future__ import annotations
 
@@ -36,9 +38,10 @@ STATUS_NAMES = {
 # Every symbol the header declares.
 EXPORTS = (
     "qmm_abi_version", "qmm_status_string", "qmm_last_error", "qmm_pack", "qmm_unpack", "qmm_dequant",
-    "qmm_workspace_bytes", "qmm_gemv", "qmm_gemm",
+    "qmm_workspace_bytes", "qmm_gemv", "qmm_gemm", "qmm_dequant_bf16", "qmm_gemv_bf16", "qmm_gemm_bf16",
 )
-ABI_VERSION = 2
+ABI_VERSION = 3
+DTYPES = (torch.float16, torch.bfloat16)
 BITS = (1, 2, 3, 4, 8)
 GEMV_MAX_M = 16
 
@@ -64,14 +67,15 @@ def _declare(lib):
     lib.qmm_pack.argtypes = [P, I, I, I, P, P, P, P]
     lib.qmm_unpack.restype = I
     lib.qmm_unpack.argtypes = [P, P, I, I, I, P, P]
-    lib.qmm_dequant.restype = I
-    lib.qmm_dequant.argtypes = [P, P, P, P, I, I, I, I, P, P]
     lib.qmm_workspace_bytes.restype = SZ
     lib.qmm_workspace_bytes.argtypes = [I, I, I, I, I]
-    lib.qmm_gemv.restype = I
-    lib.qmm_gemv.argtypes = [P, I, I, P, P, P, P, P, I, I, I, P, P, SZ, P]
-    lib.qmm_gemm.restype = I
-    lib.qmm_gemm.argtypes = [P, I, I, P, P, P, P, P, I, I, I, P, P]
+    for suffix in ("", "_bf16"):
+        f = getattr(lib, "qmm_dequant" + suffix)
+        f.restype, f.argtypes = I, [P, P, P, P, I, I, I, I, P, P]
+        f = getattr(lib, "qmm_gemv" + suffix)
+        f.restype, f.argtypes = I, [P, I, I, P, P, P, P, P, I, I, I, P, P, SZ, P]
+        f = getattr(lib, "qmm_gemm" + suffix)
+        f.restype, f.argtypes = I, [P, I, I, P, P, P, P, P, I, I, I, P, P]
     if lib.qmm_abi_version() != ABI_VERSION:
         raise RuntimeError(f"libqmm ABI version {lib.qmm_abi_version()} does not match the binding's {ABI_VERSION}")
     return lib
@@ -158,15 +162,30 @@ def qmm_unpack(qweight: torch.Tensor, qweight_lo: torch.Tensor | None, K: int, b
     return codes
 
 
+def _data_dtype(t, name):
+    """The floating-point data type of a call, taken from its first float tensor."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in DTYPES:
+        raise TypeError(f"{name} must be float16 or bfloat16 (got {t.dtype})")
+    return t.dtype
+
+
+def _entry(name, dtype):
+    return getattr(library(), name + ("_bf16" if dtype == torch.bfloat16 else ""))
+
+
 def qmm_dequant(qweight, qweight_lo, zeros, scales, K: int, bits: int, group_size: int, out=None):
-    """The dequantized weight as (K, N) fp16: fp16(scale * (q - zero)), rounded once."""
+    """The dequantized weight as (K, N) in the scales' dtype (float16 or
+    bfloat16): scale * (q - zero), rounded once."""
+    dt = _data_dtype(scales, "scales")
     _gpu(qweight, "qweight", torch.int32)
     if bits == 3:
         if qweight_lo is None:
             raise ValueError("3-bit weights need qweight_lo (the 1-bit plane)")
         _gpu(qweight_lo, "qweight_lo", torch.int32)
-    _gpu(zeros, "zeros", torch.float16)
-    _gpu(scales, "scales", torch.float16)
+    _gpu(zeros, "zeros", dt)
+    _gpu(scales, "scales", dt)
     N = qweight.shape[1]
     if bits in BITS:
         shp, shp_lo = packed_shapes(K, N, bits)
@@ -175,10 +194,12 @@ def qmm_dequant(qweight, qweight_lo, zeros, scales, K: int, bits: int, group_siz
     if zeros.shape != scales.shape or zeros.shape[1] != N:
         raise ValueError("zeros and scales must both be (G, N)")
     dev = qweight.device
-    w = torch.empty((K, N), dtype=torch.float16, device=dev) if out is None else out
+    w = torch.empty((K, N), dtype=dt, device=dev) if out is None else _gpu(out, "out", dt)
+    if tuple(w.shape) != (K, N):
+        raise ValueError(f"out must be ({K}, {N})")
     with torch.cuda.device(dev):
-        _check(library().qmm_dequant(_ptr(qweight), _ptr(qweight_lo), _ptr(zeros), _ptr(scales), K, N, bits,
-                                     group_size, _ptr(w), _stream(dev)), "qmm_dequant")
+        _check(_entry("qmm_dequant", dt)(_ptr(qweight), _ptr(qweight_lo), _ptr(zeros), _ptr(scales), K, N, bits,
+                                         group_size, _ptr(w), _stream(dev)), "qmm_dequant")
     return w
 
 
@@ -204,23 +225,24 @@ def gemv_workspace(device, nbytes: int, stream=None) -> torch.Tensor | None:
     return ws
 
 
-def _check_bias(bias, N):
+def _check_bias(bias, N, dtype):
     if bias is None:
         return
-    _gpu(bias, "bias", torch.float16, ndim=1)
+    _gpu(bias, "bias", dtype, ndim=1)
     if bias.shape[0] != N:
         raise ValueError(f"bias must have N={N} elements")
 
 
 def _check_product_args(x, qweight, qweight_lo, zeros, scales, bits):
-    _gpu(x, "x", torch.float16)
+    dt = _data_dtype(x, "x")
+    _gpu(x, "x", dt)
     _gpu(qweight, "qweight", torch.int32)
     if bits == 3:
         if qweight_lo is None:
             raise ValueError("3-bit weights need qweight_lo (the 1-bit plane)")
         _gpu(qweight_lo, "qweight_lo", torch.int32)
-    _gpu(zeros, "zeros", torch.float16)
-    _gpu(scales, "scales", torch.float16)
+    _gpu(zeros, "zeros", dt)
+    _gpu(scales, "scales", dt)
     M, K = x.shape
     N = qweight.shape[1]
     if bits in BITS:
@@ -229,20 +251,29 @@ def _check_product_args(x, qweight, qweight_lo, zeros, scales, bits):
             raise ValueError(f"packed weight shapes {tuple(qweight.shape)} do not match K={K}, N={N}, bits={bits}")
     if zeros.shape != scales.shape or zeros.shape[1] != N:
         raise ValueError("zeros and scales must both be (G, N)")
-    return M, K, N
+    return M, K, N, dt
+
+
+def _output(out, M, N, dt, dev):
+    if out is None:
+        return torch.empty((M, N), dtype=dt, device=dev)
+    _gpu(out, "out", dt)
+    if tuple(out.shape) != (M, N):
+        raise ValueError(f"out must be ({M}, {N})")
+    return out
 
 
 def qmm_gemv(x, qweight, qweight_lo, zeros, scales, bits: int, group_size: int, out=None, workspace=None,
              bias=None):
-    """y = x @ dequantize(W) (+ bias) for 1 <= M <= 16; returns (M, N) fp16."""
-    M, K, N = _check_product_args(x, qweight, qweight_lo, zeros, scales, bits)
-    _check_bias(bias, N)
+    """y = x @ dequantize(W) (+ bias) for 1 <= M <= 16; returns (M, N) in x's dtype."""
+    M, K, N, dt = _check_product_args(x, qweight, qweight_lo, zeros, scales, bits)
+    _check_bias(bias, N, dt)
     dev = x.device
-    y = torch.empty((M, N), dtype=torch.float16, device=dev) if out is None else out
+    y = _output(out, M, N, dt, dev)
     nbytes = workspace_bytes(M, K, N, bits, group_size) if M <= GEMV_MAX_M else 0
     ws = workspace if workspace is not None else gemv_workspace(dev, nbytes)
     with torch.cuda.device(dev):
-        _check(library().qmm_gemv(_ptr(x), M, K, _ptr(qweight), _ptr(qweight_lo), _ptr(zeros), _ptr(scales),
+        _check(_entry("qmm_gemv", dt)(_ptr(x), M, K, _ptr(qweight), _ptr(qweight_lo), _ptr(zeros), _ptr(scales),
                                   _ptr(bias), N, bits, group_size, _ptr(y), _ptr(ws), 0 if ws is None else ws.numel(),
                                   _stream(dev)),
                "qmm_gemv")
@@ -250,13 +281,13 @@ def qmm_gemv(x, qweight, qweight_lo, zeros, scales, bits: int, group_size: int, 
 
 
 def qmm_gemm(x, qweight, qweight_lo, zeros, scales, bits: int, group_size: int, out=None, bias=None):
-    """y = x @ dequantize(W) (+ bias) for any M on the matrix cores; returns (M, N) fp16."""
-    M, K, N = _check_product_args(x, qweight, qweight_lo, zeros, scales, bits)
-    _check_bias(bias, N)
+    """y = x @ dequantize(W) (+ bias) for any M on the matrix cores; returns (M, N) in x's dtype."""
+    M, K, N, dt = _check_product_args(x, qweight, qweight_lo, zeros, scales, bits)
+    _check_bias(bias, N, dt)
     dev = x.device
-    y = torch.empty((M, N), dtype=torch.float16, device=dev) if out is None else out
+    y = _output(out, M, N, dt, dev)
     with torch.cuda.device(dev):
-        _check(library().qmm_gemm(_ptr(x), M, K, _ptr(qweight), _ptr(qweight_lo), _ptr(zeros), _ptr(scales),
+        _check(_entry("qmm_gemm", dt)(_ptr(x), M, K, _ptr(qweight), _ptr(qweight_lo), _ptr(zeros), _ptr(scales),
                                   _ptr(bias), N, bits, group_size, _ptr(y), _stream(dev)),
                "qmm_gemm")
     return y
@@ -265,7 +296,7 @@ def qmm_gemm(x, qweight, qweight_lo, zeros, scales, bits: int, group_size: int, 
 def quantized_matmul(x, qweight, qzeros, scales, bits: int, group_size: int, qweight_lo=None, bias=None):
     """output = x @ dequantize(qweight) (+ bias), in the argument order of the functional API.
 
-    ``qzeros`` are the (G, N) fp16 zero points; M <= 16 runs the decode GEMV
+    ``qzeros`` are the (G, N) zero points, in x's dtype (float16 or bfloat16); M <= 16 runs the decode GEMV
     (the GEMM when the GEMV's staging limits reject the shape), larger M the
     prefill GEMM.
     """

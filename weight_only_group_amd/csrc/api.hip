@@ -25,6 +25,7 @@ qmm_status ok() {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; }
 
 bool bits_ok(int bits) { return bits == 1 || bits == 2 || bits == 3 || bits == 4 || bits == 8; }
 
@@ -47,8 +48,8 @@ qmm_status check_group(int K, int group_size) {
 }
 
 qmm_status check_product(const uint16_t* x, int M, int K, const int32_t* qweight, const int32_t* qweight_lo,
-                         const uint16_t* zeros, const uint16_t* scales, int N, int bits, int group_size,
-                         const uint16_t* y, int max_m) {
+                         const uint16_t* zeros, const uint16_t* scales, const uint16_t* bias, int N, int bits,
+                         int group_size, const uint16_t* y, int max_m) {
   if (!bits_ok(bits)) return fail(QMM_ERR_BITS, "bits=%d is not one of 1, 2, 3, 4, 8", bits);
   if (M < 1 || M > max_m) return fail(QMM_ERR_SHAPE, "M=%d must be in [1, %d]", M, max_m);
   if (K < 32 || K % 32) return fail(QMM_ERR_SHAPE, "K=%d must be a positive multiple of 32", K);
@@ -69,12 +70,65 @@ qmm_status check_product(const uint16_t* x, int M, int K, const int32_t* qweight
   if (!aligned16(x) || !aligned16(qweight) || !aligned16(zeros) || !aligned16(scales) || !aligned16(y) ||
       (bits == 3 && !aligned16(qweight_lo)))
     return fail(QMM_ERR_ALIGN, "x, qweight, qweight_lo, zeros, scales and y must be 16-byte aligned");
+  if (!aligned(bias, 2)) return fail(QMM_ERR_ALIGN, "bias must be 2-byte aligned");
   return QMM_OK;
 }
 
 qmm_status from_hip(hipError_t e, const char* what) {
   if (e == hipSuccess) return ok();
   return fail(QMM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+qmm_status dequant_impl(const int32_t* qweight, const int32_t* qweight_lo, const uint16_t* zeros,
+                       const uint16_t* scales, int K, int N, int bits, int group_size, uint16_t* w,
+                       bool bf16, hipStream_t stream) {
+  qmm_status st = check_packing(K, N, bits, qweight, qweight_lo);
+  if (st != QMM_OK) return st;
+  if (K % 32) return fail(QMM_ERR_SHAPE, "K=%d must be a multiple of 32", K);
+  st = check_group(K, group_size);
+  if (st != QMM_OK) return st;
+  if (!zeros || !scales || !w) return fail(QMM_ERR_NULL, "zeros, scales and w must not be NULL");
+  if (!aligned(qweight, 4) || (bits == 3 && !aligned(qweight_lo, 4)) || !aligned(zeros, 2) || !aligned(scales, 2) ||
+      !aligned(w, 2))
+    return fail(QMM_ERR_ALIGN, "qweight and qweight_lo must be 4-byte aligned, zeros, scales and w 2-byte aligned");
+  return from_hip(qmm::launch_dequant(reinterpret_cast<const uint32_t*>(qweight),
+                                      reinterpret_cast<const uint32_t*>(qweight_lo), zeros, scales, K, N, bits,
+                                      group_size, w, bf16, stream),
+                  "qmm_dequant launch");
+}
+
+qmm_status gemv_impl(const uint16_t* x, int M, int K, const int32_t* qweight, const int32_t* qweight_lo,
+                    const uint16_t* zeros, const uint16_t* scales, const uint16_t* bias, int N, int bits,
+                    int group_size, uint16_t* y, void* workspace, size_t workspace_bytes, bool bf16,
+                    hipStream_t stream) {
+  qmm_status st = check_product(x, M, K, qweight, qweight_lo, zeros, scales, bias, N, bits, group_size, y, 16);
+  if (st != QMM_OK) return st;
+  if (N > qmm::kGemvMaxN) return fail(QMM_ERR_SHAPE, "N=%d exceeds the decode product's limit of %d", N, qmm::kGemvMaxN);
+  const qmm::GemvPlan plan = qmm::gemv_plan(M, K, N, bits, group_size);
+  if (!plan.valid)
+    return fail(QMM_ERR_SHAPE, "M=%d, K=%d, group_size=%d exceed the decode product's staging limits; use qmm_gemm",
+                M, K, group_size);
+  if (plan.workspace_bytes > 0) {
+    if (!workspace) return fail(QMM_ERR_WORKSPACE, "workspace is NULL but %zu bytes are needed", plan.workspace_bytes);
+    if (workspace_bytes < plan.workspace_bytes)
+      return fail(QMM_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, plan.workspace_bytes);
+    if (!aligned16(workspace)) return fail(QMM_ERR_ALIGN, "workspace must be 16-byte aligned");
+  }
+  return from_hip(qmm::launch_gemv(plan, x, M, K, reinterpret_cast<const uint32_t*>(qweight),
+                                   reinterpret_cast<const uint32_t*>(qweight_lo), zeros, scales, bias, N, bits,
+                                   group_size, y, workspace, bf16, stream),
+                  "qmm_gemv launch");
+}
+
+qmm_status gemm_impl(const uint16_t* x, int M, int K, const int32_t* qweight, const int32_t* qweight_lo,
+                    const uint16_t* zeros, const uint16_t* scales, const uint16_t* bias, int N, int bits,
+                    int group_size, uint16_t* y, bool bf16, hipStream_t stream) {
+  qmm_status st = check_product(x, M, K, qweight, qweight_lo, zeros, scales, bias, N, bits, group_size, y, 1 << 30);
+  if (st != QMM_OK) return st;
+  return from_hip(qmm::launch_gemm(x, M, K, reinterpret_cast<const uint32_t*>(qweight),
+                                   reinterpret_cast<const uint32_t*>(qweight_lo), zeros, scales, bias, N, bits,
+                                   group_size, y, bf16, stream),
+                  "qmm_gemm launch");
 }
 
 }  // namespace
@@ -119,58 +173,48 @@ qmm_status qmm_unpack(const int32_t* qweight, const int32_t* qweight_lo, int K, 
                   "qmm_unpack launch");
 }
 
-qmm_status qmm_dequant(const int32_t* qweight, const int32_t* qweight_lo, const uint16_t* zeros,
-                       const uint16_t* scales, int K, int N, int bits, int group_size, uint16_t* w,
-                       hipStream_t stream) {
-  qmm_status st = check_packing(K, N, bits, qweight, qweight_lo);
-  if (st != QMM_OK) return st;
-  if (K % 32) return fail(QMM_ERR_SHAPE, "K=%d must be a multiple of 32", K);
-  st = check_group(K, group_size);
-  if (st != QMM_OK) return st;
-  if (!zeros || !scales || !w) return fail(QMM_ERR_NULL, "zeros, scales and w must not be NULL");
-  return from_hip(qmm::launch_dequant(reinterpret_cast<const uint32_t*>(qweight),
-                                      reinterpret_cast<const uint32_t*>(qweight_lo), zeros, scales, K, N, bits,
-                                      group_size, w, stream),
-                  "qmm_dequant launch");
-}
-
 size_t qmm_workspace_bytes(int M, int K, int N, int bits, int group_size) {
   if (!bits_ok(bits) || M < 1 || M > 16 || K < 32 || K % 32 || N < 8 || N % 8 || N > qmm::kGemvMaxN) return 0;
   if (group_size != -1 && (group_size <= 0 || group_size % 32 || K % group_size)) return 0;
   return qmm::gemv_plan(M, K, N, bits, group_size).workspace_bytes;
 }
 
+qmm_status qmm_dequant(const int32_t* qweight, const int32_t* qweight_lo, const uint16_t* zeros,
+                       const uint16_t* scales, int K, int N, int bits, int group_size, uint16_t* w,
+                       hipStream_t stream) {
+  return dequant_impl(qweight, qweight_lo, zeros, scales, K, N, bits, group_size, w, false, stream);
+}
+
+qmm_status qmm_dequant_bf16(const int32_t* qweight, const int32_t* qweight_lo, const uint16_t* zeros,
+                            const uint16_t* scales, int K, int N, int bits, int group_size, uint16_t* w,
+                            hipStream_t stream) {
+  return dequant_impl(qweight, qweight_lo, zeros, scales, K, N, bits, group_size, w, true, stream);
+}
+
 qmm_status qmm_gemv(const uint16_t* x, int M, int K, const int32_t* qweight, const int32_t* qweight_lo,
                     const uint16_t* zeros, const uint16_t* scales, const uint16_t* bias, int N, int bits,
                     int group_size, uint16_t* y, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  qmm_status st = check_product(x, M, K, qweight, qweight_lo, zeros, scales, N, bits, group_size, y, 16);
-  if (st != QMM_OK) return st;
-  if (N > qmm::kGemvMaxN) return fail(QMM_ERR_SHAPE, "N=%d exceeds the decode product's limit of %d", N, qmm::kGemvMaxN);
-  const qmm::GemvPlan plan = qmm::gemv_plan(M, K, N, bits, group_size);
-  if (!plan.valid)
-    return fail(QMM_ERR_SHAPE, "M=%d, K=%d, group_size=%d exceed the decode product's staging limits; use qmm_gemm",
-                M, K, group_size);
-  if (plan.workspace_bytes > 0) {
-    if (!workspace) return fail(QMM_ERR_WORKSPACE, "workspace is NULL but %zu bytes are needed", plan.workspace_bytes);
-    if (workspace_bytes < plan.workspace_bytes)
-      return fail(QMM_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, plan.workspace_bytes);
-    if (!aligned16(workspace)) return fail(QMM_ERR_ALIGN, "workspace must be 16-byte aligned");
-  }
-  return from_hip(qmm::launch_gemv(plan, x, M, K, reinterpret_cast<const uint32_t*>(qweight),
-                                   reinterpret_cast<const uint32_t*>(qweight_lo), zeros, scales, bias, N, bits,
-                                   group_size, y, workspace, stream),
-                  "qmm_gemv launch");
+  return gemv_impl(x, M, K, qweight, qweight_lo, zeros, scales, bias, N, bits, group_size, y, workspace,
+                   workspace_bytes, false, stream);
+}
+
+qmm_status qmm_gemv_bf16(const uint16_t* x, int M, int K, const int32_t* qweight, const int32_t* qweight_lo,
+                         const uint16_t* zeros, const uint16_t* scales, const uint16_t* bias, int N, int bits,
+                         int group_size, uint16_t* y, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return gemv_impl(x, M, K, qweight, qweight_lo, zeros, scales, bias, N, bits, group_size, y, workspace,
+                   workspace_bytes, true, stream);
 }
 
 qmm_status qmm_gemm(const uint16_t* x, int M, int K, const int32_t* qweight, const int32_t* qweight_lo,
                     const uint16_t* zeros, const uint16_t* scales, const uint16_t* bias, int N, int bits,
                     int group_size, uint16_t* y, hipStream_t stream) {
-  qmm_status st = check_product(x, M, K, qweight, qweight_lo, zeros, scales, N, bits, group_size, y, 1 << 30);
-  if (st != QMM_OK) return st;
-  return from_hip(qmm::launch_gemm(x, M, K, reinterpret_cast<const uint32_t*>(qweight),
-                                   reinterpret_cast<const uint32_t*>(qweight_lo), zeros, scales, bias, N, bits,
-                                   group_size, y, stream),
-                  "qmm_gemm launch");
+  return gemm_impl(x, M, K, qweight, qweight_lo, zeros, scales, bias, N, bits, group_size, y, false, stream);
+}
+
+qmm_status qmm_gemm_bf16(const uint16_t* x, int M, int K, const int32_t* qweight, const int32_t* qweight_lo,
+                         const uint16_t* zeros, const uint16_t* scales, const uint16_t* bias, int N, int bits,
+                         int group_size, uint16_t* y, hipStream_t stream) {
+  return gemm_impl(x, M, K, qweight, qweight_lo, zeros, scales, bias, N, bits, group_size, y, true, stream);
 }
 
 }  // extern "C"

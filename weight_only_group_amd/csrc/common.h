@@ -14,6 +14,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 // Two fp16 1024.0 values. OR-ing a code q < 1024 into the low mantissa bits of
 // a half gives exactly 1024 + q, so one integer op turns two codes into two
@@ -24,6 +27,24 @@ __device__ __forceinline__ f16x2 as_f16x2(uint32_t u) { return __builtin_bit_cas
 __device__ __forceinline__ uint32_t as_u32(f16x2 h) { return __builtin_bit_cast(uint32_t, h); }
 __device__ __forceinline__ float half_bits_to_float(uint16_t b) {
   return (float)__builtin_bit_cast(f16, b);
+}
+
+// 16-bit floating-point data is stored as bit patterns: IEEE binary16 (BF
+// false) or bfloat16 (BF true, the upper half of a binary32).
+template <bool BF>
+__device__ __forceinline__ float bits_to_float(uint16_t b) {
+  if constexpr (BF) return __builtin_bit_cast(float, (uint32_t)b << 16);
+  else return (float)__builtin_bit_cast(f16, b);
+}
+// Rounded to nearest, ties to even.
+template <bool BF>
+__device__ __forceinline__ uint16_t float_to_bits(float v) {
+  if constexpr (BF) return __builtin_bit_cast(uint16_t, (bf16)v);
+  else return __builtin_bit_cast(uint16_t, (f16)v);
+}
+// Two floats as a bf16 pair (element 0 in the low half), each rounded to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, bf16x2{(bf16)lo, (bf16)hi});
 }
 
 // Rows of the weight per group: group_size, or K for group_size == -1.
@@ -51,20 +72,21 @@ struct GemvPlan {
   int valid;        // 0: the shape does not fit the decode product's staging limits
 };
 GemvPlan gemv_plan(int M, int K, int N, int bits, int group_size);
+// bf16: x, zeros, scales, bias and y hold bfloat16 instead of fp16 bit patterns.
 hipError_t launch_gemv(const GemvPlan& p, const uint16_t* x, int M, int K, const uint32_t* qw,
                        const uint32_t* qlo, const uint16_t* zeros, const uint16_t* scales,
                        const uint16_t* bias, int N, int bits, int group_size, uint16_t* y,
-                       void* workspace, hipStream_t stream);
+                       void* workspace, bool bf16, hipStream_t stream);
 
 // ---- prefill GEMM ---------------------------------------------------------
 hipError_t launch_gemm(const uint16_t* x, int M, int K, const uint32_t* qw, const uint32_t* qlo,
                        const uint16_t* zeros, const uint16_t* scales, const uint16_t* bias, int N,
-                       int bits, int group_size, uint16_t* y, hipStream_t stream);
+                       int bits, int group_size, uint16_t* y, bool bf16, hipStream_t stream);
 
 // ---- dequantize to fp16 -------------------------------------------------------
 hipError_t launch_dequant(const uint32_t* qw, const uint32_t* qlo, const uint16_t* zeros,
                           const uint16_t* scales, int K, int N, int bits, int group_size, uint16_t* w,
-                          hipStream_t stream);
+                          bool bf16, hipStream_t stream);
 
 // ---- pack / unpack ----------------------------------------------------------
 hipError_t launch_pack(const uint8_t* codes, int K, int N, int bits, uint32_t* qw, uint32_t* qlo,

@@ -11,7 +11,11 @@
 // one of the 1-bit plane), the chunk's zero point and scale once (32 divides
 // the group size), and writes 32 halves down its column. Consecutive threads
 // take consecutive columns, so each row of stores of a wave is contiguous.
-// This is a one-off HBM stream (2 bytes written per weight).
+// This is a one-off HBM stream (2 bytes written per weight). With bf16 data
+// (scales, zero points and the output in bfloat16) the fp64 product is rounded
+// once to bf16: first to binary32 rounding to odd (truncate, then set the last
+// bit if anything was dropped), then to bf16 to nearest even, which equals one
+// direct rounding since binary32 keeps more than two extra bits.
 #include "common.h"
 
 namespace qmm {
@@ -32,7 +36,20 @@ __device__ __forceinline__ uint32_t code_at(const uint32_t (&wd)[words_per_chunk
   }
 }
 
-template <int BITS>
+// fp64 -> bf16 bits, rounded once to nearest even (finite values).
+__device__ __forceinline__ uint16_t f64_to_bf16_bits(double d) {
+  const float f = (float)d;  // nearest binary32
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  const double back = (double)f;
+  if (back != d) {
+    if (__builtin_fabs(back) > __builtin_fabs(d)) u -= 1u;  // truncate: one step toward zero
+    u |= 1u;                                                 // round to odd
+  }
+  u += 0x7FFFu + ((u >> 16) & 1u);  // nearest even at 16 bits
+  return (uint16_t)(u >> 16);
+}
+
+template <int BITS, bool BF>
 __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint32_t* __restrict__ qw,
                                                            const uint32_t* __restrict__ qlo,
                                                            const uint16_t* __restrict__ zeros,
@@ -49,40 +66,47 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint32_t* __res
   for (int r = 0; r < NWORDS; ++r) wd[r] = qw[(size_t)(c * NWORDS + r) * N + n];
   const uint32_t lo = BITS == 3 ? qlo[(size_t)c * N + n] : 0u;
   const int g = (32 * c) / rows_per_group;
-  const double s = (double)half_bits_to_float(scales[(size_t)g * N + n]);
-  const double z = (double)half_bits_to_float(zeros[(size_t)g * N + n]);
+  const double s = (double)bits_to_float<BF>(scales[(size_t)g * N + n]);
+  const double z = (double)bits_to_float<BF>(zeros[(size_t)g * N + n]);
   uint16_t* col = w + (size_t)32 * c * N + n;
 #pragma unroll
   for (int k = 0; k < 32; ++k) {
     const double v = ((double)code_at<BITS>(wd, lo, k) - z) * s;
-    col[(size_t)k * N] = __builtin_bit_cast(uint16_t, (f16)v);
+    col[(size_t)k * N] = BF ? f64_to_bf16_bits(v) : __builtin_bit_cast(uint16_t, (f16)v);
   }
 }
 
-template <int BITS>
+template <int BITS, bool BF>
 hipError_t launch_typed(const uint32_t* qw, const uint32_t* qlo, const uint16_t* zeros, const uint16_t* scales,
                         int K, int N, int rows_per_group, uint16_t* w, hipStream_t s) {
   const long long total = (long long)(K / 32) * N;
   if (total == 0) return hipSuccess;
   const unsigned blocks = (unsigned)((total + kThreads - 1) / kThreads);
-  dequant_kernel<BITS><<<blocks, kThreads, 0, s>>>(qw, qlo, zeros, scales, K, N, rows_per_group, w);
+  dequant_kernel<BITS, BF><<<blocks, kThreads, 0, s>>>(qw, qlo, zeros, scales, K, N, rows_per_group, w);
   return hipGetLastError();
+}
+
+template <bool BF>
+hipError_t launch_dtype(const uint32_t* qw, const uint32_t* qlo, const uint16_t* zeros, const uint16_t* scales,
+                        int K, int N, int bits, int rows, uint16_t* w, hipStream_t s) {
+  switch (bits) {
+    case 1: return launch_typed<1, BF>(qw, qlo, zeros, scales, K, N, rows, w, s);
+    case 2: return launch_typed<2, BF>(qw, qlo, zeros, scales, K, N, rows, w, s);
+    case 3: return launch_typed<3, BF>(qw, qlo, zeros, scales, K, N, rows, w, s);
+    case 4: return launch_typed<4, BF>(qw, qlo, zeros, scales, K, N, rows, w, s);
+    case 8: return launch_typed<8, BF>(qw, qlo, zeros, scales, K, N, rows, w, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
 
 hipError_t launch_dequant(const uint32_t* qw, const uint32_t* qlo, const uint16_t* zeros,
                           const uint16_t* scales, int K, int N, int bits, int group_size, uint16_t* w,
-                          hipStream_t s) {
+                          bool bf16, hipStream_t s) {
   const int rows = group_rows(K, group_size);
-  switch (bits) {
-    case 1: return launch_typed<1>(qw, qlo, zeros, scales, K, N, rows, w, s);
-    case 2: return launch_typed<2>(qw, qlo, zeros, scales, K, N, rows, w, s);
-    case 3: return launch_typed<3>(qw, qlo, zeros, scales, K, N, rows, w, s);
-    case 4: return launch_typed<4>(qw, qlo, zeros, scales, K, N, rows, w, s);
-    case 8: return launch_typed<8>(qw, qlo, zeros, scales, K, N, rows, w, s);
-    default: return hipErrorInvalidValue;
-  }
+  return bf16 ? launch_dtype<true>(qw, qlo, zeros, scales, K, N, bits, rows, w, s)
+              : launch_dtype<false>(qw, qlo, zeros, scales, K, N, bits, rows, w, s);
 }
 
 }  // namespace qmm

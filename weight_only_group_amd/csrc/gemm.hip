@@ -146,7 +146,9 @@ constexpr int cmax(int a, int b) { return a > b ? a : b; }
 // WM x WN waves, each wave TM x TN MFMA tiles of 32 x 32. Group j takes the
 // 64-k slabs j, j + KG, j + 2 KG, ... with LDS buffers of its own; the groups'
 // fp32 sums are added in group order at the end.
-template <int BITS, bool POST_SCALE, bool KTAIL, int WM, int WN, int TM, int TN, int KG>
+// BF: bf16 data (x, scales, zero points, bias, y); dequantized codes are then
+// formed in fp32 and rounded once to bf16 for the bf16 matrix-core form.
+template <int BITS, bool POST_SCALE, bool KTAIL, int WM, int WN, int TM, int TN, int KG, bool BF>
 __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) {
   constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN;
   constexpr int LDY = BN + 8;  // halves per LDS row of the staged output tile
@@ -277,6 +279,7 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
   // codes dequantize with one packed add. The remainder z - round(z) (zero
   // for integer zero points) is taken out in the epilogue.
   f16x2 zc[TN];
+  float czf[TN];  // bf16 data, one group per column: 1024 + z in fp32
   // Steps past the end of K (and the padding slab) need no masking here:
   // their activations are stored as zeros, and the weights they meet are
   // finite values of row 0 or of the last slab.
@@ -284,7 +287,22 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
     constexpr bool FAST = decltype(fast_tag)::value;
     uint32_t h[4], d[4];
     frag_codes<BITS>(S.w[t], S.l[t], kc, s, h);
-    if constexpr (FAST) {
+    if constexpr (BF) {
+      // (1024 + q) - (1024 + z) in fp32 (times the group's scale), one rounding to bf16
+      float cz, sc = 1.f;
+      if constexpr (POST_SCALE) {
+        cz = czf[t];
+      } else {
+        cz = 1024.f + bits_to_float<true>(Z.z[t][s >> 1]);
+        sc = bits_to_float<true>(Z.s[t][s >> 1]);
+      }
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const f16x2 hp = as_f16x2(h[p]);
+        d[p] = POST_SCALE ? pack_bf16((float)hp.x - cz, (float)hp.y - cz)
+                          : pack_bf16(((float)hp.x - cz) * sc, ((float)hp.y - cz) * sc);
+      }
+    } else if constexpr (FAST) {
 #pragma unroll
       for (int p = 0; p < 4; ++p) d[p] = as_u32(as_f16x2(h[p]) + zc[t]);
     } else {
@@ -348,8 +366,13 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
 #pragma unroll
       for (int a = 0; a < TM; ++a)
 #pragma unroll
-        for (int b = 0; b < TN; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[s & 1][a], fb[b], acc[a][b], 0, 0, 0);
+        for (int b = 0; b < TN; ++b) {
+          if constexpr (BF)
+            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa[s & 1][a]),
+                                                                 __builtin_bit_cast(bf16x8, fb[b]), acc[a][b], 0, 0, 0);
+          else
+            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[s & 1][a], fb[b], acc[a][b], 0, 0, 0);
+        }
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -379,8 +402,12 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
   if constexpr (POST_SCALE) {
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
-      const f16 c = (f16)((f16)(-1024.f) - __builtin_bit_cast(f16, Z0.z[t][0]));
-      zc[t] = f16x2{c, c};
+      if constexpr (BF) {
+        czf[t] = 1024.f + bits_to_float<true>(Z0.z[t][0]);
+      } else {
+        const f16 c = (f16)((f16)(-1024.f) - __builtin_bit_cast(f16, Z0.z[t][0]));
+        zc[t] = f16x2{c, c};
+      }
     }
   }
   run(std::integral_constant<bool, POST_SCALE>{});
@@ -400,7 +427,7 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
 #pragma unroll
   for (int t = 0; t < TN; ++t) {
     delta[t] = 0.f;
-    if constexpr (POST_SCALE) delta[t] = (half_bits_to_float(Z0.z[t][0]) + 1024.f) + (float)zc[t].x;
+    if constexpr (POST_SCALE && !BF) delta[t] = (half_bits_to_float(Z0.z[t][0]) + 1024.f) + (float)zc[t].x;
     off = off || delta[t] != 0.f;
   }
   const bool need = __syncthreads_or(off);  // every group is past its last slab
@@ -457,15 +484,15 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
     for (int b = 0; b < TN; ++b) {
       const int col = (BN / WN) * wn + 32 * b + (lane & 31);
       float sc = 1.f, bv = 0.f;
-      if constexpr (POST_SCALE) sc = half_bits_to_float(g.scales[min(n0 + col, g.N - 1)]);
-      if (g.bias) bv = half_bits_to_float(g.bias[min(n0 + col, g.N - 1)]);
+      if constexpr (POST_SCALE) sc = bits_to_float<BF>(g.scales[min(n0 + col, g.N - 1)]);
+      if (g.bias) bv = bits_to_float<BF>(g.bias[min(n0 + col, g.N - 1)]);
 #pragma unroll
       for (int a = 0; a < TM; ++a)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float v = acc[a][b][r];
           if constexpr (NEED) v -= delta[b] * rsum[acc_row(a, r)];
-          lds[acc_row(a, r) * LDY + col] = (f16)(v * sc + bv);
+          lds[acc_row(a, r) * LDY + col] = __builtin_bit_cast(f16, float_to_bits<BF>(v * sc + bv));
         }
     }
   };
@@ -483,7 +510,7 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
   }
 }
 
-template <int BITS, int WM, int WN, int TM, int TN, int KG>
+template <int BITS, int WM, int WN, int TM, int TN, int KG, bool BF>
 hipError_t launch_tiles(GemmArgs a, hipStream_t s) {
   constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN;
   a.mblocks = (a.M + BM - 1) / BM;
@@ -492,10 +519,10 @@ hipError_t launch_tiles(GemmArgs a, hipStream_t s) {
   const bool post = a.upg * 32 == a.K;
   const bool tail = a.K % BK != 0;
   constexpr int T = 64 * WM * WN * KG;
-  if (post && !tail) gemm_kernel<BITS, true, false, WM, WN, TM, TN, KG><<<nblocks, T, 0, s>>>(a);
-  else if (post) gemm_kernel<BITS, true, true, WM, WN, TM, TN, KG><<<nblocks, T, 0, s>>>(a);
-  else if (!tail) gemm_kernel<BITS, false, false, WM, WN, TM, TN, KG><<<nblocks, T, 0, s>>>(a);
-  else gemm_kernel<BITS, false, true, WM, WN, TM, TN, KG><<<nblocks, T, 0, s>>>(a);
+  if (post && !tail) gemm_kernel<BITS, true, false, WM, WN, TM, TN, KG, BF><<<nblocks, T, 0, s>>>(a);
+  else if (post) gemm_kernel<BITS, true, true, WM, WN, TM, TN, KG, BF><<<nblocks, T, 0, s>>>(a);
+  else if (!tail) gemm_kernel<BITS, false, false, WM, WN, TM, TN, KG, BF><<<nblocks, T, 0, s>>>(a);
+  else gemm_kernel<BITS, false, true, WM, WN, TM, TN, KG, BF><<<nblocks, T, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -503,19 +530,31 @@ hipError_t launch_tiles(GemmArgs a, hipStream_t s) {
 // (8 waves of 128 x 64), else 128 x 128 (two K groups of 4 waves of 64 x 64),
 // else 64 x 64 (four K groups of 4 waves of 32 x 32). Smaller tiles have
 // short slabs, so their blocks split K to keep more loads in flight.
-template <int BITS>
+template <int BITS, bool BF>
 hipError_t launch_bits(const GemmArgs& a, hipStream_t s) {
   auto blocks = [&](int bm, int bn) { return (long long)((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn); };
-  if (blocks(256, 256) >= kCUs) return launch_tiles<BITS, 2, 4, 4, 2, 1>(a, s);
-  if (blocks(128, 128) >= kCUs) return launch_tiles<BITS, 2, 2, 2, 2, 2>(a, s);
-  return launch_tiles<BITS, 2, 2, 1, 1, 4>(a, s);
+  if (blocks(256, 256) >= kCUs) return launch_tiles<BITS, 2, 4, 4, 2, 1, BF>(a, s);
+  if (blocks(128, 128) >= kCUs) return launch_tiles<BITS, 2, 2, 2, 2, 2, BF>(a, s);
+  return launch_tiles<BITS, 2, 2, 1, 1, 4, BF>(a, s);
+}
+
+template <bool BF>
+hipError_t launch_dtype(const GemmArgs& a, int bits, hipStream_t s) {
+  switch (bits) {
+    case 1: return launch_bits<1, BF>(a, s);
+    case 2: return launch_bits<2, BF>(a, s);
+    case 3: return launch_bits<3, BF>(a, s);
+    case 4: return launch_bits<4, BF>(a, s);
+    case 8: return launch_bits<8, BF>(a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
 
 hipError_t launch_gemm(const uint16_t* x, int M, int K, const uint32_t* qw, const uint32_t* qlo,
                        const uint16_t* zeros, const uint16_t* scales, const uint16_t* bias, int N, int bits,
-                       int group_size, uint16_t* y, hipStream_t s) {
+                       int group_size, uint16_t* y, bool bf16, hipStream_t s) {
   GemmArgs a;
   a.x = x;
   a.qw = qw;
@@ -531,14 +570,7 @@ hipError_t launch_gemm(const uint16_t* x, int M, int K, const uint32_t* qw, cons
   a.upg_log2 = -1;
   for (int l = 0; l < 31; ++l)
     if ((1 << l) == a.upg) a.upg_log2 = l;
-  switch (bits) {
-    case 1: return launch_bits<1>(a, s);
-    case 2: return launch_bits<2>(a, s);
-    case 3: return launch_bits<3>(a, s);
-    case 4: return launch_bits<4>(a, s);
-    case 8: return launch_bits<8>(a, s);
-    default: return hipErrorInvalidValue;
-  }
+  return bf16 ? launch_dtype<true>(a, bits, s) : launch_dtype<false>(a, bits, s);
 }
 
 }  // namespace qmm

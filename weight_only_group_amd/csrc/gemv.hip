@@ -238,7 +238,9 @@ __device__ __forceinline__ int unit_rows(int w) {
 constexpr int stage_bytes(int waves) { return waves * 5 * 1024; }
 constexpr int kXPerThread = 4;  // activation slots one thread stages at most
 
-template <int BITS, int VEC, int WAVES>
+// BF: bf16 data (x, scales, zero points, bias, y); the dequantized codes are
+// then formed in fp32 and rounded once to bf16 for the bf16 matrix-core form.
+template <int BITS, int VEC, int WAVES, bool BF>
 __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs g) {
   constexpr int NW = Bits<BITS>::NW;
   constexpr int CH = chunk_units<BITS, VEC, WAVES>();
@@ -342,14 +344,16 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs g) {
     const int mm = sl >> (ubp_log2 + 2), uu = (sl >> 2) & ((1 << ubp_log2) - 1);
     if (mm < g.M && uu < nub) xs[sl] = x_operand<BITS>(xraw[i]);
   }
-  bool exact = true;
+  bool exact = !BF;
   if (sz_on) {
     *reinterpret_cast<u32x4*>(szs + sz_row * COLS + 8 * sz_cp) = sraw;
     *reinterpret_cast<u32x4*>(szs + ((1 << g.gp_log2) + sz_row) * COLS + 8 * sz_cp) = zraw;
+    if constexpr (!BF) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float z = half_bits_to_float((uint16_t)(zraw[e >> 1] >> (16 * (e & 1))));
-      exact = exact && (z == __builtin_rintf(z)) && (__builtin_fabsf(z) <= 1024.f);
+      for (int e = 0; e < 8; ++e) {
+        const float z = half_bits_to_float((uint16_t)(zraw[e >> 1] >> (16 * (e & 1))));
+        exact = exact && (z == __builtin_rintf(z)) && (__builtin_fabsf(z) <= 1024.f);
+      }
     }
   }
   const bool wave_ok = __all(exact);
@@ -371,10 +375,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs g) {
     f32x4 acc[2][VEC];
 #pragma unroll
     for (int v = 0; v < VEC; ++v) acc[0][v] = acc[1][v] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float sc[VEC];
+    float sc[VEC], czf[VEC];  // scale; 1024 + z in fp32 (bf16 data)
     f16x2 zc[VEC];  // -(1024 + z) on the exact path, else -z (1024 removed separately)
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) { sc[v] = 0.f; zc[v] = f16x2{0, 0}; }
+    for (int v = 0; v < VEC; ++v) { sc[v] = 0.f; czf[v] = 0.f; zc[v] = f16x2{0, 0}; }
     int cur_g = -1;
     auto chunk = [&](int base) {
 #pragma unroll
@@ -397,29 +401,44 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs g) {
               *reinterpret_cast<const typename Halves<VEC>::T*>(srow + (COLS << g.gp_log2));
 #pragma unroll
           for (int v = 0; v < VEC; ++v) {
-            sc[v] = half_bits_to_float(half_at<VEC>(sh, v));
-            const f16 zf = __builtin_bit_cast(f16, half_at<VEC>(zh, v));
-            // exact on the fast path: integer zero point, |z| <= 1024
-            const f16 t = FAST ? (f16)((f16)(-1024.f) - zf) : (f16)(-zf);
-            zc[v] = f16x2{t, t};
+            sc[v] = bits_to_float<BF>(half_at<VEC>(sh, v));
+            if constexpr (BF) {
+              czf[v] = 1024.f + bits_to_float<BF>(half_at<VEC>(zh, v));
+            } else {
+              const f16 zf = __builtin_bit_cast(f16, half_at<VEC>(zh, v));
+              // exact on the fast path: integer zero point, |z| <= 1024
+              const f16 t = FAST ? (f16)((f16)(-1024.f) - zf) : (f16)(-zf);
+              zc[v] = f16x2{t, t};
+            }
           }
         }
-        const f16x8 A = __builtin_bit_cast(f16x8, xrow[4 * (u - ub0)]);
+        const u32x4 araw = xrow[4 * (u - ub0)];
 #pragma unroll
         for (int v = 0; v < VEC; ++v) {
           uint32_t b[4];
           decode8<BITS>(word_at<VEC>(wv[c][0], v), NW > 1 ? word_at<VEC>(wv[c][NW - 1], v) : 0u, j, b);
           uint32_t d[4];
-          if constexpr (FAST) {
+          if constexpr (BF) {
 #pragma unroll
-            for (int p = 0; p < 4; ++p) d[p] = as_u32(as_f16x2(b[p]) + zc[v]);
+            for (int p = 0; p < 4; ++p) {
+              const f16x2 h = as_f16x2(b[p]);
+              d[p] = pack_bf16((float)h.x - czf[v], (float)h.y - czf[v]);
+            }
+            acc[c & 1][v] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, araw), __builtin_bit_cast(bf16x8, u32x4{d[0], d[1], d[2], d[3]}),
+                acc[c & 1][v], 0, 0, 0);
           } else {
-            const f16x2 m1024 = f16x2{(f16)(-1024.f), (f16)(-1024.f)};
+            if constexpr (FAST) {
 #pragma unroll
-            for (int p = 0; p < 4; ++p) d[p] = as_u32((as_f16x2(b[p]) + m1024) + zc[v]);
+              for (int p = 0; p < 4; ++p) d[p] = as_u32(as_f16x2(b[p]) + zc[v]);
+            } else {
+              const f16x2 m1024 = f16x2{(f16)(-1024.f), (f16)(-1024.f)};
+#pragma unroll
+              for (int p = 0; p < 4; ++p) d[p] = as_u32((as_f16x2(b[p]) + m1024) + zc[v]);
+            }
+            acc[c & 1][v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, araw),
+                                                                   pack8(d[0], d[1], d[2], d[3]), acc[c & 1][v], 0, 0, 0);
           }
-          acc[c & 1][v] =
-              __builtin_amdgcn_mfma_f32_16x16x32_f16(A, pack8(d[0], d[1], d[2], d[3]), acc[c & 1][v], 0, 0, 0);
         }
       }
     };
@@ -456,12 +475,12 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs g) {
     return sum;
   };
   // The bias joins the fp32 sum before its one rounding to fp16.
-  auto bias_at = [&](int n) { return g.bias ? half_bits_to_float(g.bias[n]) : 0.f; };
+  auto bias_at = [&](int n) { return g.bias ? bits_to_float<BF>(g.bias[n]) : 0.f; };
   if (g.ksplit == 1) {
     for (int e = tid; e < entries; e += THREADS) {
       const int row = e / COLS, col = e - row * COLS;
       if (n0 + col < g.N)
-        g.y[(size_t)row * g.N + n0 + col] = __builtin_bit_cast(uint16_t, (f16)(block_sum(e) + bias_at(n0 + col)));
+        g.y[(size_t)row * g.N + n0 + col] = float_to_bits<BF>(block_sum(e) + bias_at(n0 + col));
     }
     return;
   }
@@ -500,25 +519,39 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs g) {
       float sum = pv[0];
 #pragma unroll
       for (int sp = 1; sp < kMaxSplit; ++sp) sum += (sp < g.ksplit) ? pv[sp] : 0.f;
-      g.y[off] = __builtin_bit_cast(uint16_t, (f16)(sum + bias_at(n0 + col)));
+      g.y[off] = float_to_bits<BF>(sum + bias_at(n0 + col));
     }
   }
   if (tid == 0) __hip_atomic_store(&g.counters[strip], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int BITS, int VEC, int WAVES>
+template <int BITS, int VEC, int WAVES, bool BF>
 hipError_t launch_typed(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
   dim3 grid(p.nstrips, p.ksplit);
-  gemv_kernel<BITS, VEC, WAVES><<<grid, 64 * WAVES, 0, s>>>(a);
+  gemv_kernel<BITS, VEC, WAVES, BF><<<grid, 64 * WAVES, 0, s>>>(a);
   return hipGetLastError();
 }
 
-template <int BITS>
+// The plan uses 16 waves per block, and 8 for 4 columns per lane at 3 or 8
+// bits; other wave counts are tuning options.
+template <int BITS, bool BF>
 hipError_t launch_bits(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
-  if (p.vec == 1) return p.waves == 16 ? launch_typed<BITS, 1, 16>(p, a, s) : launch_typed<BITS, 1, 8>(p, a, s);
-  if (p.waves == 16) return p.vec == 2 ? launch_typed<BITS, 2, 16>(p, a, s) : launch_typed<BITS, 4, 16>(p, a, s);
-  if (p.waves == 8) return p.vec == 2 ? launch_typed<BITS, 2, 8>(p, a, s) : launch_typed<BITS, 4, 8>(p, a, s);
-  return p.vec == 2 ? launch_typed<BITS, 2, 4>(p, a, s) : launch_typed<BITS, 4, 4>(p, a, s);
+  if (p.vec == 1) return p.waves == 16 ? launch_typed<BITS, 1, 16, BF>(p, a, s) : launch_typed<BITS, 1, 8, BF>(p, a, s);
+  if (p.waves == 16) return p.vec == 2 ? launch_typed<BITS, 2, 16, BF>(p, a, s) : launch_typed<BITS, 4, 16, BF>(p, a, s);
+  if (p.waves == 8) return p.vec == 2 ? launch_typed<BITS, 2, 8, BF>(p, a, s) : launch_typed<BITS, 4, 8, BF>(p, a, s);
+  return p.vec == 2 ? launch_typed<BITS, 2, 4, BF>(p, a, s) : launch_typed<BITS, 4, 4, BF>(p, a, s);
+}
+
+template <bool BF>
+hipError_t launch_dtype(const GemvPlan& p, const GemvArgs& a, int bits, hipStream_t s) {
+  switch (bits) {
+    case 1: return launch_bits<1, BF>(p, a, s);
+    case 2: return launch_bits<2, BF>(p, a, s);
+    case 3: return launch_bits<3, BF>(p, a, s);
+    case 4: return launch_bits<4, BF>(p, a, s);
+    case 8: return launch_bits<8, BF>(p, a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 int ceil_log2(int v) {
@@ -591,7 +624,7 @@ GemvPlan gemv_plan(int M, int K, int N, int bits, int group_size) {
 hipError_t launch_gemv(const GemvPlan& p, const uint16_t* x, int M, int K, const uint32_t* qw,
                        const uint32_t* qlo, const uint16_t* zeros, const uint16_t* scales,
                        const uint16_t* bias, int N, int bits, int group_size, uint16_t* y,
-                       void* workspace, hipStream_t s) {
+                       void* workspace, bool bf16, hipStream_t s) {
   if (!p.valid) return hipErrorInvalidValue;
   GemvArgs a;
   a.x = x;
@@ -612,14 +645,7 @@ hipError_t launch_gemv(const GemvPlan& p, const uint16_t* x, int M, int K, const
   a.ksplit = p.ksplit;
   a.ubp_log2 = p.ubp_log2;
   a.gp_log2 = p.gp_log2;
-  switch (bits) {
-    case 1: return launch_bits<1>(p, a, s);
-    case 2: return launch_bits<2>(p, a, s);
-    case 3: return launch_bits<3>(p, a, s);
-    case 4: return launch_bits<4>(p, a, s);
-    case 8: return launch_bits<8>(p, a, s);
-    default: return hipErrorInvalidValue;
-  }
+  return bf16 ? launch_dtype<true>(p, a, bits, s) : launch_dtype<false>(p, a, bits, s);
 }
 
 }  // namespace qmm
