@@ -25,6 +25,8 @@ The JSON line also carries:
                 per column: TFLOP/s against the 2.5 PFLOP/s fp16 dense peak
   readme_shapes the prefill kernel at the README's own benchmark shapes
                 (128x512x1024, 256x1024x2048, 512x2048x4096; 4-bit g128), cold
+  bf16          the decode and prefill products again with bf16 activations,
+                scales, zero points and output (the _bf16 entry points)
   floors        reference kernels timed the same way: an empty kernel as a
                 graph node, a plain streaming read of the decode product's
                 byte count (cold), a long streaming read, a dense MFMA loop
@@ -89,26 +91,33 @@ def cpu_threads() -> int:
     return 1
 
 
-def bench_gemv(w, torch, datagen, steps: int, warmup: int):
+def device_inputs(torch, datagen, d, bf16: bool, dev):
+    """x, zeros, scales of one case on the GPU, as fp16 or as bf16 (the same draws re-rounded)."""
+    if not bf16:
+        return tuple(torch.from_numpy(d[k]).to(dev) for k in ("x", "zeros", "scales"))
+    b = datagen.as_bf16_case(d)
+    return tuple(torch.from_numpy(b[k].view("int16")).view(torch.bfloat16).to(dev) for k in ("x", "zeros", "scales"))
+
+
+def bench_gemv(w, torch, datagen, steps: int, warmup: int, bf16: bool = False):
     wl = datagen.WORKLOADS[datagen.HEADLINE_GEMV]
     dev = torch.device("cuda:0")
     d = datagen.generate(wl)
-    x = torch.from_numpy(d["x"]).to(dev)
-    z0 = torch.from_numpy(d["zeros"]).to(dev)
-    s0 = torch.from_numpy(d["scales"]).to(dev)
+    x, z0, s0 = device_inputs(torch, datagen, d, bf16, dev)
     qw0, qlo0 = w.qmm_pack(torch.from_numpy(d["codes"]).to(dev), wl.bits)
     per_copy = qw0.nbytes + z0.nbytes + s0.nbytes + (qlo0.nbytes if qlo0 is not None else 0)
     R = max(1, math.ceil(COLD_BYTES / per_copy))
     copies = [(qw0, qlo0, z0, s0)] + [
         (qw0.clone(), None if qlo0 is None else qlo0.clone(), z0.clone(), s0.clone()) for _ in range(R - 1)]
-    y = torch.empty((wl.M, wl.N), dtype=torch.float16, device=dev)
+    y = torch.empty((wl.M, wl.N), dtype=x.dtype, device=dev)
     nbytes = w.workspace_bytes(wl.M, wl.K, wl.N, wl.bits, wl.group_size)
     ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=dev)
     lib = w.library()
+    gemv = lib.qmm_gemv_bf16 if bf16 else lib.qmm_gemv
 
     def launch(i: int, stream_ptr: int):
         qw, qlo, z, s = copies[i % R]
-        st = lib.qmm_gemv(x.data_ptr(), wl.M, wl.K, qw.data_ptr(), None if qlo is None else qlo.data_ptr(),
+        st = gemv(x.data_ptr(), wl.M, wl.K, qw.data_ptr(), None if qlo is None else qlo.data_ptr(),
                           z.data_ptr(), s.data_ptr(), None, wl.N, wl.bits, wl.group_size, y.data_ptr(), ws.data_ptr(),
                           ws.numel(), stream_ptr)
         if st != 0:
@@ -149,22 +158,21 @@ def bench_gemv(w, torch, datagen, steps: int, warmup: int):
     }
 
 
-def bench_gemm(w, torch, datagen, steps: int, warmup: int):
+def bench_gemm(w, torch, datagen, steps: int, warmup: int, bf16: bool = False):
     wl = datagen.WORKLOADS[datagen.HEADLINE_GEMM]
     dev = torch.device("cuda:0")
     d = datagen.generate(wl)
-    x = torch.from_numpy(d["x"]).to(dev)
-    z0 = torch.from_numpy(d["zeros"]).to(dev)
-    s0 = torch.from_numpy(d["scales"]).to(dev)
+    x, z0, s0 = device_inputs(torch, datagen, d, bf16, dev)
     qw0, _ = w.qmm_pack(torch.from_numpy(d["codes"]).to(dev), wl.bits)
     R = 4  # weight copies rotated (235 MB of packed weights)
     copies = [(qw0, z0, s0)] + [(qw0.clone(), z0.clone(), s0.clone()) for _ in range(R - 1)]
-    y = torch.empty((wl.M, wl.N), dtype=torch.float16, device=dev)
+    y = torch.empty((wl.M, wl.N), dtype=x.dtype, device=dev)
     lib = w.library()
+    gemm = lib.qmm_gemm_bf16 if bf16 else lib.qmm_gemm
 
     def launch(i: int):
         qw, z, s = copies[i % R]
-        st = lib.qmm_gemm(x.data_ptr(), wl.M, wl.K, qw.data_ptr(), None, z.data_ptr(), s.data_ptr(), None, wl.N, wl.bits,
+        st = gemm(x.data_ptr(), wl.M, wl.K, qw.data_ptr(), None, z.data_ptr(), s.data_ptr(), None, wl.N, wl.bits,
                           wl.group_size, y.data_ptr(), torch.cuda.current_stream().cuda_stream)
         if st != 0:
             raise RuntimeError(f"qmm_gemm failed: {lib.qmm_last_error().decode()}")
@@ -344,7 +352,8 @@ def main():
     ap.add_argument("--no-gemm", action="store_true")
     ap.add_argument("--no-floors", action="store_true", help="skip the reference kernels (empty launch, "
                     "streaming read, MFMA loop)")
-    ap.add_argument("--only", choices=("gemv", "gemm"), default=None,
+    ap.add_argument("--no-bf16", action="store_true", help="skip the bf16 products")
+    ap.add_argument("--only", choices=("gemv", "gemm", "gemv_bf16", "gemm_bf16"), default=None,
                     help="run one product only and print its own line (for profiling runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the products, run 4 plain device copies of MIB MiB each (outside every timed "
@@ -385,17 +394,29 @@ def copy_calibration(torch, mib: int):
           flush=True)
 
 
+def gemm_line(gm):
+    return {"workload": gm["wl"].name, "ms_per_step": round(gm["ms_per_step"], 4),
+            "mean_launch_ms": round(gm["mean_launch_ms"], 4),
+            "TFLOP/s": round(gm["flops"] / (gm["mean_launch_ms"] * 1e-3) / 1e12, 2)}
+
+
+def gemv_line(gv):
+    return {"workload": gv["wl"].name, "ms_per_step": round(gv["ms_per_step"], 6),
+            "GB/s": round(gv["bytes"] / (gv["ms_per_step"] * 1e-3) / 1e9, 2)}
+
+
 def run(args, torch, datagen, w):
-    if args.only == "gemm":
-        gm = bench_gemm(w, torch, datagen, args.gemm_steps, args.gemm_warmup)
-        print(json.dumps({"workload": gm["wl"].name, "ms_per_step": round(gm["ms_per_step"], 4),
-                          "mean_launch_ms": round(gm["mean_launch_ms"], 4),
-                          "TFLOP/s": round(gm["flops"] / (gm["mean_launch_ms"] * 1e-3) / 1e12, 2)}), flush=True)
+    if args.only in ("gemm", "gemm_bf16"):
+        gm = bench_gemm(w, torch, datagen, args.gemm_steps, args.gemm_warmup, bf16=args.only == "gemm_bf16")
+        print(json.dumps(dict(gemm_line(gm), dtype="bf16" if args.only == "gemm_bf16" else "f16")), flush=True)
+        return
+    if args.only == "gemv_bf16":
+        gv = bench_gemv(w, torch, datagen, args.steps, args.warmup, bf16=True)
+        print(json.dumps(dict(gemv_line(gv), dtype="bf16")), flush=True)
         return
     gv = bench_gemv(w, torch, datagen, args.steps, args.warmup)
     if args.only == "gemv":
-        print(json.dumps({"workload": gv["wl"].name, "ms_per_step": round(gv["ms_per_step"], 6),
-                          "GB/s": round(gv["bytes"] / (gv["ms_per_step"] * 1e-3) / 1e9, 2)}), flush=True)
+        print(json.dumps(dict(gemv_line(gv), dtype="f16")), flush=True)
         return
     wl = gv["wl"]
     value = gv["bytes"] / (gv["ms_per_step"] * 1e-3) / 1e9
@@ -439,6 +460,15 @@ def run(args, torch, datagen, w):
         }
     if not args.no_gemm:
         out["readme_shapes"] = bench_readme_shapes(w, torch, datagen)
+    if not args.no_bf16:
+        # bf16 data, same workloads; the bf16 dense MFMA peak equals the fp16 one
+        gvb = bench_gemv(w, torch, datagen, args.steps, args.warmup, bf16=True)
+        out["bf16"] = {"gemv": dict(gemv_line(gvb), pct_of_hbm_peak=round(
+            100 * gvb["bytes"] / (gvb["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 2))}
+        if not args.no_gemm:
+            gmb = bench_gemm(w, torch, datagen, args.gemm_steps, args.gemm_warmup, bf16=True)
+            t = gmb["flops"] / (gmb["mean_launch_ms"] * 1e-3) / 1e12
+            out["bf16"]["gemm"] = dict(gemm_line(gmb), pct_of_bf16_dense_peak=round(100 * t / FP16_DENSE_PEAK_TFLOPS, 2))
     if not args.no_floors:
         out["floors"] = floors(torch, gv["bytes"])
     if not args.no_cpu_baseline:
