@@ -16,9 +16,11 @@
 //    and zero points, then every wave requests its weight words. Loads
 //    complete in order, so the block waits for the first two only, puts them
 //    in LDS, and each unit is computed as soon as its own weight words arrive.
-//  * Codes become halves with one AND-OR into the mantissa of 1024.0 (exact),
-//    then one packed subtract of (1024 + zero) when the zero point is an
-//    integer (exact), else two subtracts.
+//  * Codes become halves with one bitfield insert into the mantissa of 1024.0
+//    (exact). A code may sit 2^e places up in that mantissa (1024 + 2^e q),
+//    which saves shifts; one packed fused multiply-add by 2^-e then subtracts
+//    1024 2^-e + zero, exactly when the zero point is an integer; otherwise q
+//    is formed first (exact) and the zero point subtracted after.
 //  * The multiply-accumulate runs on the matrix cores: V_MFMA_F32_16X16X32_F16
 //    with x as the 16 x 32 A operand (rows >= M repeat row 0 and are never
 //    stored) and the dequantized codes as the 32 x 16 B operand. Lane group
@@ -81,25 +83,63 @@ __device__ __forceinline__ uint32_t word_at(typename Vec<VEC>::T w, int v) {
   else return w[v];
 }
 
-// Four fp16 pairs 1024 + q for the 8 codes lane group j takes from its
+// (w & m) | (c & ~m). With m and c held in registers (below) this is one
+// bitfield insert (v_bfi_b32) instead of an AND and an OR with literals.
+__device__ __forceinline__ uint32_t bfi(uint32_t m, uint32_t w, uint32_t c) { return (w & m) | (c & ~m); }
+
+// Masks of decode8, made once per kernel: the empty asm statements keep them
+// in registers (a vector register per mask, the magic 1024.0 pair in a scalar
+// one) instead of being folded back into literals.
+template <int BITS> struct DecodeMasks {
+  uint32_t m[4];
+  uint32_t magic;
+};
+template <int BITS> __device__ __forceinline__ DecodeMasks<BITS> decode_masks() {
+  DecodeMasks<BITS> d;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    d.m[p] = BITS == 4 ? (p & 1 ? 0x00F000F0u : 0x000F000Fu)
+           : BITS == 2 ? (p & 1 ? 0x000C000Cu : 0x00030003u)
+           : BITS == 1 ? ((1u << p) | (1u << (20 + p))) : 0u;
+    if (BITS == 1 || ((BITS == 2 || BITS == 4) && p < 2)) asm("" : "+v"(d.m[p]));
+  }
+  d.magic = kMagic1024x2;
+  asm("" : "+s"(d.magic));
+  return d;
+}
+
+// Place of a code in the fp16 mantissa after decode8: half `hi` of pair p
+// holds 1024 + 2^e q with e = code_exp(p, hi).
+template <int BITS> __host__ __device__ constexpr int code_exp(int p, int hi) {
+  return BITS == 4 ? 4 * (p & 1) : BITS == 2 ? 2 * (p & 1) : BITS == 1 ? p + 4 * hi : 0;
+}
+
+// Four fp16 pairs 1024 + 2^e q for the 8 codes lane group j takes from its
 // word(s) of one column. Element order (pair p = elements 2p, 2p+1):
 //  4-bit: slots (p, p + 4) of the word          -> k = 8j + {p, p+4}
 //  1-bit: slots (8j + p, 8j + p + 4) of the word -> k = 8j + {p, p+4}
 //  8-bit: slots (0,1),(2,3) of word 0, then of 1 -> k = 8j + e
 //  2/3-bit: slots (i0 + p, i0 + p + 8), i0 = 4 (j & 1), of the plane-2 word
 //           -> k = 16 (j >> 1) + i0 + {p, p + 8}
+// 4-bit: odd pairs are masked 4 places up (one shift for all four pairs);
+// 2-bit: odd pairs 2 places up (two shifts); 1-bit: byte j is copied into
+// both halves and pair p masked at bit p of the low half and bit 4 + p of the
+// high half.
 template <int BITS>
-__device__ __forceinline__ void decode8(uint32_t w0, uint32_t w1, int j, uint32_t (&b)[4]) {
+__device__ __forceinline__ void decode8(uint32_t w0, uint32_t w1, int j, const DecodeMasks<BITS>& dm,
+                                        uint32_t (&b)[4]) {
+  const uint32_t magic = dm.magic;
   if constexpr (BITS == 4) {
-#pragma unroll
-    for (int p = 0; p < 4; ++p) b[p] = ((w0 >> (4 * p)) & 0x000F000Fu) | kMagic1024x2;
+    const uint32_t t = w0 >> 8;
+    b[0] = bfi(dm.m[0], w0, magic);
+    b[1] = bfi(dm.m[1], w0, magic);
+    b[2] = bfi(dm.m[0], t, magic);
+    b[3] = bfi(dm.m[1], t, magic);
   } else if constexpr (BITS == 1) {
-    const uint32_t t = w0 >> (8 * j);
+    // bytes (j, 0, j, 0) of the word: 0x0C selects a zero byte
+    const uint32_t t = __builtin_amdgcn_perm(0u, w0, (uint32_t)j | 0x0C000C00u | ((uint32_t)j << 16));
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t u = (t >> p) & 0x11u;  // codes p and p + 4 at bits 0 and 4
-      b[p] = ((u | (u << 12)) & 0x00010001u) | kMagic1024x2;
-    }
+    for (int p = 0; p < 4; ++p) b[p] = bfi(dm.m[p], t, magic);
   } else if constexpr (BITS == 8) {
     // byte permute: (byte0, 0x64, byte1, 0x64) = halves (1024 + q0, 1024 + q1)
     b[0] = __builtin_amdgcn_perm(0x64646464u, w0, 0x04010400u);
@@ -108,8 +148,11 @@ __device__ __forceinline__ void decode8(uint32_t w0, uint32_t w1, int j, uint32_
     b[3] = __builtin_amdgcn_perm(0x64646464u, w1, 0x04030402u);
   } else if constexpr (BITS == 2) {
     const uint32_t ws = w0 >> (8 * (j & 1));
-#pragma unroll
-    for (int p = 0; p < 4; ++p) b[p] = ((ws >> (2 * p)) & 0x00030003u) | kMagic1024x2;
+    const uint32_t t = ws >> 4;
+    b[0] = bfi(dm.m[0], ws, magic);
+    b[1] = bfi(dm.m[1], ws, magic);
+    b[2] = bfi(dm.m[0], t, magic);
+    b[3] = bfi(dm.m[1], t, magic);
   } else {
     // plane2 word w0 holds q >> 1 for 16 k; plane1 word w1 holds q & 1 for the
     // unit's 32 k. Gather the low bits of this word's slots 0-7 into bits 0-7
@@ -166,6 +209,21 @@ __device__ __forceinline__ uint16_t half_at(typename Halves<VEC>::T h, int v) {
   if constexpr (VEC == 1) return h;
   else if constexpr (VEC == 2) return (uint16_t)(h >> (16 * v));
   else return (uint16_t)(h[v >> 1] >> (16 * (v & 1)));
+}
+
+// Pair classes: pairs whose codes sit at the same mantissa places.
+template <int BITS> constexpr int kPairClasses = BITS == 1 ? 4 : ((BITS == 2 || BITS == 4) ? 2 : 1);
+template <int BITS> __device__ __forceinline__ constexpr int pair_class(int p) {
+  return BITS == 1 ? p : ((BITS == 2 || BITS == 4) ? (p & 1) : 0);
+}
+// 2^-e per half of pair p.
+template <int BITS> __device__ __forceinline__ f16x2 pair_scale(int p) {
+  return f16x2{(f16)(1.0f / (float)(1 << code_exp<BITS>(p, 0))), (f16)(1.0f / (float)(1 << code_exp<BITS>(p, 1)))};
+}
+// h 2^-e + c, one packed operation (an add where e is 0 in both halves).
+template <int BITS> __device__ __forceinline__ f16x2 scale_add(int p, f16x2 h, f16x2 c) {
+  if (code_exp<BITS>(p, 0) == 0 && code_exp<BITS>(p, 1) == 0) return h + c;
+  return __builtin_elementwise_fma(h, pair_scale<BITS>(p), c);
 }
 
 // First k (within a unit) of the activations lane group j feeds: 8 consecutive
@@ -243,6 +301,7 @@ constexpr int kXPerThread = 4;  // activation slots one thread stages at most
 template <int BITS, int VEC, int WAVES, bool BF>
 __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs g) {
   constexpr int NW = Bits<BITS>::NW;
+  constexpr int NPC = kPairClasses<BITS>;
   constexpr int CH = chunk_units<BITS, VEC, WAVES>();
   constexpr int COLS = 16 * VEC;
   constexpr int CP = COLS / 8;  // 16-byte pieces per staged row of scales or zero points
@@ -365,6 +424,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs g) {
   const int zfast = __builtin_amdgcn_readfirstlane(all_ok);
 
   // ---- 4. the wave's units.
+  const DecodeMasks<BITS> dm = decode_masks<BITS>();
   f32x4 total[VEC];
 #pragma unroll
   for (int v = 0; v < VEC; ++v) total[v] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -375,10 +435,19 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs g) {
     f32x4 acc[2][VEC];
 #pragma unroll
     for (int v = 0; v < VEC; ++v) acc[0][v] = acc[1][v] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float sc[VEC], czf[VEC];  // scale; 1024 + z in fp32 (bf16 data)
-    f16x2 zc[VEC];  // -(1024 + z) on the exact path, else -z (1024 removed separately)
+    // Per pair class c (pairs whose codes sit at the same places e_lo, e_hi)
+    // and column v: fp16 -(1024 2^-e + z) per half on the exact path, else
+    // -z (the 1024 2^-e is removed first). For bf16 data, fp32 1024 2^-e + z
+    // where both halves share e (all widths but 1), else z alone.
+    constexpr bool SPLIT_E = BITS == 1;
+    float sc[VEC], czf[NPC][VEC];
+    f16x2 zc[NPC][VEC];
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) { sc[v] = 0.f; czf[v] = 0.f; zc[v] = f16x2{0, 0}; }
+    for (int v = 0; v < VEC; ++v) {
+      sc[v] = 0.f;
+#pragma unroll
+      for (int c = 0; c < NPC; ++c) { czf[c][v] = 0.f; zc[c][v] = f16x2{0, 0}; }
+    }
     int cur_g = -1;
     auto chunk = [&](int base) {
 #pragma unroll
@@ -402,13 +471,19 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs g) {
 #pragma unroll
           for (int v = 0; v < VEC; ++v) {
             sc[v] = bits_to_float<BF>(half_at<VEC>(sh, v));
-            if constexpr (BF) {
-              czf[v] = 1024.f + bits_to_float<BF>(half_at<VEC>(zh, v));
-            } else {
-              const f16 zf = __builtin_bit_cast(f16, half_at<VEC>(zh, v));
-              // exact on the fast path: integer zero point, |z| <= 1024
-              const f16 t = FAST ? (f16)((f16)(-1024.f) - zf) : (f16)(-zf);
-              zc[v] = f16x2{t, t};
+            const float zf = bits_to_float<BF>(half_at<VEC>(zh, v));
+#pragma unroll
+            for (int c = 0; c < NPC; ++c) {
+              const float base_lo = 1024.f / (float)(1 << code_exp<BITS>(c, 0));
+              const float base_hi = 1024.f / (float)(1 << code_exp<BITS>(c, 1));
+              if constexpr (BF) {
+                czf[c][v] = SPLIT_E ? zf : base_lo + zf;
+              } else if constexpr (FAST) {
+                // exact: integer zero point, |z| <= 1024, and 1024 2^-e + z within 2048
+                zc[c][v] = f16x2{(f16)(-(base_lo + zf)), (f16)(-(base_hi + zf))};
+              } else {
+                zc[c][v] = f16x2{(f16)(-zf), (f16)(-zf)};
+              }
             }
           }
         }
@@ -416,13 +491,22 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs g) {
 #pragma unroll
         for (int v = 0; v < VEC; ++v) {
           uint32_t b[4];
-          decode8<BITS>(word_at<VEC>(wv[c][0], v), NW > 1 ? word_at<VEC>(wv[c][NW - 1], v) : 0u, j, b);
+          decode8<BITS>(word_at<VEC>(wv[c][0], v), NW > 1 ? word_at<VEC>(wv[c][NW - 1], v) : 0u, j, dm, b);
           uint32_t d[4];
           if constexpr (BF) {
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
               const f16x2 h = as_f16x2(b[p]);
-              d[p] = pack_bf16((float)h.x - czf[v], (float)h.y - czf[v]);
+              const int c = pair_class<BITS>(p);
+              const float s_lo = 1.0f / (float)(1 << code_exp<BITS>(p, 0));
+              const float s_hi = 1.0f / (float)(1 << code_exp<BITS>(p, 1));
+              if constexpr (SPLIT_E) {
+                // q exactly, then one rounding of q - z
+                d[p] = pack_bf16(__builtin_fmaf((float)h.x, s_lo, -1024.f * s_lo) - czf[c][v],
+                                 __builtin_fmaf((float)h.y, s_hi, -1024.f * s_hi) - czf[c][v]);
+              } else {
+                d[p] = pack_bf16(__builtin_fmaf((float)h.x, s_lo, -czf[c][v]), __builtin_fmaf((float)h.y, s_hi, -czf[c][v]));
+              }
             }
             acc[c & 1][v] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                 __builtin_bit_cast(bf16x8, araw), __builtin_bit_cast(bf16x8, u32x4{d[0], d[1], d[2], d[3]}),
@@ -430,11 +514,15 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs g) {
           } else {
             if constexpr (FAST) {
 #pragma unroll
-              for (int p = 0; p < 4; ++p) d[p] = as_u32(as_f16x2(b[p]) + zc[v]);
+              for (int p = 0; p < 4; ++p)
+                d[p] = as_u32(scale_add<BITS>(p, as_f16x2(b[p]), zc[pair_class<BITS>(p)][v]));
             } else {
-              const f16x2 m1024 = f16x2{(f16)(-1024.f), (f16)(-1024.f)};
 #pragma unroll
-              for (int p = 0; p < 4; ++p) d[p] = as_u32((as_f16x2(b[p]) + m1024) + zc[v]);
+              for (int p = 0; p < 4; ++p) {
+                const f16x2 s = pair_scale<BITS>(p);
+                const f16x2 q = scale_add<BITS>(p, as_f16x2(b[p]), f16x2{(f16)(-1024.f) * s.x, (f16)(-1024.f) * s.y});
+                d[p] = as_u32(q + zc[pair_class<BITS>(p)][v]);
+              }
             }
             acc[c & 1][v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, araw),
                                                                    pack8(d[0], d[1], d[2], d[3]), acc[c & 1][v], 0, 0, 0);
