@@ -140,7 +140,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, size_
 // that run beside each other on one XCD.
 constexpr int kWeightPolicy = 1;
 
-constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
 // Block tile BM x BN = (32 TM WM) x (32 TN WN), computed by KG groups of
 // WM x WN waves, each wave TM x TN MFMA tiles of 32 x 32. Group j takes the

@@ -199,18 +199,6 @@ template <int BITS, int VEC, int WAVES> constexpr int chunk_units() {
   return (Bits<BITS>::NW * VEC <= (WAVES >= 8 ? 2 : 4)) ? 8 : 4;
 }
 
-// Fp16 scale/zero values of a lane's VEC columns, as read from LDS.
-template <int VEC> struct Halves;
-template <> struct Halves<1> { typedef uint16_t T; };
-template <> struct Halves<2> { typedef uint32_t T; };
-template <> struct Halves<4> { typedef u32x2 T; };
-template <int VEC>
-__device__ __forceinline__ uint16_t half_at(typename Halves<VEC>::T h, int v) {
-  if constexpr (VEC == 1) return h;
-  else if constexpr (VEC == 2) return (uint16_t)(h >> (16 * v));
-  else return (uint16_t)(h[v >> 1] >> (16 * (v & 1)));
-}
-
 // Pair classes: pairs whose codes sit at the same mantissa places.
 template <int BITS> constexpr int kPairClasses = BITS == 1 ? 4 : ((BITS == 2 || BITS == 4) ? 2 : 1);
 template <int BITS> __device__ __forceinline__ constexpr int pair_class(int p) {
@@ -290,10 +278,11 @@ __device__ __forceinline__ int unit_rows(int w) {
   else return w == 0 ? 2 : 1;
 }
 
-// LDS of a block: staged activations and scales / zero points (5 KiB per
-// wave: 80 KiB for 16 waves, so that blocks of fewer waves can share a CU),
-// and apart from them the per-wave partial sums.
-constexpr int stage_bytes(int waves) { return waves * 5 * 1024; }
+// LDS of a block: staged activations and scales / zero points, 9 KiB per
+// wave (144 KiB for 16 waves, so that blocks of fewer waves can share a CU).
+// The per-wave partial sums reuse the same space once every wave is done
+// with the staged data.
+constexpr int stage_bytes(int waves) { return waves * 9 * 1024; }
 constexpr int kXPerThread = 4;  // activation slots one thread stages at most
 
 // BF: bf16 data (x, scales, zero points, bias, y); the dequantized codes are
@@ -307,8 +296,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs g) {
   constexpr int CP = COLS / 8;  // 16-byte pieces per staged row of scales or zero points
   constexpr int CP_LOG2 = VEC == 1 ? 1 : (VEC == 2 ? 2 : 3);
   constexpr int THREADS = 64 * WAVES;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[stage_bytes(WAVES)];
-  __shared__ float red[WAVES * kMaxM * COLS];  // [WAVES][M][COLS]
+  constexpr int kRedBytes = WAVES * kMaxM * COLS * 4;  // [WAVES][M][COLS] fp32
+  __shared__ __attribute__((aligned(16))) unsigned char lds[cmax(stage_bytes(WAVES), kRedBytes)];
+  float* red = reinterpret_cast<float*>(lds);
   __shared__ int wave_exact[WAVES];
   __shared__ int last_flag;
 
@@ -394,9 +384,17 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs g) {
   // ---- 3. staged data into LDS, waiting for the staging requests only. The
   // barrier also tells every wave whether all of the block's zero points are
   // integers (|z| <= 1024), for which one packed add dequantizes exactly.
+  // Scales and zero points are staged ready for use, per (group row, column):
+  // the fp32 scale; the fp16 pair (-z, -z); and per pair class c the fp16
+  // pair -(1024 2^-e + z) (exact path) or, for bf16 data, fp32 1024 2^-e + z
+  // (z alone for 1-bit codes, whose halves differ in e).
+  constexpr bool SPLIT_E = BITS == 1;
   u32x4* xs = reinterpret_cast<u32x4*>(lds);
   const int xs_bytes = g.M << (ubp_log2 + 6);
-  uint16_t* szs = reinterpret_cast<uint16_t*>(lds + xs_bytes);  // [2][1 << gp_log2][COLS]
+  const int gstride = COLS << g.gp_log2;  // words per staged array
+  float* s_sc = reinterpret_cast<float*>(lds + xs_bytes);       // [group row][COLS]
+  uint32_t* s_zs = reinterpret_cast<uint32_t*>(s_sc + gstride);  // [group row][COLS]
+  uint32_t* s_zc = s_zs + gstride;                               // [NPC][group row][COLS]
 #pragma unroll
   for (int i = 0; i < kXPerThread; ++i) {
     const int sl = tid + THREADS * i;
@@ -405,14 +403,41 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs g) {
   }
   bool exact = !BF;
   if (sz_on) {
-    *reinterpret_cast<u32x4*>(szs + sz_row * COLS + 8 * sz_cp) = sraw;
-    *reinterpret_cast<u32x4*>(szs + ((1 << g.gp_log2) + sz_row) * COLS + 8 * sz_cp) = zraw;
-    if constexpr (!BF) {
+    uint32_t scv[8], zsv[8], zcv[NPC][8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float z = half_bits_to_float((uint16_t)(zraw[e >> 1] >> (16 * (e & 1))));
-        exact = exact && (z == __builtin_rintf(z)) && (__builtin_fabsf(z) <= 1024.f);
+    for (int e = 0; e < 8; ++e) {
+      const uint16_t sb = (uint16_t)(sraw[e >> 1] >> (16 * (e & 1)));
+      const uint16_t zb = (uint16_t)(zraw[e >> 1] >> (16 * (e & 1)));
+      const float zf = bits_to_float<BF>(zb);
+      scv[e] = __builtin_bit_cast(uint32_t, bits_to_float<BF>(sb));
+      if constexpr (!BF) {
+        exact = exact && (zf == __builtin_rintf(zf)) && (__builtin_fabsf(zf) <= 1024.f);
+        const f16 nz = -__builtin_bit_cast(f16, zb);
+        zsv[e] = as_u32(f16x2{nz, nz});
       }
+#pragma unroll
+      for (int c = 0; c < NPC; ++c) {
+        const float base_lo = 1024.f / (float)(1 << code_exp<BITS>(c, 0));
+        const float base_hi = 1024.f / (float)(1 << code_exp<BITS>(c, 1));
+        if constexpr (BF) {
+          zcv[c][e] = __builtin_bit_cast(uint32_t, SPLIT_E ? zf : base_lo + zf);
+        } else {
+          // exact when the zero point is an integer with |z| <= 1024 (1024 2^-e + z within 2048)
+          zcv[c][e] = as_u32(f16x2{(f16)(-(base_lo + zf)), (f16)(-(base_hi + zf))});
+        }
+      }
+    }
+    const int o = sz_row * COLS + 8 * sz_cp;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      *reinterpret_cast<u32x4*>(reinterpret_cast<uint32_t*>(s_sc) + o + 4 * h) =
+          u32x4{scv[4 * h], scv[4 * h + 1], scv[4 * h + 2], scv[4 * h + 3]};
+      if constexpr (!BF)
+        *reinterpret_cast<u32x4*>(s_zs + o + 4 * h) = u32x4{zsv[4 * h], zsv[4 * h + 1], zsv[4 * h + 2], zsv[4 * h + 3]};
+#pragma unroll
+      for (int c = 0; c < NPC; ++c)
+        *reinterpret_cast<u32x4*>(s_zc + c * gstride + o + 4 * h) =
+            u32x4{zcv[c][4 * h], zcv[c][4 * h + 1], zcv[c][4 * h + 2], zcv[c][4 * h + 3]};
     }
   }
   const bool wave_ok = __all(exact);
@@ -432,62 +457,50 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs g) {
 
   auto run = [&](auto fast_tag) {
     constexpr bool FAST = decltype(fast_tag)::value;
-    f32x4 acc[2][VEC];
-#pragma unroll
-    for (int v = 0; v < VEC; ++v) acc[0][v] = acc[1][v] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // Per pair class c (pairs whose codes sit at the same places e_lo, e_hi)
-    // and column v: fp16 -(1024 2^-e + z) per half on the exact path, else
-    // -z (the 1024 2^-e is removed first). For bf16 data, fp32 1024 2^-e + z
-    // where both halves share e (all widths but 1), else z alone.
-    constexpr bool SPLIT_E = BITS == 1;
+    // One accumulator per column, added into `total` times the group's scale
+    // and cleared when the next group starts.
+    f32x4 acc[VEC];
     float sc[VEC], czf[NPC][VEC];
-    f16x2 zc[NPC][VEC];
+    f16x2 zc[NPC][VEC], mz[VEC];
 #pragma unroll
     for (int v = 0; v < VEC; ++v) {
+      acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
       sc[v] = 0.f;
+      mz[v] = f16x2{0, 0};
 #pragma unroll
       for (int c = 0; c < NPC; ++c) { czf[c][v] = 0.f; zc[c][v] = f16x2{0, 0}; }
     }
     int cur_g = -1;
     auto chunk = [&](int base) {
+      const u32x4* xb = xrow + 4 * (base - ub0);  // unit base + c at xb[4 c]
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
         const int u = base + c;
         if (u >= uz) break;  // scalar
         const int grp = group_of(u);
         if (grp != cur_g) {  // scalar
-          if (cur_g >= 0) {
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) {
-              total[v] += sc[v] * (acc[0][v] + acc[1][v]);
-              acc[0][v] = acc[1][v] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-          }
-          cur_g = grp;
-          const uint16_t* srow = szs + (grp - gb0) * COLS + VEC * cl;
-          const typename Halves<VEC>::T sh = *reinterpret_cast<const typename Halves<VEC>::T*>(srow);
-          const typename Halves<VEC>::T zh =
-              *reinterpret_cast<const typename Halves<VEC>::T*>(srow + (COLS << g.gp_log2));
+          // A real branch: the group change is rare, and selecting its
+          // results on every unit would cost more than the branch.
+          asm volatile("" ::: "memory");
 #pragma unroll
           for (int v = 0; v < VEC; ++v) {
-            sc[v] = bits_to_float<BF>(half_at<VEC>(sh, v));
-            const float zf = bits_to_float<BF>(half_at<VEC>(zh, v));
+            total[v] += sc[v] * acc[v];
+            acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+          cur_g = grp;
+          const int o = (grp - gb0) * COLS + VEC * cl;
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) {
+            sc[v] = s_sc[o + v];
+            if constexpr (!BF) mz[v] = as_f16x2(s_zs[o + v]);
 #pragma unroll
             for (int c = 0; c < NPC; ++c) {
-              const float base_lo = 1024.f / (float)(1 << code_exp<BITS>(c, 0));
-              const float base_hi = 1024.f / (float)(1 << code_exp<BITS>(c, 1));
-              if constexpr (BF) {
-                czf[c][v] = SPLIT_E ? zf : base_lo + zf;
-              } else if constexpr (FAST) {
-                // exact: integer zero point, |z| <= 1024, and 1024 2^-e + z within 2048
-                zc[c][v] = f16x2{(f16)(-(base_lo + zf)), (f16)(-(base_hi + zf))};
-              } else {
-                zc[c][v] = f16x2{(f16)(-zf), (f16)(-zf)};
-              }
+              if constexpr (BF) czf[c][v] = __builtin_bit_cast(float, s_zc[c * gstride + o + v]);
+              else zc[c][v] = as_f16x2(s_zc[c * gstride + o + v]);
             }
           }
         }
-        const u32x4 araw = xrow[4 * (u - ub0)];
+        const u32x4 araw = xb[4 * c];
 #pragma unroll
         for (int v = 0; v < VEC; ++v) {
           uint32_t b[4];
@@ -508,9 +521,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs g) {
                 d[p] = pack_bf16(__builtin_fmaf((float)h.x, s_lo, -czf[c][v]), __builtin_fmaf((float)h.y, s_hi, -czf[c][v]));
               }
             }
-            acc[c & 1][v] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, araw), __builtin_bit_cast(bf16x8, u32x4{d[0], d[1], d[2], d[3]}),
-                acc[c & 1][v], 0, 0, 0);
+            const bf16x8 A = __builtin_bit_cast(bf16x8, araw);
+            const bf16x8 B = __builtin_bit_cast(bf16x8, u32x4{d[0], d[1], d[2], d[3]});
+            acc[v] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[v], 0, 0, 0);
           } else {
             if constexpr (FAST) {
 #pragma unroll
@@ -521,11 +534,12 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs g) {
               for (int p = 0; p < 4; ++p) {
                 const f16x2 s = pair_scale<BITS>(p);
                 const f16x2 q = scale_add<BITS>(p, as_f16x2(b[p]), f16x2{(f16)(-1024.f) * s.x, (f16)(-1024.f) * s.y});
-                d[p] = as_u32(q + zc[pair_class<BITS>(p)][v]);
+                d[p] = as_u32(q + mz[v]);
               }
             }
-            acc[c & 1][v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, araw),
-                                                                   pack8(d[0], d[1], d[2], d[3]), acc[c & 1][v], 0, 0, 0);
+            const f16x8 A = __builtin_bit_cast(f16x8, araw);
+            const f16x8 B = pack8(d[0], d[1], d[2], d[3]);
+            acc[v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, acc[v], 0, 0, 0);
           }
         }
       }
@@ -535,15 +549,17 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs g) {
       load_batch(base);
       chunk(base);
     }
-    if (cur_g >= 0) {
+    {
 #pragma unroll
-      for (int v = 0; v < VEC; ++v) total[v] += sc[v] * (acc[0][v] + acc[1][v]);
+      for (int v = 0; v < VEC; ++v) total[v] += sc[v] * acc[v];
     }
   };
   if (zfast) run(std::integral_constant<bool, true>{});
   else run(std::integral_constant<bool, false>{});
 
-  // ---- 5. the block's waves are summed in wave order.
+  // ---- 5. the block's waves are summed in wave order, in LDS that held
+  // the staged data (hence the barrier first).
+  __syncthreads();
   // D layout: lane holds rows 4 j + i (i < 4) of column VEC * cl + v.
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -691,7 +707,8 @@ GemvPlan gemv_plan(int M, int K, int N, int bits, int group_size) {
     }
     const int gp_log2 = ceil_log2(groups);
     const long long x_slots = (long long)M << (ubp_log2 + 2);
-    const long long stage = (x_slots << 4) + (2LL << gp_log2) * cols * 2;
+    const int npc = bits == 1 ? 4 : ((bits == 2 || bits == 4) ? 2 : 1);
+    const long long stage = (x_slots << 4) + (1LL << gp_log2) * cols * 4 * (2 + npc);
     if (x_slots <= (long long)kXPerThread * threads && ((long long)(cols / 8) << gp_log2) <= threads &&
         stage <= stage_bytes(p.waves)) {
       p.units_per_block = upb;
