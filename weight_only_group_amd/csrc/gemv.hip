@@ -100,8 +100,9 @@ template <int BITS> __device__ __forceinline__ DecodeMasks<BITS> decode_masks() 
   for (int p = 0; p < 4; ++p) {
     d.m[p] = BITS == 4 ? (p & 1 ? 0x00F000F0u : 0x000F000Fu)
            : BITS == 2 ? (p & 1 ? 0x000C000Cu : 0x00030003u)
+           : BITS == 3 ? (p & 1 ? 0x00020002u : 0x000C000Cu)  // 2-bit plane at bits 2-3, 1-bit plane at bit 1
            : BITS == 1 ? ((1u << p) | (1u << (20 + p))) : 0u;
-    if (BITS == 1 || ((BITS == 2 || BITS == 4) && p < 2)) asm("" : "+v"(d.m[p]));
+    if (BITS == 1 || ((BITS == 2 || BITS == 3 || BITS == 4) && p < 2)) asm("" : "+v"(d.m[p]));
   }
   d.magic = kMagic1024x2;
   asm("" : "+s"(d.magic));
@@ -111,7 +112,7 @@ template <int BITS> __device__ __forceinline__ DecodeMasks<BITS> decode_masks() 
 // Place of a code in the fp16 mantissa after decode8: half `hi` of pair p
 // holds 1024 + 2^e q with e = code_exp(p, hi).
 template <int BITS> __host__ __device__ constexpr int code_exp(int p, int hi) {
-  return BITS == 4 ? 4 * (p & 1) : BITS == 2 ? 2 * (p & 1) : BITS == 1 ? p + 4 * hi : 0;
+  return BITS == 4 ? 4 * (p & 1) : BITS == 2 ? 2 * (p & 1) : BITS == 1 ? p + 4 * hi : BITS == 3 ? 1 : 0;
 }
 
 // Four fp16 pairs 1024 + 2^e q for the 8 codes lane group j takes from its
@@ -124,7 +125,9 @@ template <int BITS> __host__ __device__ constexpr int code_exp(int p, int hi) {
 // 4-bit: odd pairs are masked 4 places up (one shift for all four pairs);
 // 2-bit: odd pairs 2 places up (two shifts); 1-bit: byte j is copied into
 // both halves and pair p masked at bit p of the low half and bit 4 + p of the
-// high half.
+// high half; 3-bit: q >> 1 (2-bit plane) goes to bits 2-3 and q & 1 (1-bit
+// plane, its bytes of this lane group copied into both halves) to bit 1, so
+// each half is 1024 + 2q.
 template <int BITS>
 __device__ __forceinline__ void decode8(uint32_t w0, uint32_t w1, int j, const DecodeMasks<BITS>& dm,
                                         uint32_t (&b)[4]) {
@@ -154,18 +157,19 @@ __device__ __forceinline__ void decode8(uint32_t w0, uint32_t w1, int j, const D
     b[2] = bfi(dm.m[0], t, magic);
     b[3] = bfi(dm.m[1], t, magic);
   } else {
-    // plane2 word w0 holds q >> 1 for 16 k; plane1 word w1 holds q & 1 for the
-    // unit's 32 k. Gather the low bits of this word's slots 0-7 into bits 0-7
-    // and of slots 8-15 into bits 16-23, so one shift serves both halves.
-    const int base = 16 * (j >> 1);
-    const uint32_t lo8 = (w1 >> base) & 0xFFu;
-    const uint32_t hi8 = (w1 >> (base + 8)) & 0xFFu;
+    // plane2 word w0 holds q >> 1 for 16 k (slot i0 + p of pair p at bits
+    // 2 (i0 + p) and 2 (i0 + p) + 16); plane1 word w1 holds q & 1 for the
+    // unit's 32 k (k = 16 (j >> 1) + i0 + p at that bit, and 8 more for the
+    // high half). After the shifts below, pair p's planes sit at bits 2p of
+    // hs and p of ls (low half) and 16 more (high half).
     const int i0 = 4 * (j & 1);
-    const uint32_t ls = (lo8 | (hi8 << 16)) >> i0;
-    const uint32_t hs = (w0 >> (2 * i0)) << 1;
-#pragma unroll
-    for (int p = 0; p < 4; ++p)
-      b[p] = ((hs >> (2 * p)) & 0x00060006u) | ((ls >> p) & 0x00010001u) | kMagic1024x2;
+    const uint32_t hs = w0 >> (2 * i0);
+    const uint32_t t = w1 >> (16 * (j >> 1) + i0);
+    const uint32_t ls = __builtin_amdgcn_perm(0u, t, 0x0C010C00u);  // bytes (0, -, 1, -) of t
+    b[0] = bfi(dm.m[0], hs << 2, bfi(dm.m[1], ls << 1, magic));
+    b[1] = bfi(dm.m[0], hs, bfi(dm.m[1], ls, magic));
+    b[2] = bfi(dm.m[0], hs >> 2, bfi(dm.m[1], ls >> 1, magic));
+    b[3] = bfi(dm.m[0], hs >> 4, bfi(dm.m[1], ls >> 2, magic));
   }
 }
 
