@@ -12,14 +12,17 @@
 //    Products too small to give every CU such a tile take 128 x 128 or
 //    64 x 64 tiles of 4 waves (the README's own benchmark shapes are of this
 //    kind).
-//  * Activations go through LDS (row pitch 72 halves, so the 16-byte
-//    fragment reads of a wave spread over all banks): three buffers rotate,
-//    the next slab is stored during the third 16-k step of the current one,
-//    and one barrier per slab suffices.
+//  * Activations go straight from memory into LDS (buffer loads with the
+//    LDS destination, no registers), three slabs rotating, each requested two
+//    slabs before its first read; rows are unpadded and their 16-byte chunks
+//    XOR-swizzled so the fragment reads of a wave spread over all banks. One
+//    barrier per slab publishes the next slab.
 //  * Weights never touch LDS. Each lane loads exactly the packed words of its
 //    own B fragments (32 adjacent columns of one word row per half wave:
-//    128-byte segments) with buffer loads two slabs ahead, and dequantizes
-//    them in registers right before the MFMAs that use them.
+//    128-byte segments) with buffer loads two slabs ahead.
+//  * Software pipelining: while a 16-k step's MFMAs run, the next step's A
+//    fragments are read from LDS and its weight words dequantized, and the
+//    compiler is asked to interleave these with the MFMAs one by one.
 //  * Dequantization: codes are ORed into the mantissa of 1024.0 (a byte
 //    permute for 8-bit) and the zero point is subtracted in fp16. With one
 //    group per column, one packed add of c = -(1024 + z) rounded to fp16
@@ -27,7 +30,7 @@
 //    remainder (zero for integer zero points) is removed in the epilogue with
 //    the row sums of x, and the scale is applied to the fp32 accumulator. With smaller groups each half
 //    is (q - z) * scale in fp16 (one rounding of an exact difference).
-//  * Register sets of two slabs in flight and of the A fragments of two steps
+//  * Register sets of two slabs in flight and of the fragments of two steps
 //    are indexed by compile-time parity (two slabs per loop iteration), so no
 //    registers are copied between sets.
 //  * The epilogue stages the fp16 tile through LDS and writes rows with
@@ -42,7 +45,6 @@ namespace qmm {
 namespace {
 
 constexpr int BK = 64;
-constexpr int LDK = BK + 8;  // halves per LDS row of a staged activation slab
 constexpr int kCUs = 256;
 
 struct GemmArgs {
@@ -135,6 +137,26 @@ __device__ __forceinline__ int remap_block(int pid, int nblocks) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, size_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)(uint32_t)bytes, 0x00020000);
 }
+// Wait until at most n vector-memory operations of this wave are in flight
+// (s_waitcnt's vmcnt field, expcnt and lgkmcnt left unconstrained).
+#define QMM_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+
+// A 16-byte-per-lane load from a buffer straight into LDS: lane l's bytes
+// land at lds_addr + 16 l (lds_addr wave-uniform). Written as one asm block
+// because the compiler, seeing such a store through the builtin, would make
+// every later LDS read wait for it; completion is instead awaited with an
+// explicit vmcnt before the barrier that publishes the slab. No register is
+// written.
+__device__ __forceinline__ void load_to_lds16(__amdgpu_buffer_rsrc_t r, uint32_t lds_addr, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(r)
+               : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
 // Cache policy of the weight loads: the scope bit only (no non-temporal
 // hint), which measured fastest; a weight panel is reused by the row tiles
 // that run beside each other on one XCD.
@@ -155,14 +177,16 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
   constexpr int ACC = TM * TN * 16;  // accumulators per lane
   // Each group's three activation buffers; then, reusing them, the other
   // groups' partial sums and the output tile.
-  constexpr int kLdsHalves = cmax(cmax(KG * 3 * BM * LDK, BM * LDY), (KG - 1) * GW * ACC * 64 * 2);
+  constexpr int kLdsHalves = cmax(cmax(KG * 3 * BM * BK, BM * LDY), (KG - 1) * GW * ACC * 64 * 2);
   __shared__ __attribute__((aligned(16))) f16 lds[kLdsHalves];
   __shared__ float rsum[BM];  // row sums of x, for zero points that are not integers
   constexpr int GT = 64 * GW;  // threads per group
   constexpr int THREADS = GT * KG;
-  constexpr int CA = BM * BK / 8 / GT;  // 16-byte activation chunks per thread per slab
+  constexpr int CQ = BM * BK * 2 / 1024 / GW;  // 1 KiB activation loads per wave per slab
+  static_assert(CQ >= 1 && CQ * GW * 1024 == BM * BK * 2, "slab must split into 1 KiB loads per wave");
   constexpr int NW = Frag<BITS>::NW, NL = Frag<BITS>::NL;
   constexpr int NG = POST_SCALE ? 1 : 2;     // zero/scale pairs per column per slab (one per 32 k)
+  constexpr int NBS = TN * (NW + NL);        // weight loads per wave per 16-k step
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -190,15 +214,21 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
   const __amdgpu_buffer_rsrc_t rz = make_rsrc(g.zeros, (size_t)(g.K / 32 / g.upg) * g.N * 2);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(g.scales, (size_t)(g.K / 32 / g.upg) * g.N * 2);
 
-  // A (activations) go through LDS: rows a_row + (GT / 8) i, clamped to
-  // M - 1 (rows beyond M only feed outputs that are never stored), 8 halves
-  // at column chunk a_chk.
-  const int a_row = gtid >> 3, a_chk = gtid & 7;
-  uint32_t a_voff[CA];
+  // A (activations) go through LDS, loaded straight into it. One load of a
+  // wave fills 1 KiB: 8 rows of the 64-k slab, 128 bytes each, unpadded. The
+  // 16-byte chunk c of row r sits in slot c ^ (r & 7) ^ ((r >> 3) & 1), so the
+  // fragment reads of 8 (or 16) consecutive rows fall on distinct banks. Rows
+  // are clamped to M - 1 (rows beyond M only feed outputs that are never
+  // stored); chunks past the end of K are written as zeros instead.
+  uint32_t a_voff[CQ];
+  int a_c[CQ];
 #pragma unroll
-  for (int i = 0; i < CA; ++i)
-    a_voff[i] = (uint32_t)(min(m0 + a_row + (GT / 8) * i, g.M - 1) * g.K + 8 * a_chk) * 2u;
-  f16* const glds = lds + kg * 3 * BM * LDK;  // the group's activation buffers
+  for (int q = 0; q < CQ; ++q) {
+    const int row = (gwave * CQ + q) * 8 + (lane >> 3);
+    a_c[q] = (lane & 7) ^ (row & 7) ^ ((row >> 3) & 1);
+    a_voff[q] = (uint32_t)min(m0 + row, g.M - 1) * (uint32_t)g.K * 2u + 16u * (uint32_t)a_c[q];
+  }
+  f16* const glds = lds + kg * 3 * BM * BK;  // the group's activation buffers
 
   // B (weights) go straight to registers: each lane reads the words of its
   // fragments. Columns beyond N are clamped to N - 1 (never stored).
@@ -206,29 +236,29 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
 #pragma unroll
   for (int t = 0; t < TN; ++t) b_voff[t] = (uint32_t)min(n0 + (BN / WN) * wn + 32 * t + (lane & 31), g.N - 1) * 4u;
 
-  auto loadA = [&](u32x4 (&SA)[CA], int ks_in) {
-    const int ks = min(ks_in, nk - 1);  // slabs past the end reload the last one (never used)
-    // Chunks past the end of K (second half of the last slab when K % 64 != 0)
-    // read the chunk 32 halves before instead; they are zeroed when stored.
-    const uint32_t adj = (KTAIL && ks * BK + 8 * a_chk >= g.K) ? 64u : 0u;
+  // Slab ks into buffer buf. Slabs past the end of K (which pad the group's
+  // slab count) and chunks past it are zeros: their lanes read out of range,
+  // which writes zeros (a zero-length resource, or the offset x's size; x's
+  // size is a multiple of 64 below 4 GiB, so that offset does not wrap).
+  // Nothing here branches, so the step's instructions stay one block.
+  const __amdgpu_buffer_rsrc_t rnone = make_rsrc(g.x, 0);
+  const uint32_t x_bytes = (uint32_t)g.M * (uint32_t)g.K * 2u;
+  auto dmaA = [&](int buf, int ks) {
+    const uint32_t A = lds_offset(glds + buf * BM * BK);
+    const __amdgpu_buffer_rsrc_t r = (!KTAIL && ks >= nk) ? rnone : rx;
 #pragma unroll
-    for (int i = 0; i < CA; ++i) SA[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, a_voff[i] - adj, ks * BK * 2, 0);
-  };
-  auto storeA = [&](const u32x4 (&SA)[CA], int buf, int ks) {
-    f16* A = glds + buf * BM * LDK;
-    // Chunks at or past the end of K are stored as zeros: the second half of a
-    // final 32-k slab, and the whole slab that pads an odd slab count.
-    const bool zero = ks * BK + 8 * a_chk >= g.K;
-#pragma unroll
-    for (int i = 0; i < CA; ++i) {
-      u32x4 v = SA[i];
-      if (zero) v = u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(A + (a_row + (GT / 8) * i) * LDK + 8 * a_chk) = v;
+    for (int q = 0; q < CQ; ++q) {
+      uint32_t off = a_voff[q] + (uint32_t)ks * (BK * 2);
+      if constexpr (KTAIL) off = ks * BK + 8 * a_c[q] >= g.K ? x_bytes : off;
+      load_to_lds16(r, A + (gwave * CQ + q) * 1024, off);
     }
   };
+  // Rows of the lane's fragments (32 apart) share their chunk swizzle.
+  const int fr = (BM / WM) * wm + (lane & 31);
+  const int fkey = (fr & 7) ^ ((fr >> 3) & 1);
   auto frag_a = [&](int buf, int s, int t) {
-    const f16* A = glds + buf * BM * LDK;
-    return *reinterpret_cast<const f16x8*>(A + ((BM / WM) * wm + 32 * t + (lane & 31)) * LDK + 16 * s + 8 * kc);
+    const f16* A = glds + buf * BM * BK;
+    return *reinterpret_cast<const f16x8*>(A + (fr + 32 * t) * BK + 8 * ((2 * s + kc) ^ fkey));
   };
 
   // Weight words of one k-step for all TN tiles, plus the step's zero point
@@ -329,49 +359,67 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-  // Register sets: weight words and zero/scale values of two slabs in flight
-  // (slab ks uses set ks % 2 and refills it with slab ks + 2), and the A
-  // fragments of the current and next 16-k step (set s % 2). Indices are
-  // compile-time constants throughout, so nothing is copied between sets.
-  u32x4 SA[CA];
+  // Register sets: weight words and zero/scale values of two slabs in flight,
+  // and the A and B fragments of the current and next 16-k step (set s % 2).
+  // Indices are compile-time constants throughout, so nothing is copied
+  // between sets.
   BStep B0[4], B1[4];
   ZS Z0, Z1;
   f16x8 fa[2][TM];
+  f16x8 fb[2][TN];
 
-  // One 64-k slab: four 16-k steps of TM x TN MFMAs. A fragments of the next
-  // step are read from LDS while the current step's MFMAs run; each step's
-  // weight words are dequantized in registers and their registers refilled
-  // with the same step of slab ks + 2. Activation slabs rotate through three
-  // LDS buffers: slab ks + 1, requested during step 3 of the slab before, is
+  // One 64-k slab: four 16-k steps of TM x TN MFMAs. While a step's MFMAs
+  // run, the next step's A fragments are read from LDS and its weight words
+  // dequantized; the registers those words held are refilled right away
+  // with the same step two slabs on. Activation slabs rotate through three
+  // LDS buffers: slab i + 1, requested during step 3 of the slab before, is
   // stored during step 2 into a buffer last read two slabs ago, and the one
-  // barrier per slab sits before step 3, so the first fragments of the next
-  // slab are read while step 3's MFMAs run.
-  auto slab = [&](auto fast_tag, int i, BStep (&B)[4], ZS& Z) __attribute__((always_inline)) {
+  // barrier per slab sits before step 3, whose next-step reads are the first
+  // of slab i + 1.
+  auto slab = [&](auto fast_tag, int i, BStep (&Bc)[4], BStep (&Bn)[4], ZS& Zc, ZS& Zn) __attribute__((always_inline)) {
     const int cur = i % 3, nxt = (i + 1) % 3;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       // Scheduling fence: each step's instructions stay in their step.
       __builtin_amdgcn_sched_barrier(0);
-      if (s == 3) __syncthreads();  // slab ks + 1 is in LDS
-#pragma unroll
-      for (int t = 0; t < TM; ++t) fa[(s + 1) & 1][t] = s < 3 ? frag_a(cur, s + 1, t) : frag_a(nxt, 0, t);
-      f16x8 fb[TN];
-#pragma unroll
-      for (int t = 0; t < TN; ++t) fb[t] = frag_b(fast_tag, B[s], Z, t, s);
-      loadB(B[s], gslab(i + 2), s);
-      if (!POST_SCALE && s == 3) loadZS(Z, gslab(i + 2));
-      if (s == 2) storeA(SA, nxt, gslab(i + 1));
-      if (s == 3) loadA(SA, gslab(i + 2));  // three steps before it is stored
+      if (s == 3) {
+        // This wave's loads of slab i + 1, issued two slabs ago, are done:
+        // at least 7 steps' weight loads were issued after them.
+        QMM_WAIT_VMCNT(cmin(7 * NBS, 63));
+        __syncthreads();  // slab i + 1 is in LDS
+      }
 #pragma unroll
       for (int a = 0; a < TM; ++a)
 #pragma unroll
         for (int b = 0; b < TN; ++b) {
           if constexpr (BF)
             acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa[s & 1][a]),
-                                                                 __builtin_bit_cast(bf16x8, fb[b]), acc[a][b], 0, 0, 0);
+                                                                 __builtin_bit_cast(bf16x8, fb[s & 1][b]), acc[a][b], 0, 0, 0);
           else
-            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[s & 1][a], fb[b], acc[a][b], 0, 0, 0);
+            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[s & 1][a], fb[s & 1][b], acc[a][b], 0, 0, 0);
         }
+#pragma unroll
+      for (int t = 0; t < TM; ++t) fa[(s + 1) & 1][t] = s < 3 ? frag_a(cur, s + 1, t) : frag_a(nxt, 0, t);
+      if (s < 3) {
+#pragma unroll
+        for (int t = 0; t < TN; ++t) fb[(s + 1) & 1][t] = frag_b(fast_tag, Bc[s + 1], Zc, t, s + 1);
+        loadB(Bc[s + 1], gslab(i + 2), s + 1);
+      } else {
+#pragma unroll
+        for (int t = 0; t < TN; ++t) fb[0][t] = frag_b(fast_tag, Bn[0], Zn, t, 0);
+        loadB(Bn[0], gslab(i + 3), 0);
+      }
+      if (!POST_SCALE && s == 3) loadZS(Zc, gslab(i + 2));
+      if (s == 3) dmaA(cur, gslab(i + 3));  // every wave is past its reads of slab i
+      // Interleave: each MFMA is followed by a share of the step's other work.
+      constexpr int NM = TM * TN;
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // an LDS read
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // vector ALU
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // a global load
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -380,20 +428,21 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
   // and the accumulators one place.
   auto run = [&](auto fast_tag) __attribute__((always_inline)) {
     for (int i = 0; i < ni; i += 2) {
-      slab(fast_tag, i, B0, Z0);
-      slab(fast_tag, i + 1, B1, POST_SCALE ? Z0 : Z1);
+      slab(fast_tag, i, B0, B1, Z0, POST_SCALE ? Z0 : Z1);
+      slab(fast_tag, i + 1, B1, B0, POST_SCALE ? Z0 : Z1, Z0);
     }
   };
 
-  loadA(SA, gslab(0));
+  dmaA(0, gslab(0));
+  dmaA(1, gslab(1));
+  dmaA(2, gslab(2));
 #pragma unroll
   for (int s = 0; s < 4; ++s) loadB(B0[s], gslab(0), s);
   loadZS(Z0, gslab(0));  // with one group per column: the only zero/scale load
 #pragma unroll
   for (int s = 0; s < 4; ++s) loadB(B1[s], gslab(1), s);
   if (!POST_SCALE) loadZS(Z1, gslab(1));
-  storeA(SA, 0, gslab(0));
-  loadA(SA, gslab(1));
+  QMM_WAIT_VMCNT(cmin(8 * NBS, 63));  // the three slabs' loads, issued first
   __syncthreads();
 #pragma unroll
   for (int t = 0; t < TM; ++t) fa[0][t] = frag_a(0, 0, t);
@@ -409,7 +458,13 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
       }
     }
   }
-  run(std::integral_constant<bool, POST_SCALE>{});
+  auto start = [&](auto fast_tag) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < TN; ++t) fb[0][t] = frag_b(fast_tag, B0[0], Z0, t, 0);
+    loadB(B0[0], gslab(2), 0);
+    run(fast_tag);
+  };
+  start(std::integral_constant<bool, POST_SCALE>{});
 
   // Accumulator register r of a 32 x 32 tile holds row 8 (r / 4) + 4 (lane / 32)
   // + r % 4, column lane % 32.
@@ -429,6 +484,7 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
     if constexpr (POST_SCALE && !BF) delta[t] = (half_bits_to_float(Z0.z[t][0]) + 1024.f) + (float)zc[t].x;
     off = off || delta[t] != 0.f;
   }
+  QMM_WAIT_VMCNT(0);  // loads into LDS past the last slab are done before the LDS is reused
   const bool need = __syncthreads_or(off);  // every group is past its last slab
   if constexpr (KG > 1) {
     // Groups 1.. hand their sums to group 0 through LDS (over the activation
