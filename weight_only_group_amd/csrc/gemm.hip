@@ -231,10 +231,21 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
   f16* const glds = lds + kg * 3 * BM * BK;  // the group's activation buffers
 
   // B (weights) go straight to registers: each lane reads the words of its
-  // fragments. Columns beyond N are clamped to N - 1 (never stored).
-  uint32_t b_voff[TN];
+  // fragments. With an even number of tiles per wave, tiles 2p and 2p + 1
+  // take interleaved columns (column j of tile 2p + e is column 2 j + e of
+  // the pair's 64), so that one 8-byte load brings a lane the words of both.
+  // Columns beyond N are clamped (never stored).
+  constexpr bool PAIR = TN % 2 == 0;
+  constexpr int NP = PAIR ? TN / 2 : 1;
+  auto tile_col = [&](int t) {  // the lane's column of tile t, within the block
+    return PAIR ? (BN / WN) * wn + 64 * (t >> 1) + 2 * (lane & 31) + (t & 1) : (BN / WN) * wn + 32 * t + (lane & 31);
+  };
+  uint32_t b_voff[TN];  // per tile: byte offset of the lane's column in a word row
+  uint32_t p_voff[NP];  // per pair: the same for its even column (clamped to N - 2, 8-byte aligned)
 #pragma unroll
-  for (int t = 0; t < TN; ++t) b_voff[t] = (uint32_t)min(n0 + (BN / WN) * wn + 32 * t + (lane & 31), g.N - 1) * 4u;
+  for (int t = 0; t < TN; ++t) b_voff[t] = (uint32_t)min(n0 + tile_col(t), g.N - 1) * 4u;
+#pragma unroll
+  for (int p = 0; p < NP; ++p) p_voff[p] = (uint32_t)min(n0 + tile_col(2 * p), g.N - 2) * 4u;
 
   // Slab ks into buffer buf. Slabs past the end of K (which pad the group's
   // slab count) and chunks past it are zeros: their lanes read out of range,
@@ -270,14 +281,33 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
   auto loadB = [&](BStep& S, int ks_in, int s) {
     const int ks = min(ks_in, nk - 1);
     const bool past = KTAIL && ks * BK + 16 * s >= g.K;  // this step is past the end of K: read row 0
+    // kc is a lane property: it goes in the per-lane offset
+    const uint32_t kcoff = past ? 0u : (BITS == 8 ? 2u * kc : (BITS == 4 ? (uint32_t)kc : 0u)) * (uint32_t)g.N * 4u;
+    if constexpr (PAIR) {
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          const int row0 = past ? 0 : frag_row<BITS>(ks, s, 0, w);
+          const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rw, p_voff[p] + kcoff, row0 * g.N * 4, kWeightPolicy);
+          S.w[2 * p][w] = v.x;
+          S.w[2 * p + 1][w] = v.y;
+        }
+        if constexpr (NL > 0) {
+          const int lrow = past ? 0 : ks * 2 + (s >> 1);
+          const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rl, p_voff[p], lrow * g.N * 4, kWeightPolicy);
+          S.l[2 * p][0] = v.x;
+          S.l[2 * p + 1][0] = v.y;
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        // kc is a lane property: it goes in the per-lane offset
         const int row0 = past ? 0 : frag_row<BITS>(ks, s, 0, w);
-        const uint32_t kcoff = (BITS == 8 ? 2u * kc : (BITS == 4 ? (uint32_t)kc : 0u)) * (uint32_t)g.N * 4u;
-        S.w[t][w] = __builtin_amdgcn_raw_buffer_load_b32(rw, b_voff[t] + (past ? 0u : kcoff), row0 * g.N * 4, kWeightPolicy);
+        S.w[t][w] = __builtin_amdgcn_raw_buffer_load_b32(rw, b_voff[t] + kcoff, row0 * g.N * 4, kWeightPolicy);
       }
       if constexpr (NL > 0) {
         const int lrow = past ? 0 : ks * 2 + (s >> 1);
@@ -537,7 +567,7 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
     constexpr bool NEED = decltype(need_tag)::value;
 #pragma unroll
     for (int b = 0; b < TN; ++b) {
-      const int col = (BN / WN) * wn + 32 * b + (lane & 31);
+      const int col = tile_col(b);
       float sc = 1.f, bv = 0.f;
       if constexpr (POST_SCALE) sc = bits_to_float<BF>(g.scales[min(n0 + col, g.N - 1)]);
       if (g.bias) bv = bits_to_float<BF>(g.bias[min(n0 + col, g.N - 1)]);
