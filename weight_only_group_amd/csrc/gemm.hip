@@ -189,7 +189,10 @@ constexpr int kWeightPolicy = 1;
 // fp32 sums are added in group order at the end.
 // BF: bf16 data (x, scales, zero points, bias, y); dequantized codes are then
 // formed in fp32 and rounded once to bf16 for the bf16 matrix-core form.
-template <int BITS, bool POST_SCALE, bool KTAIL, int WM, int WN, int TM, int TN, int KG, bool BF>
+// ZM, how zero points and scales vary along K: 2, one group per column (the
+// scale is applied to the fp32 sums); 1, groups of whole 64-k slabs (one
+// row per slab); 0, groups of 32-k units (one row per unit).
+template <int BITS, int ZM, bool KTAIL, int WM, int WN, int TM, int TN, int KG, bool BF>
 __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) {
   constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN;
   constexpr int LDY = BN + 8;  // halves per LDS row of the staged output tile
@@ -205,7 +208,8 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
   constexpr int CQ = BM * BK * 2 / 1024 / GW;  // 1 KiB activation loads per wave per slab
   static_assert(CQ >= 1 && CQ * GW * 1024 == BM * BK * 2, "slab must split into 1 KiB loads per wave");
   constexpr int NW = Frag<BITS>::NW, NL = Frag<BITS>::NL;
-  constexpr int NG = POST_SCALE ? 1 : 2;     // zero/scale pairs per column per slab (one per 32 k)
+  constexpr bool POST_SCALE = ZM == 2;
+  constexpr int NG = ZM == 0 ? 2 : 1;  // rows of zero points / scales per slab
   constexpr int NBS = TN * (NW + NL);        // weight loads per wave per 16-k step
 
   const int tid = threadIdx.x;
@@ -335,9 +339,11 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
     }
   };
   // Zero points and scales of this lane's TN columns: once (one group per
-  // column) or per 32-k unit.
+  // column) or per slab. With paired tiles the lane's two columns are
+  // adjacent, and one 4-byte load brings both (tile 2p in the low half).
+  constexpr int NZ = PAIR ? NP : TN;
   struct ZS {
-    uint16_t z[TN][NG], s[TN][NG];
+    uint32_t z[NZ][NG], s[NZ][NG];
   };
   auto loadZS = [&](ZS& Z, int ks_in) {
     const int ks = min(ks_in, nk - 1);
@@ -346,11 +352,25 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
       const int u = POST_SCALE ? 0 : min(ks * 2 + h, g.K / 32 - 1);
       const int grp = POST_SCALE ? 0 : (g.upg_log2 >= 0 ? (u >> g.upg_log2) : u / g.upg);
 #pragma unroll
-      for (int t = 0; t < TN; ++t) {
-        Z.z[t][h] = __builtin_amdgcn_raw_buffer_load_b16(rz, b_voff[t] / 2u, grp * g.N * 2, 0);
-        Z.s[t][h] = __builtin_amdgcn_raw_buffer_load_b16(rs, b_voff[t] / 2u, grp * g.N * 2, 0);
+      for (int q = 0; q < NZ; ++q) {
+        if constexpr (PAIR) {
+          Z.z[q][h] = __builtin_amdgcn_raw_buffer_load_b32(rz, p_voff[q] / 2u, grp * g.N * 2, 0);
+          Z.s[q][h] = __builtin_amdgcn_raw_buffer_load_b32(rs, p_voff[q] / 2u, grp * g.N * 2, 0);
+        } else {
+          Z.z[q][h] = __builtin_amdgcn_raw_buffer_load_b16(rz, b_voff[q] / 2u, grp * g.N * 2, 0);
+          Z.s[q][h] = __builtin_amdgcn_raw_buffer_load_b16(rs, b_voff[q] / 2u, grp * g.N * 2, 0);
+        }
       }
     }
+  };
+  // Bits of tile t's zero point / scale for 16-k step s.
+  auto zbits = [&](const ZS& Z, int t, int s) -> uint16_t {
+    const int h = NG == 2 ? (s >> 1) : 0;
+    return PAIR ? (uint16_t)(Z.z[t >> 1][h] >> (16 * (t & 1))) : (uint16_t)Z.z[t][h];
+  };
+  auto sbits = [&](const ZS& Z, int t, int s) -> uint16_t {
+    const int h = NG == 2 ? (s >> 1) : 0;
+    return PAIR ? (uint16_t)(Z.s[t >> 1][h] >> (16 * (t & 1))) : (uint16_t)Z.s[t][h];
   };
   // One group per column: c = -(1024 + z) rounded to fp16, per column. For
   // |z| < 1024 it is an integer, and 1024 + q + c = q - round(z) exactly, so
@@ -371,8 +391,8 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
       if constexpr (POST_SCALE) {
         cz = czf[t];
       } else {
-        cz = 1024.f + bits_to_float<true>(Z.z[t][s >> 1]);
-        sc = bits_to_float<true>(Z.s[t][s >> 1]);
+        cz = 1024.f + bits_to_float<true>(zbits(Z, t, s));
+        sc = bits_to_float<true>(sbits(Z, t, s));
       }
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
@@ -383,15 +403,31 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
     } else if constexpr (FAST) {
 #pragma unroll
       for (int p = 0; p < 4; ++p) d[p] = as_u32(as_f16x2(h[p]) + zc[t]);
+    } else if constexpr (BITS == 4 && !POST_SCALE) {
+      // A byte of two codes in both halves of 1024.0, masked to the even
+      // code at mantissa bit 0 and the odd one at bit 4 (1024 + q0 and
+      // 1024 + 16 q1); one packed FMA by (1, 1/16) less (1024, 64) gives the
+      // codes exactly. Then (q - z) * s as below, the same roundings.
+      const f16x2 ee = f16x2{(f16)1.f, (f16)0.0625f};
+      const f16x2 mm = f16x2{(f16)(-1024.f), (f16)(-64.f)};
+      const f16 zh = __builtin_bit_cast(f16, zbits(Z, t, s));
+      const f16 sh = __builtin_bit_cast(f16, sbits(Z, t, s));
+      const f16x2 zz = f16x2{(f16)-zh, (f16)-zh};
+      const f16x2 ss = f16x2{sh, sh};
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t hp = __builtin_amdgcn_perm(0x64646464u, S.w[t][0], 0x04000400u | (uint32_t)p | ((uint32_t)p << 16)) & 0x64F0640Fu;
+        d[p] = as_u32((__builtin_elementwise_fma(as_f16x2(hp), ee, mm) + zz) * ss);
+      }
     } else {
       const f16x2 m1024 = f16x2{(f16)(-1024.f), (f16)(-1024.f)};
-      const f16 zh = __builtin_bit_cast(f16, Z.z[t][POST_SCALE ? 0 : (s >> 1)]);
+      const f16 zh = __builtin_bit_cast(f16, zbits(Z, t, s));
       const f16x2 zz = f16x2{(f16)-zh, (f16)-zh};
       if constexpr (POST_SCALE) {
 #pragma unroll
         for (int p = 0; p < 4; ++p) d[p] = as_u32((as_f16x2(h[p]) + m1024) + zz);
       } else {
-        const f16 sh = __builtin_bit_cast(f16, Z.s[t][s >> 1]);
+        const f16 sh = __builtin_bit_cast(f16, sbits(Z, t, s));
         const f16x2 ss = f16x2{sh, sh};
 #pragma unroll
         for (int p = 0; p < 4; ++p) d[p] = as_u32(((as_f16x2(h[p]) + m1024) + zz) * ss);
@@ -500,9 +536,9 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
       if constexpr (BF) {
-        czf[t] = 1024.f + bits_to_float<true>(Z0.z[t][0]);
+        czf[t] = 1024.f + bits_to_float<true>(zbits(Z0, t, 0));
       } else {
-        const f16 c = (f16)((f16)(-1024.f) - __builtin_bit_cast(f16, Z0.z[t][0]));
+        const f16 c = (f16)((f16)(-1024.f) - __builtin_bit_cast(f16, zbits(Z0, t, 0)));
         zc[t] = f16x2{c, c};
       }
     }
@@ -530,7 +566,7 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
 #pragma unroll
   for (int t = 0; t < TN; ++t) {
     delta[t] = 0.f;
-    if constexpr (POST_SCALE && !BF) delta[t] = (half_bits_to_float(Z0.z[t][0]) + 1024.f) + (float)zc[t].x;
+    if constexpr (POST_SCALE && !BF) delta[t] = (half_bits_to_float(zbits(Z0, t, 0)) + 1024.f) + (float)zc[t].x;
     off = off || delta[t] != 0.f;
   }
   QMM_WAIT_VMCNT(0);  // loads into LDS past the last slab are done before the LDS is reused
@@ -620,13 +656,15 @@ hipError_t launch_tiles(GemmArgs a, hipStream_t s) {
   a.mblocks = (a.M + BM - 1) / BM;
   a.nblocks = (a.N + BN - 1) / BN;
   const int nblocks = a.mblocks * a.nblocks;
-  const bool post = a.upg * 32 == a.K;
+  const int zm = a.upg * 32 == a.K ? 2 : (a.upg % 2 == 0 ? 1 : 0);
   const bool tail = a.K % BK != 0;
   constexpr int T = 64 * WM * WN * KG;
-  if (post && !tail) gemm_kernel<BITS, true, false, WM, WN, TM, TN, KG, BF><<<nblocks, T, 0, s>>>(a);
-  else if (post) gemm_kernel<BITS, true, true, WM, WN, TM, TN, KG, BF><<<nblocks, T, 0, s>>>(a);
-  else if (!tail) gemm_kernel<BITS, false, false, WM, WN, TM, TN, KG, BF><<<nblocks, T, 0, s>>>(a);
-  else gemm_kernel<BITS, false, true, WM, WN, TM, TN, KG, BF><<<nblocks, T, 0, s>>>(a);
+  if (zm == 2 && !tail) gemm_kernel<BITS, 2, false, WM, WN, TM, TN, KG, BF><<<nblocks, T, 0, s>>>(a);
+  else if (zm == 2) gemm_kernel<BITS, 2, true, WM, WN, TM, TN, KG, BF><<<nblocks, T, 0, s>>>(a);
+  else if (zm == 1 && !tail) gemm_kernel<BITS, 1, false, WM, WN, TM, TN, KG, BF><<<nblocks, T, 0, s>>>(a);
+  else if (zm == 1) gemm_kernel<BITS, 1, true, WM, WN, TM, TN, KG, BF><<<nblocks, T, 0, s>>>(a);
+  else if (!tail) gemm_kernel<BITS, 0, false, WM, WN, TM, TN, KG, BF><<<nblocks, T, 0, s>>>(a);
+  else gemm_kernel<BITS, 0, true, WM, WN, TM, TN, KG, BF><<<nblocks, T, 0, s>>>(a);
   return hipGetLastError();
 }
 
