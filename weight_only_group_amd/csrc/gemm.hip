@@ -195,12 +195,11 @@ constexpr int kWeightPolicy = 1;
 template <int BITS, int ZM, bool KTAIL, int WM, int WN, int TM, int TN, int KG, bool BF>
 __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) {
   constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN;
-  constexpr int LDY = BN + 8;  // halves per LDS row of the staged output tile
   constexpr int GW = WM * WN;  // waves per group
   constexpr int ACC = TM * TN * 16;  // accumulators per lane
   // Each group's three activation buffers; then, reusing them, the other
-  // groups' partial sums and the output tile.
-  constexpr int kLdsHalves = cmax(cmax(KG * 3 * BM * BK, BM * LDY), (KG - 1) * GW * ACC * 64 * 2);
+  // groups' partial sums.
+  constexpr int kLdsHalves = cmax(KG * 3 * BM * BK, (KG - 1) * GW * ACC * 64 * 2);
   __shared__ __attribute__((aligned(16))) f16 lds[kLdsHalves];
   __shared__ float rsum[BM];  // row sums of x, for zero points that are not integers
   constexpr int GT = 64 * GW;  // threads per group
@@ -596,7 +595,6 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
             for (int r = 0; r < 16; ++r)
               acc[a][b][r] += part[(((j - 1) * GW + gwave) * ACC + (a * TN + b) * 16 + r) * 64 + lane];
     }
-    __syncthreads();  // the output tile reuses the same LDS
   }
   if (need) {
     for (int row = tid >> 3; row < BM; row += THREADS / 8) {
@@ -616,37 +614,51 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
   }
 
   // Epilogue: remainder correction, scale (one group per column) and bias in
-  // fp32, one rounding to fp16, the tile staged in LDS, rows written with
-  // 16-byte stores. The accumulators are only read.
-  auto emit = [&](auto need_tag) __attribute__((always_inline)) {
+  // fp32, one rounding to fp16, stored straight from the accumulators. With
+  // paired tiles a lane's two columns are adjacent: one 4-byte store, and the
+  // 32 lanes of a row write 128 contiguous bytes. Tiles inside the output
+  // store unconditionally; edge tiles check each row and column.
+  auto emit = [&](auto need_tag, auto full_tag) __attribute__((always_inline)) {
     constexpr bool NEED = decltype(need_tag)::value;
+    constexpr bool FULL = decltype(full_tag)::value;
+    constexpr int TS = PAIR ? 2 : 1;  // tiles per store
 #pragma unroll
-    for (int b = 0; b < TN; ++b) {
-      const int col = tile_col(b);
-      float sc = 1.f, bv = 0.f;
-      if constexpr (POST_SCALE) sc = bits_to_float<BF>(g.scales[min(n0 + col, g.N - 1)]);
-      if (g.bias) bv = bits_to_float<BF>(g.bias[min(n0 + col, g.N - 1)]);
+    for (int q = 0; q < TN / TS; ++q) {
+      const int col = tile_col(TS * q);  // even when paired
+      float sc[TS], bv[TS];
+#pragma unroll
+      for (int e = 0; e < TS; ++e) {
+        const int n = min(n0 + col + e, g.N - 1);
+        sc[e] = POST_SCALE ? bits_to_float<BF>(g.scales[n]) : 1.f;
+        bv[e] = g.bias ? bits_to_float<BF>(g.bias[n]) : 0.f;
+      }
+      const bool col_ok = FULL || n0 + col < g.N;
 #pragma unroll
       for (int a = 0; a < TM; ++a)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float v = acc[a][b][r];
-          if constexpr (NEED) v -= delta[b] * rsum[acc_row(a, r)];
-          lds[acc_row(a, r) * LDY + col] = __builtin_bit_cast(f16, float_to_bits<BF>(v * sc + bv));
+          const int row = acc_row(a, r);
+          uint32_t out = 0;
+#pragma unroll
+          for (int e = 0; e < TS; ++e) {
+            float v = acc[a][TS * q + e][r];
+            if constexpr (NEED) v -= delta[TS * q + e] * rsum[row];
+            out |= (uint32_t)float_to_bits<BF>(v * sc[e] + bv[e]) << (16 * e);
+          }
+          uint16_t* dst = g.y + (size_t)(m0 + row) * g.N + n0 + col;
+          if (FULL || (col_ok && m0 + row < g.M)) {
+            if constexpr (PAIR) *reinterpret_cast<uint32_t*>(dst) = out;
+            else *dst = (uint16_t)out;
+          }
         }
     }
   };
   if (kg == 0) {  // scalar
-    if (need) emit(std::integral_constant<bool, true>{});
-    else emit(std::integral_constant<bool, false>{});
-  }
-  __syncthreads();
-#pragma unroll 4
-  for (int c = tid; c < BM * (BN / 8); c += THREADS) {
-    const int row = c / (BN / 8), chunk = c - row * (BN / 8);
-    const int gr = m0 + row, gc = n0 + 8 * chunk;
-    if (gr < g.M && gc < g.N)
-      *reinterpret_cast<u32x4*>(g.y + (size_t)gr * g.N + gc) = *reinterpret_cast<const u32x4*>(lds + row * LDY + 8 * chunk);
+    const bool full = m0 + BM <= g.M && n0 + BN <= g.N;
+    if (need && full) emit(std::integral_constant<bool, true>{}, std::integral_constant<bool, true>{});
+    else if (need) emit(std::integral_constant<bool, true>{}, std::integral_constant<bool, false>{});
+    else if (full) emit(std::integral_constant<bool, false>{}, std::integral_constant<bool, true>{});
+    else emit(std::integral_constant<bool, false>{}, std::integral_constant<bool, false>{});
   }
 }
 
