@@ -418,6 +418,34 @@ def test_workload_prefill_sampled_rows(gpu):
     _check(y_rows, y_ref, a, f"{wl.name} rows={len(rows)}")
 
 
+# Products wide enough for the 256 x 256 block tile, with partial tiles at the
+# right and bottom edges, across code widths and group layouts: groups of whole
+# 64-k slabs, groups of an odd number of 32-k units with a K tail, 32-k groups,
+# one group per column with a K tail (with integer and with non-integer zero
+# points). Sampled rows, every column, are compared with the oracle.
+LARGE_TILE = [(4100, 512, 4104, 4, 128, False), (4100, 480, 4104, 4, 96, False), (4100, 512, 4104, 3, 64, False),
+              (4100, 544, 4104, 8, -1, False), (4100, 544, 4104, 8, -1, True), (4100, 512, 4104, 2, 32, False),
+              (4100, 512, 4104, 1, 64, False)]
+
+
+@pytest.mark.parametrize("M,K,N,bits,gs,nonint", LARGE_TILE)
+def test_gemm_large_tile_sampled_rows(gpu, M, K, N, bits, gs, nonint):
+    _say(f"gemm large tile M={M} K={K} N={N} bits={bits} gs={gs} nonint-z={nonint}")
+    d = datagen.small_case(M, K, N, bits, gs, seed=K + bits * 7 + (gs if gs > 0 else 3))
+    if nonint:
+        d["zeros"] = np.random.default_rng(5).uniform(-1.5, (1 << bits) + 0.5, size=d["zeros"].shape).astype(np.float16)
+    g = _to_gpu_case(d)
+    qw, qlo = _pack_gpu(gpu, d["codes"], bits)
+    y = gpu.qmm_gemm(g["x"], qw, qlo, g["zeros"], g["scales"], bits, gs)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, 4095, 4096, M - 2, M - 1], rng.choice(M, 40, replace=False)]))
+    y_rows = y[torch.as_tensor(rows, device=DEV)].cpu().numpy()
+    w_ref = oracle.dequantize(d["codes"], d["scales"], d["zeros"], gs)
+    y_ref, a = oracle.matmul(d["x"][rows], w_ref)
+    _check(y_rows, y_ref, a, f"gemm large tile bits={bits} gs={gs}")
+
+
 def test_workspace_shared_across_shapes(gpu):
     """Calls of different shapes share one cached workspace: wider problems place their
     partial sums where a narrower problem's would not, and the arrival counters never move."""

@@ -673,8 +673,8 @@ hipError_t launch_tiles(GemmArgs a, hipStream_t s) {
   constexpr int T = 64 * WM * WN * KG;
   if (zm == 2 && !tail) gemm_kernel<BITS, 2, false, WM, WN, TM, TN, KG, BF><<<nblocks, T, 0, s>>>(a);
   else if (zm == 2) gemm_kernel<BITS, 2, true, WM, WN, TM, TN, KG, BF><<<nblocks, T, 0, s>>>(a);
-  else if (zm == 1 && !tail) gemm_kernel<BITS, 1, false, WM, WN, TM, TN, KG, BF><<<nblocks, T, 0, s>>>(a);
-  else if (zm == 1) gemm_kernel<BITS, 1, true, WM, WN, TM, TN, KG, BF><<<nblocks, T, 0, s>>>(a);
+  // Groups of whole slabs make K a multiple of 64: no tail.
+  else if (zm == 1) gemm_kernel<BITS, 1, false, WM, WN, TM, TN, KG, BF><<<nblocks, T, 0, s>>>(a);
   else if (!tail) gemm_kernel<BITS, 0, false, WM, WN, TM, TN, KG, BF><<<nblocks, T, 0, s>>>(a);
   else gemm_kernel<BITS, 0, true, WM, WN, TM, TN, KG, BF><<<nblocks, T, 0, s>>>(a);
   return hipGetLastError();
