@@ -393,11 +393,16 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
         cz = 1024.f + bits_to_float<true>(zbits(Z, t, s));
         sc = bits_to_float<true>(sbits(Z, t, s));
       }
+      // fma(h, 1, -cz) is h - cz with one rounding; with the 1 kept opaque
+      // the compiler converts the fp16 half inside the mixed-precision FMA
+      // (v_fma_mix_f32) instead of a conversion and a subtraction.
+      float one = 1.f;
+      asm("" : "+v"(one));
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         const f16x2 hp = as_f16x2(h[p]);
-        d[p] = POST_SCALE ? pack_bf16((float)hp.x - cz, (float)hp.y - cz)
-                          : pack_bf16(((float)hp.x - cz) * sc, ((float)hp.y - cz) * sc);
+        const float lo = __builtin_fmaf((float)hp.x, one, -cz), hi = __builtin_fmaf((float)hp.y, one, -cz);
+        d[p] = POST_SCALE ? pack_bf16(lo, hi) : pack_bf16(lo * sc, hi * sc);
       }
     } else if constexpr (FAST) {
 #pragma unroll
