@@ -511,12 +511,17 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs g) {
           decode8<BITS>(word_at<VEC>(wv[c][0], v), NW > 1 ? word_at<VEC>(wv[c][NW - 1], v) : 0u, j, dm, b);
           uint32_t d[4];
           if constexpr (BF) {
+            // A factor of 1 is kept opaque: the compiler would otherwise fold
+            // fma(h, 1, c) into a conversion and an add, where the
+            // mixed-precision FMA (v_fma_mix_f32) takes the fp16 half as is.
+            float one = 1.f;
+            asm("" : "+v"(one));
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
               const f16x2 h = as_f16x2(b[p]);
               const int c = pair_class<BITS>(p);
-              const float s_lo = 1.0f / (float)(1 << code_exp<BITS>(p, 0));
-              const float s_hi = 1.0f / (float)(1 << code_exp<BITS>(p, 1));
+              const float s_lo = code_exp<BITS>(p, 0) == 0 ? one : 1.0f / (float)(1 << code_exp<BITS>(p, 0));
+              const float s_hi = code_exp<BITS>(p, 1) == 0 ? one : 1.0f / (float)(1 << code_exp<BITS>(p, 1));
               if constexpr (SPLIT_E) {
                 // q exactly, then one rounding of q - z
                 d[p] = pack_bf16(__builtin_fmaf((float)h.x, s_lo, -1024.f * s_lo) - czf[c][v],
