@@ -82,6 +82,9 @@ __device__ __forceinline__ int frag_row(int ks, int s, int kc, int w) {
   else return ks * 4 + s;  // 2-bit and the 2-bit plane of 3-bit codes
 }
 
+// (a & m) | (b & ~m)
+__device__ __forceinline__ uint32_t bfi32(uint32_t m, uint32_t a, uint32_t b) { return (a & m) | (b & ~m); }
+
 // Four fp16 pairs 1024 + q (pair p = codes 2p, 2p + 1 of the lane's 8 k) from
 // the fragment's words. kc selects the lane's half of a 16-code word; s the
 // 16-k step within the 32 codes of a 1-bit plane word.
@@ -99,29 +102,29 @@ __device__ __forceinline__ void frag_codes(const uint32_t* w, const uint32_t* l,
       const uint32_t t = w[0] >> (8 * p);
       h[p] = (t & 0xFu) | ((t << 12) & 0xF0000u) | kMagic1024x2;
     }
-  } else if constexpr (BITS == 1) {
-    const uint32_t u = w[0] >> (16 * (s & 1) + 8 * kc);
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t t = u >> (2 * p);
-      h[p] = (t & 0x1u) | ((t << 15) & 0x10000u) | kMagic1024x2;
-    }
-  } else if constexpr (BITS == 2) {
-    const uint32_t u = w[0] >> (16 * kc);
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t t = u >> (4 * p);
-      h[p] = (t & 0x3u) | ((t << 14) & 0x30000u) | kMagic1024x2;
-    }
   } else {
-    const uint32_t u = w[0] >> (16 * kc);
-    const uint32_t v = l[0] >> (16 * (s & 1) + 8 * kc);
+    // The lane's 8 codes come from one extract per plane. Doubling a field
+    // (x | x << 15, or x << 1 | x << 15 for the 2-bit plane of 3-bit codes)
+    // puts code 2p + 1's bits 16 places above code 2p's once shifted right
+    // by p fields, so one or two bit-field inserts per pair into 1024.0 give
+    // both halves 1024 + q.
+    if constexpr (BITS == 1) {
+      const uint32_t v = __builtin_amdgcn_ubfe(w[0], 16 * (s & 1) + 8 * kc, 8);
+      const uint32_t b = v | (v << 15);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t t = u >> (4 * p), b = v >> (2 * p);
-      const uint32_t hi = ((t & 0x3u) << 1) | ((t << 15) & 0x60000u);
-      const uint32_t lo = (b & 0x1u) | ((b << 15) & 0x10000u);
-      h[p] = hi | lo | kMagic1024x2;
+      for (int p = 0; p < 4; ++p) h[p] = bfi32(0x00010001u, b >> (2 * p), kMagic1024x2);
+    } else if constexpr (BITS == 2) {
+      const uint32_t u = __builtin_amdgcn_ubfe(w[0], 16 * kc, 16);
+      const uint32_t b = u | (u << 14);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) h[p] = bfi32(0x00030003u, b >> (4 * p), kMagic1024x2);
+    } else {
+      const uint32_t u = __builtin_amdgcn_ubfe(w[0], 16 * kc, 16);
+      const uint32_t v = __builtin_amdgcn_ubfe(l[0], 16 * (s & 1) + 8 * kc, 8);
+      const uint32_t bh = (u << 1) | (u << 15), bl = v | (v << 15);
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+        h[p] = bfi32(0x00060006u, bh >> (4 * p), bfi32(0x00010001u, bl >> (2 * p), kMagic1024x2));
     }
   }
 }
