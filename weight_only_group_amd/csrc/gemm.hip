@@ -82,9 +82,6 @@ __device__ __forceinline__ int frag_row(int ks, int s, int kc, int w) {
   else return ks * 4 + s;  // 2-bit and the 2-bit plane of 3-bit codes
 }
 
-// (a & m) | (b & ~m)
-__device__ __forceinline__ uint32_t bfi32(uint32_t m, uint32_t a, uint32_t b) { return (a & m) | (b & ~m); }
-
 // Four fp16 pairs 1024 + q (pair p = codes 2p, 2p + 1 of the lane's 8 k) from
 // the fragment's words. kc selects the lane's half of a 16-code word; s the
 // 16-k step within the 32 codes of a 1-bit plane word.
@@ -97,34 +94,41 @@ __device__ __forceinline__ void frag_codes(const uint32_t* w, const uint32_t* l,
     h[2] = __builtin_amdgcn_perm(0x64646464u, w[1], 0x04010400u);
     h[3] = __builtin_amdgcn_perm(0x64646464u, w[1], 0x04030402u);
   } else if constexpr (BITS == 4) {
+    // Byte p of w in the low half and byte p of w >> 4 in the high half:
+    // codes 2p and 2p + 1 each in the low nibble of a half.
+    // The mask is held in a register so that the AND and the OR with 1024.0
+    // are one v_and_or_b32 (an instruction of this form takes one literal).
+    const uint32_t w4 = w[0] >> 4;
+    uint32_t m = 0x000F000Fu;
+    asm("" : "+v"(m));
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t t = w[0] >> (8 * p);
-      h[p] = (t & 0xFu) | ((t << 12) & 0xF0000u) | kMagic1024x2;
-    }
+    for (int p = 0; p < 4; ++p)
+      h[p] = (__builtin_amdgcn_perm(w4, w[0], 0x0C040C00u | (uint32_t)p | ((uint32_t)p << 16)) & m) | kMagic1024x2;
   } else {
     // The lane's 8 codes come from one extract per plane. Doubling a field
     // (x | x << 15, or x << 1 | x << 15 for the 2-bit plane of 3-bit codes)
     // puts code 2p + 1's bits 16 places above code 2p's once shifted right
     // by p fields, so one or two bit-field inserts per pair into 1024.0 give
     // both halves 1024 + q.
-    if constexpr (BITS == 1) {
-      const uint32_t v = __builtin_amdgcn_ubfe(w[0], 16 * (s & 1) + 8 * kc, 8);
-      const uint32_t b = v | (v << 15);
-#pragma unroll
-      for (int p = 0; p < 4; ++p) h[p] = bfi32(0x00010001u, b >> (2 * p), kMagic1024x2);
-    } else if constexpr (BITS == 2) {
-      const uint32_t u = __builtin_amdgcn_ubfe(w[0], 16 * kc, 16);
-      const uint32_t b = u | (u << 14);
-#pragma unroll
-      for (int p = 0; p < 4; ++p) h[p] = bfi32(0x00030003u, b >> (4 * p), kMagic1024x2);
-    } else {
+    if constexpr (BITS == 3) {
       const uint32_t u = __builtin_amdgcn_ubfe(w[0], 16 * kc, 16);
       const uint32_t v = __builtin_amdgcn_ubfe(l[0], 16 * (s & 1) + 8 * kc, 8);
       const uint32_t bh = (u << 1) | (u << 15), bl = v | (v << 15);
 #pragma unroll
-      for (int p = 0; p < 4; ++p)
-        h[p] = bfi32(0x00060006u, bh >> (4 * p), bfi32(0x00010001u, bl >> (2 * p), kMagic1024x2));
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t lo = ((bl >> (2 * p)) & 0x00010001u) | (kMagic1024x2 & ~0x00010001u);
+        h[p] = ((bh >> (4 * p)) & 0x00060006u) | (lo & ~0x00060006u);
+      }
+    } else {
+      // 1024.0 has zeros under the mask, so an insert is (x & m) | 1024.0;
+      // the mask is held in a register so that it is one v_and_or_b32.
+      uint32_t m = BITS == 1 ? 0x00010001u : 0x00030003u;
+      asm("" : "+v"(m));
+      const uint32_t x = BITS == 1 ? __builtin_amdgcn_ubfe(w[0], 16 * (s & 1) + 8 * kc, 8)
+                                   : __builtin_amdgcn_ubfe(w[0], 16 * kc, 16);
+      const uint32_t b = BITS == 1 ? x | (x << 15) : x | (x << 14);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) h[p] = ((b >> ((BITS == 1 ? 2 : 4) * p)) & m) | kMagic1024x2;
     }
   }
 }
