@@ -18,25 +18,28 @@
 //    XOR-swizzled so the fragment reads of a wave spread over all banks. One
 //    barrier per slab publishes the next slab.
 //  * Weights never touch LDS. Each lane loads exactly the packed words of its
-//    own B fragments (32 adjacent columns of one word row per half wave:
-//    128-byte segments) with buffer loads two slabs ahead.
+//    own B fragments with buffer loads two slabs ahead; a wave's two column
+//    tiles take interleaved columns, so one 8-byte load brings a lane the
+//    words of both (the 32 lanes of a half wave read 256 contiguous bytes).
 //  * Software pipelining: while a 16-k step's MFMAs run, the next step's A
 //    fragments are read from LDS and its weight words dequantized, and the
 //    compiler is asked to interleave these with the MFMAs one by one.
-//  * Dequantization: codes are ORed into the mantissa of 1024.0 (a byte
-//    permute for 8-bit) and the zero point is subtracted in fp16. With one
-//    group per column, one packed add of c = -(1024 + z) rounded to fp16
-//    subtracts z rounded to an integer (for |z| < 1024; exactly); the
-//    remainder (zero for integer zero points) is removed in the epilogue with
-//    the row sums of x, and the scale is applied to the fp32 accumulator. With smaller groups each half
-//    is (q - z) * scale in fp16 (one rounding of an exact difference).
+//  * Dequantization: codes are placed in the mantissa of 1024.0 (a byte
+//    permute, or a field extract and masked inserts) and the zero point is
+//    subtracted in fp16. With one group per column, one packed add of
+//    c = -(1024 + z) rounded to fp16 subtracts z rounded to an integer (for
+//    |z| < 1024; exactly); the remainder (zero for integer zero points) is
+//    removed in the epilogue with the row sums of x, and the scale is applied
+//    to the fp32 accumulator. With smaller groups each half is
+//    (q - z) * scale in fp16 (one rounding of an exact difference).
 //  * Register sets of two slabs in flight and of the fragments of two steps
 //    are indexed by compile-time parity (two slabs per loop iteration), so no
 //    registers are copied between sets.
-//  * The epilogue stages the fp16 tile through LDS and writes rows with
-//    16-byte stores.
-//  * Block ids are remapped so that each of the 8 XCDs (own L2 each) works on
-//    a contiguous run of tiles that share weight and activation panels.
+//  * The epilogue stores straight from the accumulators: a lane's two
+//    paired columns are adjacent, one 4-byte store each.
+//  * Each of the 8 XCDs (own L2 each) works on a contiguous range of tiles,
+//    walked in groups of row tiles so that the blocks in flight on it share
+//    weight and activation panels.
 #include <type_traits>
 
 #include "common.h"
@@ -73,7 +76,7 @@ template <> struct Frag<3> { static constexpr int NW = 1, NL = 1, EPS = 16; };
 template <> struct Frag<1> { static constexpr int NW = 1, NL = 0, EPS = 32; };
 
 // Word row (within the plane) of word w of k-step s of slab ks, for lane
-// chunk kc; and the bit offset of the lane's first code in that word.
+// chunk kc.
 template <int BITS>
 __device__ __forceinline__ int frag_row(int ks, int s, int kc, int w) {
   if constexpr (BITS == 8) return ks * 16 + 4 * s + 2 * kc + w;
@@ -94,10 +97,10 @@ __device__ __forceinline__ void frag_codes(const uint32_t* w, const uint32_t* l,
     h[2] = __builtin_amdgcn_perm(0x64646464u, w[1], 0x04010400u);
     h[3] = __builtin_amdgcn_perm(0x64646464u, w[1], 0x04030402u);
   } else if constexpr (BITS == 4) {
-    // Byte p of w in the low half and byte p of w >> 4 in the high half:
-    // codes 2p and 2p + 1 each in the low nibble of a half.
-    // The mask is held in a register so that the AND and the OR with 1024.0
-    // are one v_and_or_b32 (an instruction of this form takes one literal).
+    // Byte p of w in the low half and byte p of w >> 4 in the high half put
+    // codes 2p and 2p + 1 each in the low nibble of a half; the mask is held
+    // in a register so that the AND and the OR with 1024.0 are one
+    // v_and_or_b32 (an instruction of this form takes one literal).
     const uint32_t w4 = w[0] >> 4;
     uint32_t m = 0x000F000Fu;
     asm("" : "+v"(m));
@@ -172,13 +175,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, size_
 // land at lds_addr + 16 l (lds_addr wave-uniform). Written as one asm block
 // because the compiler, seeing such a store through the builtin, would make
 // every later LDS read wait for it; completion is instead awaited with an
-// explicit vmcnt before the barrier that publishes the slab. No register is
-// written.
+// explicit vmcnt before the barrier that publishes the slab. No vector
+// register is written; m0 carries the LDS address and is restored after.
 __device__ __forceinline__ void load_to_lds16(__amdgpu_buffer_rsrc_t r, uint32_t lds_addr, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(lds_addr), "v"(voff), "s"(r)
-               : "memory", "m0");
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr), "v"(voff), "s"(r)
+      : "memory");
 }
 __device__ __forceinline__ uint32_t lds_offset(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
@@ -223,7 +229,6 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kg = wave / GW;        // K group
   const int gwave = wave - kg * GW;  // wave within the group
-  const int gtid = tid - kg * GT;    // thread within the group
   const int wm = gwave / WN, wn = gwave % WN;
   const int kc = lane >> 5;  // k chunk of the lane in a fragment
 
