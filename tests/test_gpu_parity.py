@@ -423,27 +423,44 @@ def test_workload_prefill_sampled_rows(gpu):
 # 64-k slabs, groups of an odd number of 32-k units with a K tail, 32-k groups,
 # one group per column with a K tail (with integer and with non-integer zero
 # points). Sampled rows, every column, are compared with the oracle.
-LARGE_TILE = [(4100, 512, 4104, 4, 128, False), (4100, 480, 4104, 4, 96, False), (4100, 512, 4104, 3, 64, False),
-              (4100, 544, 4104, 8, -1, False), (4100, 544, 4104, 8, -1, True), (4100, 512, 4104, 2, 32, False),
-              (4100, 512, 4104, 1, 64, False)]
+LARGE_TILE = [(4100, 512, 4104, 4, 128, False, False), (4100, 480, 4104, 4, 96, False, True),
+              (4100, 512, 4104, 3, 64, False, False), (4100, 544, 4104, 8, -1, False, True),
+              (4100, 544, 4104, 8, -1, True, False), (4100, 512, 4104, 2, 32, False, False),
+              (4100, 512, 4104, 1, 64, False, False)]
 
 
-@pytest.mark.parametrize("M,K,N,bits,gs,nonint", LARGE_TILE)
-def test_gemm_large_tile_sampled_rows(gpu, M, K, N, bits, gs, nonint):
-    _say(f"gemm large tile M={M} K={K} N={N} bits={bits} gs={gs} nonint-z={nonint}")
+@pytest.mark.parametrize("M,K,N,bits,gs,nonint,with_bias", LARGE_TILE)
+def test_gemm_large_tile_sampled_rows(gpu, M, K, N, bits, gs, nonint, with_bias):
+    _say(f"gemm large tile M={M} K={K} N={N} bits={bits} gs={gs} nonint-z={nonint} bias={with_bias}")
     d = datagen.small_case(M, K, N, bits, gs, seed=K + bits * 7 + (gs if gs > 0 else 3))
     if nonint:
         d["zeros"] = np.random.default_rng(5).uniform(-1.5, (1 << bits) + 0.5, size=d["zeros"].shape).astype(np.float16)
+    b = np.random.default_rng(7).uniform(-4, 4, size=N).astype(np.float16) if with_bias else None
     g = _to_gpu_case(d)
     qw, qlo = _pack_gpu(gpu, d["codes"], bits)
-    y = gpu.qmm_gemm(g["x"], qw, qlo, g["zeros"], g["scales"], bits, gs)
+    y = gpu.qmm_gemm(g["x"], qw, qlo, g["zeros"], g["scales"], bits, gs, bias=None if b is None else _t(b))
     torch.cuda.synchronize()
     rng = np.random.default_rng(1)
     rows = np.unique(np.concatenate([[0, 1, 255, 256, 4095, 4096, M - 2, M - 1], rng.choice(M, 40, replace=False)]))
     y_rows = y[torch.as_tensor(rows, device=DEV)].cpu().numpy()
     w_ref = oracle.dequantize(d["codes"], d["scales"], d["zeros"], gs)
-    y_ref, a = oracle.matmul(d["x"][rows], w_ref)
+    y_ref, a = oracle.matmul(d["x"][rows], w_ref, b)
     _check(y_rows, y_ref, a, f"gemm large tile bits={bits} gs={gs}")
+
+
+@pytest.mark.parametrize("M", [1, 16, 17, 300])
+def test_functional_form(gpu, M):
+    """quantized_matmul in the functional argument order: M <= 16 to the decode kernel, larger M to
+    the prefill kernel, same function either way."""
+    K, N, bits, gs = 512, 264, 4, 128
+    _say(f"quantized_matmul M={M}")
+    d = datagen.small_case(M, K, N, bits, gs, seed=M)
+    qw_ref, qlo_ref = oracle.pack(d["codes"], bits)
+    qw, qlo = _pack_gpu(gpu, d["codes"], bits)
+    g = _to_gpu_case(d)
+    y = gpu.quantized_matmul(g["x"], qw, g["zeros"], g["scales"], bits, gs, qweight_lo=qlo).cpu().numpy()
+    y_ref, a = oracle.quantized_matmul(d["x"], qw_ref, qlo_ref, d["zeros"], d["scales"], bits, gs)
+    _check(y, y_ref, a, f"quantized_matmul M={M}")
 
 
 def test_workspace_shared_across_shapes(gpu):
