@@ -410,11 +410,13 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
       // (v_fma_mix_f32) instead of a conversion and a subtraction.
       float one = 1.f;
       asm("" : "+v"(one));
+      // With a group scale, (h - cz) * s is one FMA h * s - cz * s (the
+      // product cz * s rounded to fp32, far inside the bf16 result's rounding).
+      const float f = POST_SCALE ? one : sc, c = POST_SCALE ? -cz : -cz * sc;
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         const f16x2 hp = as_f16x2(h[p]);
-        const float lo = __builtin_fmaf((float)hp.x, one, -cz), hi = __builtin_fmaf((float)hp.y, one, -cz);
-        d[p] = POST_SCALE ? pack_bf16(lo, hi) : pack_bf16(lo * sc, hi * sc);
+        d[p] = pack_bf16(__builtin_fmaf((float)hp.x, f, c), __builtin_fmaf((float)hp.y, f, c));
       }
     } else if constexpr (FAST) {
 #pragma unroll
