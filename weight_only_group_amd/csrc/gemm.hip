@@ -212,7 +212,8 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
   constexpr int ACC = TM * TN * 16;  // accumulators per lane
   // Each group's three activation buffers; then, reusing them, the other
   // groups' partial sums.
-  constexpr int kLdsHalves = cmax(KG * 3 * BM * BK, (KG - 1) * GW * ACC * 64 * 2);
+  constexpr int NBUF = 3;  // activation slab buffers per group
+  constexpr int kLdsHalves = cmax(KG * NBUF * BM * BK, (KG - 1) * GW * ACC * 64 * 2);
   __shared__ __attribute__((aligned(16))) f16 lds[kLdsHalves];
   __shared__ float rsum[BM];  // row sums of x, for zero points that are not integers
   constexpr int GT = 64 * GW;  // threads per group
@@ -222,7 +223,6 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
   constexpr int NW = Frag<BITS>::NW, NL = Frag<BITS>::NL;
   constexpr bool POST_SCALE = ZM == 2;
   constexpr int NG = ZM == 0 ? 2 : 1;  // rows of zero points / scales per slab
-  constexpr int NBS = TN * (NW + NL);        // weight loads per wave per 16-k step
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -262,7 +262,7 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
     a_c[q] = (lane & 7) ^ (row & 7) ^ ((row >> 3) & 1);
     a_voff[q] = (uint32_t)min(m0 + row, g.M - 1) * (uint32_t)g.K * 2u + 16u * (uint32_t)a_c[q];
   }
-  f16* const glds = lds + kg * 3 * BM * BK;  // the group's activation buffers
+  f16* const glds = lds + kg * NBUF * BM * BK;  // the group's activation buffers
 
   // B (weights) go straight to registers: each lane reads the words of its
   // fragments. With an even number of tiles per wave, tiles 2p and 2p + 1
@@ -271,6 +271,9 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
   // Columns beyond N are clamped (never stored).
   constexpr bool PAIR = TN % 2 == 0;
   constexpr int NP = PAIR ? TN / 2 : 1;
+  // Weight-load instructions a wave issues per 16-k step (one per pair of
+  // tiles, or per tile, and per plane): the explicit waits below count them.
+  constexpr int NBI = (PAIR ? NP : TN) * (NW + NL);
   auto tile_col = [&](int t) {  // the lane's column of tile t, within the block
     return PAIR ? (BN / WN) * wn + 64 * (t >> 1) + 2 * (lane & 31) + (t & 1) : (BN / WN) * wn + 32 * t + (lane & 31);
   };
@@ -480,15 +483,16 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
   // barrier per slab sits before step 3, whose next-step reads are the first
   // of slab i + 1.
   auto slab = [&](auto fast_tag, int i, BStep (&Bc)[4], BStep (&Bn)[4], ZS& Zc, ZS& Zn) __attribute__((always_inline)) {
-    const int cur = i % 3, nxt = (i + 1) % 3;
+    const int cur = i % NBUF, nxt = (i + 1) % NBUF;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       // Scheduling fence: each step's instructions stay in their step.
       __builtin_amdgcn_sched_barrier(0);
       if (s == 3) {
-        // This wave's loads of slab i + 1, issued two slabs ago, are done:
-        // at least 7 steps' weight loads were issued after them.
-        QMM_WAIT_VMCNT(cmin(7 * NBS, 63));
+        // This wave's loads of slab i + 1, issued NBUF - 1 slabs ago, are
+        // done: at least the weight loads of 4 (NBUF - 2) + 3 steps were
+        // issued after them, and loads complete in order.
+        QMM_WAIT_VMCNT(cmin((4 * (NBUF - 2) + 3) * NBI, 63));
         __syncthreads();  // slab i + 1 is in LDS
       }
 #pragma unroll
@@ -513,7 +517,7 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
         loadB(Bn[0], gslab(i + 3), 0);
       }
       if (!POST_SCALE && s == 3) loadZS(Zc, gslab(i + 2));
-      if (s == 3) dmaA(cur, gslab(i + 3));  // every wave is past its reads of slab i
+      if (s == 3) dmaA(cur, gslab(i + NBUF));  // every wave is past its reads of slab i
       // Interleave: each MFMA is followed by a share of the step's other work.
       constexpr int NM = TM * TN;
 #pragma unroll
@@ -539,13 +543,14 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
   dmaA(0, gslab(0));
   dmaA(1, gslab(1));
   dmaA(2, gslab(2));
+  if constexpr (NBUF > 3) dmaA(3, gslab(3));
 #pragma unroll
   for (int s = 0; s < 4; ++s) loadB(B0[s], gslab(0), s);
   loadZS(Z0, gslab(0));  // with one group per column: the only zero/scale load
 #pragma unroll
   for (int s = 0; s < 4; ++s) loadB(B1[s], gslab(1), s);
   if (!POST_SCALE) loadZS(Z1, gslab(1));
-  QMM_WAIT_VMCNT(cmin(8 * NBS, 63));  // the three slabs' loads, issued first
+  QMM_WAIT_VMCNT(cmin(8 * NBI, 63));  // the first slabs' loads, issued before two slabs' weight loads
   __syncthreads();
 #pragma unroll
   for (int t = 0; t < TM; ++t) fa[0][t] = frag_a(0, 0, t);
