@@ -439,6 +439,97 @@ def check_tolerance_covers_the_rounding_model():
     assert _two_roundings_worst("bf16") > 1.9 * 2.0 ** -8
 
 
+# ---------------------------------------------------------------- GPTQModel-format variants
+# The README counts the values per word (16, 10, 8, 4 for 2, 3, 4, 8 bits) but does not place
+# them. These pins fix the oracle to the reading stated there: value i at bit offset i * bits,
+# lowest first; 3-bit words of 10 values with bits 30-31 zero; weights packed along K, zero
+# points along N. They are pins of that reading, not of a layout the pages print (parity
+# unpinned against the pages).
+
+def _u32(rows):
+    return np.array(rows, dtype=np.uint32).view(np.int32)
+
+
+def check_gptq_qzeros_hand_worked():
+    # 4-bit: nibble i of 0x87654321 is i + 1
+    assert oracle.unpack_qzeros(_u32([[0x87654321]]), 4, 8).tolist() == [[1, 2, 3, 4, 5, 6, 7, 8]]
+    # 8-bit: bytes from the lowest up
+    assert oracle.unpack_qzeros(_u32([[0x04030201, 0xFF800001]]), 8, 8).tolist() == [[1, 2, 3, 4, 1, 0, 128, 255]]
+    # 2-bit: 0xE4 = 0b11_10_01_00 holds 0, 1, 2, 3 from its low bits up
+    assert oracle.unpack_qzeros(_u32([[0xE4E4E4E4]]), 2, 16).tolist() == [[0, 1, 2, 3] * 4]
+    # 3-bit, 10 per word: 1 + 2*8 + 3*64 + 4*512 + 5*4096 + 6*32768 + 7*262144 + 0*2^21 + 1*2^24
+    # + 2*2^27 = 0x111F58D1
+    assert oracle.unpack_qzeros(_u32([[0x111F58D1]]), 3, 10).tolist() == [[1, 2, 3, 4, 5, 6, 7, 0, 1, 2]]
+    # packing writes those words; a ragged row (12 values at 4 bits, 11 at 3 bits) leaves the
+    # rest of its last word zero; one row of words per group
+    z4 = np.array([[1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12]], dtype=np.uint8)
+    assert oracle.pack_qzeros(z4, 4).view(np.uint32).tolist() == [[0x87654321, 0x0000CBA9]]
+    z3 = np.array([[1, 2, 3, 4, 5, 6, 7, 0, 1, 2, 7]], dtype=np.uint8)
+    assert oracle.pack_qzeros(z3, 3).view(np.uint32).tolist() == [[0x111F58D1, 7]]
+    zg = np.array([[1] * 8, [15] * 8], dtype=np.uint8)
+    assert oracle.pack_qzeros(zg, 4).view(np.uint32).tolist() == [[0x11111111], [0xFFFFFFFF]]
+
+
+def check_gptq_3bit10_hand_worked():
+    col = np.array([1, 2, 3, 4, 5, 6, 7, 0, 1, 2, 6, 5], dtype=np.uint8).reshape(12, 1)
+    w = oracle.pack_3bit10(col).view(np.uint32)
+    assert w.shape == (2, 1)
+    assert int(w[0, 0]) == 0x111F58D1
+    assert int(w[1, 0]) == 6 + 5 * 8  # k = 10, 11 open the second word, the rest is zero
+    assert oracle.unpack_3bit10(w.view(np.int32), 12)[:, 0].tolist() == col[:, 0].tolist()
+
+
+def check_gptq_round_trips_and_padding():
+    rng = np.random.default_rng(11)
+    for bits in oracle.GPTQ_BITS:
+        e = oracle.gptq_values_per_word(bits)
+        assert e == {2: 16, 3: 10, 4: 8, 8: 4}[bits]
+        z = rng.integers(0, 1 << bits, size=(3, 37), dtype=np.uint8)
+        w = oracle.pack_qzeros(z, bits)
+        assert w.shape == (3, -(-37 // e))
+        assert np.array_equal(oracle.unpack_qzeros(w, bits, 37), z)
+        # bits past the last value of a word are zero (padding of 3-bit words, ragged last words)
+        used = np.where(np.arange(w.shape[1]) < w.shape[1] - 1, e, 37 - e * (w.shape[1] - 1))
+        for c, nv in enumerate(used):
+            assert not (w.view(np.uint32)[:, c].astype(np.uint64) >> np.uint64(nv * bits)).any(), (bits, c)
+    q = rng.integers(0, 8, size=(73, 6), dtype=np.uint8)
+    w = oracle.pack_3bit10(q)
+    assert w.shape == (8, 6) and not (w.view(np.uint32) >> np.uint32(30)).any()
+    assert not (w.view(np.uint32)[7] >> np.uint32(9)).any()  # 73 = 7 * 10 + 3: three values in the last row
+    assert np.array_equal(oracle.unpack_3bit10(w, 73), q)
+
+
+def check_gptq_product_hand_worked():
+    """The hand-worked products of the golden file, with the weights and the zero points given in
+    the GPTQModel format, give the same exact y."""
+    used = 0
+    for case in _load("dequant_examples.json")["cases"]:
+        bits = case["bits"]
+        zeros = np.array(case["zeros_gn"], dtype=np.float64)
+        if bits not in oracle.GPTQ_BITS or np.any(zeros != np.round(zeros)):
+            continue
+        codes = np.array(case["codes_kn"], dtype=np.uint8)
+        K = codes.shape[0]
+        if bits == 3:
+            qw = oracle.pack_3bit10(codes)
+        elif K % (32 // bits) == 0:
+            qw = oracle.pack_kmajor(codes, bits)
+        else:
+            continue
+        qz = oracle.pack_qzeros(zeros.astype(np.uint8), bits)
+        x = np.array(case["x"], dtype=np.float64)
+        s = np.array(case["scales_gn"], dtype=np.float64)
+        bias = np.array(case["bias_n"], dtype=np.float64) if "bias_n" in case else None
+        for gs in case["group_sizes"]:
+            if gs == -1 and s.shape[0] != 1:
+                continue
+            y, a = oracle.gptqmodel_quantized_matmul(x, qw, qz, s, bits, gs, bias)
+            assert np.array_equal(y, np.array(case["y"])), (case["name"], gs)
+            assert np.array_equal(a, np.array(case["a"])), (case["name"], gs)
+            used += 1
+    assert used >= 5
+
+
 CHECKS = [
     check_pack_words_hand_worked, check_ascending_nibbles, check_word_bijection,
     check_out_of_range_codes_masked, check_three_bit_identity, check_dequant_examples_hand_worked,
@@ -447,6 +538,8 @@ CHECKS = [
     check_rational_brute_force, check_exact_integer_recomputation, check_closed_form_constant_scale_zero,
     check_group_minus_one_is_single_group, check_widths_agree_on_small_codes, check_one_hot_rows,
     check_parity_rule, check_tolerance_covers_the_rounding_model,
+    check_gptq_qzeros_hand_worked, check_gptq_3bit10_hand_worked, check_gptq_round_trips_and_padding,
+    check_gptq_product_hand_worked,
 ]
 
 
@@ -534,6 +627,24 @@ def _mut_bf16_truncates(v):
     return (d.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
 
 
+def _mut_qzeros_slot_reversed(qzeros, bits, N):
+    u = np.asarray(qzeros).view(np.uint32)
+    e = oracle.gptq_values_per_word(bits)
+    z = np.empty((u.shape[0], N), dtype=np.uint8)
+    for n in range(N):
+        z[:, n] = (u[:, n // e] >> np.uint32((e - 1 - n % e) * bits)) & np.uint32((1 << bits) - 1)
+    return z
+
+
+def _mut_3bit10_as_eleven(codes):
+    q = np.asarray(codes).astype(np.uint32)
+    K, N = q.shape
+    words = np.zeros((-(-K // 11), N), dtype=np.uint32)
+    for k in range(K):  # 11 values per word, the last one cut at bit 32
+        words[k // 11] |= (q[k] & np.uint32(7)) << np.uint32(3 * (k % 11))
+    return words.view(np.int32)
+
+
 MUTATIONS = {
     "pack_slot_reversed": ("pack_kmajor", _mut_pack_slot_reversed),
     "unpack_arith_shift": ("unpack_kmajor", _mut_unpack_arith_shift),
@@ -545,6 +656,8 @@ MUTATIONS = {
     "matmul_drops_bias": ("matmul", _mut_matmul_drops_bias),
     "fp16_truncates": ("dequantize_fp16", _mut_fp16_truncates),
     "bf16_truncates": ("f64_to_bf16", _mut_bf16_truncates),
+    "qzeros_slot_reversed": ("unpack_qzeros", _mut_qzeros_slot_reversed),
+    "three_bit_ten_as_eleven": ("pack_3bit10", _mut_3bit10_as_eleven),
 }
 
 
