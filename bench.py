@@ -27,6 +27,9 @@ The JSON line also carries:
                 (128x512x1024, 256x1024x2048, 512x2048x4096; 4-bit g128), cold
   bf16          the decode and prefill products again with bf16 activations,
                 scales, zero points and output (the _bf16 entry points)
+  gptq_convert  the load-time conversions of GPTQModel-format inputs: 3-bit
+                words of 10 codes to the two 3-bit planes (K=2048, N=6144) and
+                packed zero points to (G, N) fp16 (G=64, N=11008), back to back
   floors        reference kernels timed the same way: an empty kernel as a
                 graph node, a plain streaming read of the decode product's
                 byte count (cold), a long streaming read, a dense MFMA loop
@@ -247,6 +250,61 @@ def bench_readme_shapes(w, torch, datagen, steps: int = 200):
     return out
 
 
+def bench_gptq_convert(w, torch, datagen, steps: int = 50):
+    """The load-time conversions of GPTQModel-format inputs, back-to-back launches between events:
+    bytes read and written per launch over the mean launch time. The packed inputs are random
+    32-bit words (every pattern is a valid input; the work does not depend on the values)."""
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+
+    def words(rows, cols):
+        return torch.randint(-2**31, 2**31 - 1, (rows, cols), dtype=torch.int32, device=dev, generator=gen)
+
+    lib = w.library()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(launch):
+        for _ in range(5):
+            launch()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            launch()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / steps
+
+    out = {}
+    K, N = 2048, 6144
+    w10 = words((K + 9) // 10, N)
+    qw = torch.empty((K // 16, N), dtype=torch.int32, device=dev)
+    qlo = torch.empty((K // 32, N), dtype=torch.int32, device=dev)
+
+    def repack():
+        sp = torch.cuda.current_stream().cuda_stream
+        if lib.qmm_repack_3bit10(w10.data_ptr(), K, N, qw.data_ptr(), qlo.data_ptr(), sp) != 0:
+            raise RuntimeError(lib.qmm_last_error().decode())
+
+    us = timed(repack)
+    nbytes = w10.nbytes + qw.nbytes + qlo.nbytes
+    out["repack_3bit10"] = {"K": K, "N": N, "us": round(us, 3), "bytes": nbytes, "GB/s": round(nbytes / us / 1e3, 1)}
+    G, N, bits = 64, 11008, 2
+    qz = words(G, (N + 15) // 16)
+    zeros = torch.empty((G, N), dtype=torch.float16, device=dev)
+
+    def unpack():
+        sp = torch.cuda.current_stream().cuda_stream
+        if lib.qmm_unpack_qzeros(qz.data_ptr(), G, N, bits, zeros.data_ptr(), sp) != 0:
+            raise RuntimeError(lib.qmm_last_error().decode())
+
+    us = timed(unpack)
+    nbytes = qz.nbytes + zeros.nbytes
+    out["unpack_qzeros"] = {"G": G, "N": N, "bits": bits, "us": round(us, 3), "bytes": nbytes,
+                            "GB/s": round(nbytes / us / 1e3, 1)}
+    return out
+
+
 def floors(torch, gemv_bytes: int):
     """Reference kernels from libqmm_probes.so, timed like the products: the dispatch floor of a
     graph node, a plain streaming read of the decode product's byte count (cold, best of a few
@@ -357,6 +415,7 @@ def main():
     ap.add_argument("--no-floors", action="store_true", help="skip the reference kernels (empty launch, "
                     "streaming read, MFMA loop)")
     ap.add_argument("--no-bf16", action="store_true", help="skip the bf16 products")
+    ap.add_argument("--no-gptq", action="store_true", help="skip the GPTQModel-format conversions")
     ap.add_argument("--only", choices=("gemv", "gemm", "gemv_bf16", "gemm_bf16"), default=None,
                     help="run one product only and print its own line (for profiling runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -474,6 +533,8 @@ def run(args, torch, datagen, w):
             gmb = bench_gemm(w, torch, datagen, args.gemm_steps, args.gemm_warmup, bf16=True)
             t = gmb["flops"] / (gmb["mean_launch_ms"] * 1e-3) / 1e12
             out["bf16"]["gemm"] = dict(gemm_line(gmb), pct_of_bf16_dense_peak=round(100 * t / FP16_DENSE_PEAK_TFLOPS, 2))
+    if not args.no_gptq:
+        out["gptq_convert"] = bench_gptq_convert(w, torch, datagen)
     if not args.no_floors:
         out["floors"] = floors(torch, gv["bytes"])
     if not args.no_cpu_baseline:

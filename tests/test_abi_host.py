@@ -32,7 +32,8 @@ def _declared():
 def test_header_declares_the_boundary():
     assert _declared() == sorted(
         ["qmm_abi_version", "qmm_status_string", "qmm_last_error", "qmm_pack", "qmm_unpack", "qmm_dequant",
-         "qmm_workspace_bytes", "qmm_gemv", "qmm_gemm", "qmm_dequant_bf16", "qmm_gemv_bf16", "qmm_gemm_bf16"])
+         "qmm_workspace_bytes", "qmm_gemv", "qmm_gemm", "qmm_dequant_bf16", "qmm_gemv_bf16", "qmm_gemm_bf16",
+         "qmm_unpack_qzeros", "qmm_unpack_qzeros_bf16", "qmm_repack_3bit10"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -49,7 +50,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = _lib()
-    assert lib.qmm_abi_version() == 3
+    assert lib.qmm_abi_version() == 4
     names = [lib.qmm_status_string(i).decode() for i in range(8)]
     assert names == ["QMM_OK", "QMM_ERR_NULL", "QMM_ERR_BITS", "QMM_ERR_SHAPE", "QMM_ERR_GROUP",
                      "QMM_ERR_ALIGN", "QMM_ERR_WORKSPACE", "QMM_ERR_HIP"]
@@ -173,6 +174,30 @@ def test_dequant_rejects_before_launch(host_only, suffix):
     assert dq(A, A, A, A, 256, 64, 4, 128, None, None) == 1
     assert dq(A, A, A, A, 256, 64, 4, 128, A + 1, None) == 5  # w not 2-byte aligned
     assert lib.qmm_last_error().decode() != ""
+
+
+@pytest.mark.parametrize("suffix", SUFFIXES)
+def test_unpack_qzeros_rejects_before_launch(host_only, suffix):
+    f = getattr(host_only, "qmm_unpack_qzeros" + suffix)
+    assert f(A, 4, 64, 1, A, None) == 2       # 1-bit zero points are not a GPTQModel packing
+    assert f(A, 4, 64, 5, A, None) == 2
+    assert f(A, 0, 64, 4, A, None) == 3
+    assert f(A, 4, 0, 4, A, None) == 3
+    assert f(None, 4, 64, 4, A, None) == 1
+    assert f(A, 4, 64, 4, None, None) == 1
+    assert f(A + 2, 4, 64, 4, A, None) == 5   # qzeros not 4-byte aligned
+    assert f(A, 4, 64, 4, A + 1, None) == 5   # zeros not 2-byte aligned
+    assert host_only.qmm_last_error().decode() != ""
+
+
+def test_repack_3bit10_rejects_before_launch(host_only):
+    f = host_only.qmm_repack_3bit10
+    assert f(A, 48, 64, A, A, None) == 3      # K % 32
+    assert f(A, 0, 64, A, A, None) == 3
+    assert f(A, 64, 0, A, A, None) == 3
+    assert f(None, 64, 64, A, A, None) == 1
+    assert f(A, 64, 64, A, None, None) == 1
+    assert f(A, 64, 64, A + 2, A, None) == 5
 
 
 def test_binding_refuses_cpu_tensors():

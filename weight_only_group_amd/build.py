@@ -15,7 +15,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ("api.hip", "pack.hip", "dequant.hip", "gemv.hip", "gemm.hip")
+SOURCES = ("api.hip", "pack.hip", "dequant.hip", "gemv.hip", "gemm.hip", "gptq.hip")
 LIB_NAME = "libqmm.so"
 # Reference kernels for measurement (empty launch, streaming read, MFMA loop);
 # a library of their own, outside the qmm ABI.
