@@ -174,6 +174,22 @@ def test_gemm_mid_m_shapes(gpu, M, N, K):
     _check(y, y_ref, a, "gemm mid-M")
 
 
+# Grids too small for 128 x 128 tiles with K long enough that six K groups of
+# two waves give each group a shorter chain of slabs than four groups of four:
+# every width, group sizes 32 / 64 / 128 / -1, a K tail (2080 = 32.5 slabs),
+# ragged M and N, integer and non-integer zero points.
+SIX_GROUPS = [(64, 4096, 136, 2, 64), (100, 2080, 200, 8, 32), (33, 2048, 520, 1, 128), (300, 4096, 264, 3, -1),
+              (200, 8192, 72, 4, 128)]
+
+
+@pytest.mark.parametrize("nonint", [False, True], ids=["intz", "fracz"])
+@pytest.mark.parametrize("M,K,N,bits,gs", SIX_GROUPS)
+def test_gemm_six_k_groups(gpu, M, K, N, bits, gs, nonint):
+    _say(f"gemm six K groups M={M} K={K} N={N} bits={bits} gs={gs} nonint={nonint}")
+    y, y_ref, a = _run(gpu, "gemm", M, K, N, bits, gs, seed=M + K + N + bits, nonint_zero=nonint)
+    _check(y, y_ref, a, "gemm six K groups")
+
+
 @pytest.mark.parametrize("path", ["gemv", "gemm"])
 @pytest.mark.parametrize("bits", [1, 2, 3, 4, 8])
 def test_non_integer_zero_points(gpu, path, bits):

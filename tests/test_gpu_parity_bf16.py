@@ -105,6 +105,8 @@ SWEEP_GEMM = [
     (1, 256, 64, 4, 128), (17, 512, 264, 4, 64), (300, 256, 520, 4, -1), (257, 320, 264, 4, 32),
     (100, 512, 136, 8, 128), (260, 1024, 264, 8, -1), (64, 96, 8, 8, 32), (270, 256, 264, 2, 32),
     (300, 256, 520, 3, 32), (8, 1024, 40, 3, -1), (70, 512, 264, 1, 64), (260, 288, 520, 1, -1),
+    # six K groups of two waves (small grids, long K), one with a K tail
+    (100, 2080, 200, 8, 32), (300, 4096, 264, 3, -1),
 ]
 
 

@@ -706,13 +706,22 @@ hipError_t launch_tiles(GemmArgs a, hipStream_t s) {
 
 // The largest block tile whose grid still gives every CU a block: 256 x 256
 // (8 waves of 128 x 64), else 128 x 128 (two K groups of 4 waves of 64 x 64),
-// else 64 x 64 (four K groups of 4 waves of 32 x 32). Smaller tiles have
-// short slabs, so their blocks split K to keep more loads in flight.
+// else 64 x 64. Smaller tiles have short slabs, so their blocks split K to
+// keep more loads in flight: a 64 x 64 block's time is about its groups'
+// chain of slabs (run in pairs) times the latency of one, so it takes six
+// K groups of 2 waves of 64 x 32 where that chain is shorter than with four
+// groups of 4 waves of 32 x 32 (K of 2048 and more), else the four groups.
 template <int BITS, bool BF>
 hipError_t launch_bits(const GemmArgs& a, hipStream_t s) {
   auto blocks = [&](int bm, int bn) { return (long long)((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn); };
   if (blocks(256, 256) >= kCUs) return launch_tiles<BITS, 2, 4, 4, 2, 1, BF>(a, s);
   if (blocks(128, 128) >= kCUs) return launch_tiles<BITS, 2, 2, 2, 2, 2, BF>(a, s);
+  const int nk = (a.K + BK - 1) / BK;
+  auto chain = [&](int kg) {
+    const int n = (nk + kg - 1) / kg;
+    return n + (n & 1);
+  };
+  if (chain(6) < chain(4)) return launch_tiles<BITS, 1, 2, 2, 1, 6, BF>(a, s);
   return launch_tiles<BITS, 2, 2, 1, 1, 4, BF>(a, s);
 }
 
