@@ -398,6 +398,24 @@ def test_bias(gpu, path, M, K, N, bits, gs):
     assert np.array_equal(y0.view(np.uint16), np.tile(b, (M, 1)).view(np.uint16))
 
 
+@pytest.mark.parametrize("M,bits,gs", [(1, 4, -1), (16, 2, 32)])
+def test_gemv_max_n(gpu, M, bits, gs):
+    """The decode product at its largest N (2^20 columns: 16384 strips of 64 columns, the
+    most arrival counters any call uses), compared with the oracle on sampled columns: the
+    first and last 64 and 4000 drawn in between."""
+    K, N = 64, 1 << 20
+    _say(f"gemv max N M={M} K={K} N={N} bits={bits} gs={gs}")
+    d = datagen.small_case(M, K, N, bits, gs, seed=M + bits)
+    g = _to_gpu_case(d)
+    qw, qlo = _pack_gpu(gpu, d["codes"], bits)
+    y = gpu.qmm_gemv(g["x"], qw, qlo, g["zeros"], g["scales"], bits, gs).cpu().numpy()
+    rng = np.random.default_rng(M)
+    cols = np.unique(np.concatenate([np.arange(64), np.arange(N - 64, N), rng.integers(0, N, 4000)]))
+    y_ref, a = oracle.quantized_matmul_codes(d["x"], d["codes"][:, cols], d["zeros"][:, cols],
+                                             d["scales"][:, cols], gs)
+    _check(y[:, cols], y_ref, a, "gemv max N")
+
+
 # ------------------------------------------------------------------ the five workloads
 
 @pytest.mark.parametrize("name", [n for n, wl in datagen.WORKLOADS.items() if wl.M <= 16])
