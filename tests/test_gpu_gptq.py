@@ -42,7 +42,7 @@ def _t(a):
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4, 8])
-@pytest.mark.parametrize("G,N", [(1, 8), (3, 37), (4, 200), (32, 4104)])
+@pytest.mark.parametrize("G,N", [(1, 8), (3, 37), (4, 200), (32, 4104), (64, 11008)])
 @pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16], ids=["fp16", "bf16"])
 def test_unpack_qzeros(w, bits, G, N, dtype):
     _say(f"unpack_qzeros bits={bits} G={G} N={N} {dtype}")
@@ -59,7 +59,7 @@ def test_unpack_qzeros(w, bits, G, N, dtype):
     assert np.array_equal(got.float().cpu().numpy(), want)
 
 
-@pytest.mark.parametrize("K,N", [(32, 1), (96, 8), (64, 200), (4096, 136)])
+@pytest.mark.parametrize("K,N", [(32, 1), (96, 8), (64, 200), (4096, 136), (2048, 6144)])
 def test_repack_3bit10(w, K, N):
     _say(f"repack_3bit10 K={K} N={N}")
     codes = datagen.draw_codes(K, N, 3, seed=K + N)
