@@ -205,6 +205,17 @@ def test_binding_refuses_cpu_tensors():
     import weight_only_group_amd as w
     with pytest.raises(ValueError):
         w.qmm_pack(torch.zeros((64, 8), dtype=torch.uint8), 4)
+    # GPTQModel-format calls check their arguments before any conversion
+    x16 = torch.zeros((1, 64), dtype=torch.float16)
+    with pytest.raises(TypeError):
+        w.gptqmodel_quantized_matmul(x16, torch.zeros((8, 8), dtype=torch.int32), torch.zeros((1, 1), dtype=torch.int32),
+                                     None, 4, -1)
+    with pytest.raises(ValueError):
+        w.qmm_unpack_qzeros(torch.zeros((1, 1), dtype=torch.int32), 4, 8)
+    with pytest.raises(ValueError):
+        w.qmm_repack_3bit10(torch.zeros((7, 8), dtype=torch.int32), 64)
+    with pytest.raises(ValueError):
+        w.gptq_values_per_word(5)
     with pytest.raises((ValueError, TypeError)):
         w.qmm_gemv(torch.zeros((1, 64), dtype=torch.float16), torch.zeros((8, 8), dtype=torch.int32), None,
                    torch.zeros((1, 8), dtype=torch.float16), torch.zeros((1, 8), dtype=torch.float16), 4, -1)

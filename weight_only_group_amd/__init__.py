@@ -372,6 +372,9 @@ def gptqmodel_quantized_matmul(x, qweight, qzeros, scales, bits: int, group_size
     dt = _data_dtype(x, "x")
     if x.dim() != 2:
         raise ValueError("x must be (M, K)")
+    _gpu(scales, "scales", dt)
+    if bits not in GPTQ_BITS:
+        raise ValueError(f"the GPTQModel format has no {bits}-bit packing (bits must be one of {GPTQ_BITS})")
     K = x.shape[1]
     N = scales.shape[1]
     zeros = qmm_unpack_qzeros(qzeros, bits, N, dt)
