@@ -152,6 +152,9 @@ SWEEP_GEMM = [
     (33, 512, 96, 2, 64), (270, 256, 264, 2, 32),
     (40, 512, 128, 3, 128), (300, 256, 520, 3, 32), (8, 1024, 40, 3, -1),
     (70, 512, 264, 1, 64), (260, 288, 520, 1, -1),
+    # extremes: the smallest legal product (one 32-row unit, 8 columns), a tall one (65536 rows,
+    # 256 row tiles in one column tile) and a wide one (65536 columns, one row tile)
+    (1, 32, 8, 4, 32), (1, 32, 8, 3, -1), (65536, 64, 8, 4, -1), (16, 32, 65536, 8, 32),
 ]
 
 
