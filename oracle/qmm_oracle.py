@@ -218,12 +218,16 @@ def bf16_to_f64(bits) -> np.ndarray:
 
 
 def f64_to_bf16(v) -> np.ndarray:
-    """float64 -> bf16 bit patterns, rounded once to nearest, ties to even (finite values of the
-    bf16 normal range; larger magnitudes become infinities).
+    """float64 -> bf16 bit patterns, rounded once to nearest, ties to even (finite values;
+    magnitudes past the largest bf16 become infinities).
 
-    bf16 keeps 8 significant bits, so the float64 significand (53 bits) loses its low 45 bits:
-    they are rounded half to even on the integer bit pattern, which carries into the exponent
-    when the significand overflows.
+    bf16 is the upper half of a binary32: 8 exponent bits biased by 127 and 7 stored fraction
+    bits. In its normal range (|v| >= 2^-126) it keeps 8 significant bits, so the float64
+    significand (53 bits) loses its low 45 bits: they are rounded half to even on the integer
+    bit pattern, which carries into the exponent when the significand overflows. Below 2^-126
+    the format has fixed spacing: every value is an integer multiple of 2^-133 (exponent -126,
+    7 fraction bits), and that integer, rounded half to even, is the bit pattern itself (128
+    being the smallest normal, 2^-126).
     """
     d = np.asarray(v, dtype=np.float64)
     u = d.view(np.uint64)
@@ -233,7 +237,13 @@ def f64_to_bf16(v) -> np.ndarray:
     up = (low > half) | ((low == half) & ((q & np.uint64(1)) == np.uint64(1)))
     q = q + up.astype(np.uint64)
     r = (q << np.uint64(45)).view(np.float64)  # exactly representable in bf16 (and binary32)
-    return (r.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    normal = (r.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    # Fixed-spacing range: |v| * 2^133 is exact (a power-of-two scaling), np.rint rounds half to even.
+    mag = np.abs(d)
+    sub = mag < 2.0 ** -126
+    units = np.rint(np.where(sub, mag, 0.0) * 2.0 ** 133).astype(np.uint16)  # 0 .. 128
+    sign = np.where(np.signbit(d), np.uint16(0x8000), np.uint16(0))
+    return np.where(sub, sign | units, normal).astype(np.uint16)
 
 
 def dequantize_bf16(q: np.ndarray, scales_bf16, zeros_bf16, group_size: int) -> np.ndarray:

@@ -180,14 +180,21 @@ def _round_half_even_bits(v: Fraction, frac_bits: int, emin: int) -> Fraction:
 
 
 def check_bf16_encode_against_exact_rounding(seed=12):
-    """f64_to_bf16 equals exact rounding to 7 fraction bits on products of bf16 scales and codes."""
+    """f64_to_bf16 equals exact rounding to 7 fraction bits on products of bf16 scales and codes,
+    and on magnitudes below the bf16 normal range (fixed spacing 2^-133), ties among them."""
     rng = np.random.default_rng(seed)
     s = oracle.f64_to_bf16(rng.uniform(1e-4, 2.0, size=400))
     z = oracle.f64_to_bf16(rng.uniform(-3.0, 260.0, size=400))
     q = rng.integers(0, 256, size=400)
     v = oracle.bf16_to_f64(s) * (q - oracle.bf16_to_f64(z))
+    # below 2^-126: random magnitudes in [2^-140, 2^-126), either sign, plus exact ties
+    # (odd multiples of 2^-134, halfway between two representable values)
+    tiny = np.ldexp(rng.uniform(1.0, 2.0, size=300), rng.integers(-140, -126, size=300))
+    tiny *= np.where(rng.integers(0, 2, size=300) == 1, -1.0, 1.0)
+    ties = np.ldexp(2.0 * rng.integers(0, 128, size=100) + 1.0, -134)
+    v = np.concatenate([v, tiny, ties, -ties])
     got = oracle.bf16_to_f64(oracle.f64_to_bf16(v))
-    for i in range(400):
+    for i in range(v.size):
         want = _round_half_even_bits(Fraction(float(v[i])), 7, -126)
         assert got[i] == float(want), (i, v[i], got[i], float(want))
 
@@ -627,6 +634,18 @@ def _mut_bf16_truncates(v):
     return (d.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
 
 
+def _mut_bf16_subnormal_truncates(v):
+    # correct in the normal range, truncating below 2^-126
+    d = np.asarray(v, dtype=np.float64)
+    u = d.view(np.uint64)
+    low = u & np.uint64((1 << 45) - 1)
+    q = u >> np.uint64(45)
+    half = np.uint64(1 << 44)
+    q = q + ((low > half) | ((low == half) & ((q & np.uint64(1)) == np.uint64(1)))).astype(np.uint64)
+    r = (q << np.uint64(45)).view(np.float64)
+    return (r.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
 def _mut_qzeros_slot_reversed(qzeros, bits, N):
     u = np.asarray(qzeros).view(np.uint32)
     e = oracle.gptq_values_per_word(bits)
@@ -656,6 +675,7 @@ MUTATIONS = {
     "matmul_drops_bias": ("matmul", _mut_matmul_drops_bias),
     "fp16_truncates": ("dequantize_fp16", _mut_fp16_truncates),
     "bf16_truncates": ("f64_to_bf16", _mut_bf16_truncates),
+    "bf16_subnormal_truncates": ("f64_to_bf16", _mut_bf16_subnormal_truncates),
     "qzeros_slot_reversed": ("unpack_qzeros", _mut_qzeros_slot_reversed),
     "three_bit_ten_as_eleven": ("pack_3bit10", _mut_3bit10_as_eleven),
 }
