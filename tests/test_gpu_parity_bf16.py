@@ -191,13 +191,19 @@ def test_bf16_bias(gpu, path, M, K, N, bits, gs):
 
 @pytest.mark.parametrize("bits,K,N,gs", [(1, 256, 72, 32), (2, 512, 136, 64), (3, 256, 200, -1),
                                          (4, 1024, 264, 128), (8, 512, 520, 32)])
-@pytest.mark.parametrize("zkind", ["integer", "fractional"])
+@pytest.mark.parametrize("zkind", ["integer", "fractional", "subnormal_scale"])
 def test_dequant_bf16_bit_exact(gpu, bits, K, N, gs, zkind):
     _say(f"dequant bf16 bits={bits} K={K} N={N} gs={gs} zeros={zkind}")
     b = _case(1, K, N, bits, gs, seed=K + N + bits)
-    if zkind == "fractional":
+    if zkind in ("fractional", "subnormal_scale"):
         rng = np.random.default_rng(bits)
         b["zeros"] = datagen.round_to_bf16(rng.uniform(-1.5, (1 << bits) + 0.5, size=b["zeros"].shape))
+    if zkind == "subnormal_scale":
+        # scales around 2^-136 .. 2^-128 (bf16 subnormals and the lowest normals): the products
+        # s * (q - z) fall below 2^-126, where bf16 has the fixed spacing 2^-133
+        rng = np.random.default_rng(100 + bits)
+        mag = np.ldexp(rng.uniform(1.0, 2.0, size=b["scales"].shape), rng.integers(-136, -128, size=b["scales"].shape))
+        b["scales"] = datagen.round_to_bf16(mag.astype(np.float32))
     want = oracle.dequantize_bf16(b["codes"], b["scales"], b["zeros"], gs)
     qw, qlo, z, s, _ = _device(gpu, b, bits)
     w = gpu.qmm_dequant(qw, qlo, z, s, K, bits, gs)

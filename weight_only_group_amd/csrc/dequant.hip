@@ -36,8 +36,16 @@ __device__ __forceinline__ uint32_t code_at(const uint32_t (&wd)[words_per_chunk
   }
 }
 
-// fp64 -> bf16 bits, rounded once to nearest even (finite values).
+// fp64 -> bf16 bits, rounded once to nearest even (finite values). Below
+// 2^-126 bf16 has fixed spacing 2^-133 and the bit pattern is the number of
+// those units, rounded to nearest even, here in fp64 so that the result does
+// not depend on how binary32 denormals are treated.
 __device__ __forceinline__ uint16_t f64_to_bf16_bits(double d) {
+  const double mag = __builtin_fabs(d);
+  if (mag < 0x1p-126) {
+    const uint32_t units = (uint32_t)__builtin_rint(mag * 0x1p133);  // 0 .. 128, exact scaling
+    return (uint16_t)(units | (__builtin_signbit(d) ? 0x8000u : 0u));
+  }
   const float f = (float)d;  // nearest binary32
   uint32_t u = __builtin_bit_cast(uint32_t, f);
   const double back = (double)f;
