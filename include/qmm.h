@@ -170,6 +170,29 @@ qmm_status qmm_gemv_bf16(const uint16_t* x, int M, int K,
                          hipStream_t stream);
 
 /*
+ * qmm_gemv_noalloc -- qmm_gemv without a workspace argument, for callers that
+ * cannot allocate device memory (code under graph capture, tight serving
+ * loops, harnesses that forbid allocation). It computes exactly what qmm_gemv
+ * computes, with the same kernels and the same bits; where the plan needs
+ * scratch memory (arrival counters and split-K partial sums), it uses a fixed
+ * 4 MiB device array held by the library, one per GPU, for the life of the
+ * process. The call itself allocates nothing.
+ *   Arguments and requirements as for qmm_gemv, minus the workspace.
+ *   Shapes needing more than 4 MiB of scratch (qmm_workspace_bytes() > 4 MiB:
+ *   narrow N with a deep K split at large M) are refused with
+ *   QMM_ERR_WORKSPACE; qmm_gemv with a workspace takes them.
+ * All calls on one GPU share that GPU's array: calls that overlap in time on
+ * one GPU (on different streams, or from several threads) race on it and
+ * must be serialised by the caller. The arrival counters start at zero when
+ * the library's code object is loaded and every call leaves them at zero.
+ */
+qmm_status qmm_gemv_noalloc(const uint16_t* x, int M, int K,
+                            const int32_t* qweight, const int32_t* qweight_lo,
+                            const uint16_t* zeros, const uint16_t* scales, const uint16_t* bias,
+                            int N, int bits, int group_size,
+                            uint16_t* y, hipStream_t stream);
+
+/*
  * qmm_gemm -- the same product for any M >= 1, the prefill product: packed
  * tiles are dequantized to fp16 in LDS and multiplied on the matrix cores
  * with fp32 accumulation. dashq_kernel.py, TritonQuantLinear.forward (batched

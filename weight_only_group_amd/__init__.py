@@ -11,6 +11,8 @@ Functions mirror the C ABI (include/qmm.h):
 * ``qmm_unpack(qweight, qweight_lo, K, bits)`` -> codes
 * ``qmm_dequant(qweight, qweight_lo, zeros, scales, K, bits, group_size)`` -> (K, N)
 * ``qmm_gemv(x, qweight, qweight_lo, zeros, scales, bits, group_size, bias=None)`` (1 <= M <= 16)
+* ``qmm_gemv_noalloc(x, qweight, qweight_lo, zeros, scales, bits, group_size, out, bias=None)``:
+  the decode product with no workspace (the library's fixed device scratch)
 * ``qmm_gemm(x, qweight, qweight_lo, zeros, scales, bits, group_size, bias=None)`` (any M)
 * ``quantized_matmul(x, qweight, qzeros, scales, bits, group_size, qweight_lo=None, bias=None)``:
   the functional form, M <= 16 to the GEMV, larger M to the GEMM.
@@ -42,7 +44,7 @@ STATUS_NAMES = {
 EXPORTS = (
     "qmm_abi_version", "qmm_status_string", "qmm_last_error", "qmm_pack", "qmm_unpack", "qmm_dequant",
     "qmm_workspace_bytes", "qmm_gemv", "qmm_gemm", "qmm_dequant_bf16", "qmm_gemv_bf16", "qmm_gemm_bf16",
-    "qmm_unpack_qzeros", "qmm_unpack_qzeros_bf16", "qmm_repack_3bit10",
+    "qmm_unpack_qzeros", "qmm_unpack_qzeros_bf16", "qmm_repack_3bit10", "qmm_gemv_noalloc",
 )
 ABI_VERSION = 4
 DTYPES = (torch.float16, torch.bfloat16)
@@ -84,6 +86,8 @@ def _declare(lib):
         f.restype, f.argtypes = I, [P, I, I, I, P, P]
     lib.qmm_repack_3bit10.restype = I
     lib.qmm_repack_3bit10.argtypes = [P, I, I, P, P, P]
+    lib.qmm_gemv_noalloc.restype = I
+    lib.qmm_gemv_noalloc.argtypes = [P, I, I, P, P, P, P, P, I, I, I, P, P]
     if lib.qmm_abi_version() != ABI_VERSION:
         raise RuntimeError(f"libqmm ABI version {lib.qmm_abi_version()} does not match the binding's {ABI_VERSION}")
     return lib
@@ -285,6 +289,23 @@ def qmm_gemv(x, qweight, qweight_lo, zeros, scales, bits: int, group_size: int, 
                                   _ptr(bias), N, bits, group_size, _ptr(y), _ptr(ws), 0 if ws is None else ws.numel(),
                                   _stream(dev)),
                "qmm_gemv")
+    return y
+
+
+def qmm_gemv_noalloc(x, qweight, qweight_lo, zeros, scales, bits: int, group_size: int, out, bias=None):
+    """qmm_gemv into a caller-given ``out`` (M, N) without any workspace: the library's own fixed
+    device scratch serves the split-K plans (float16 data; shapes needing more than its 4 MiB are
+    refused). Calls that overlap in time on one GPU must not use it concurrently."""
+    M, K, N, dt = _check_product_args(x, qweight, qweight_lo, zeros, scales, bits)
+    if dt != torch.float16:
+        raise TypeError("qmm_gemv_noalloc takes float16 data")
+    _check_bias(bias, N, dt)
+    dev = x.device
+    y = _output(out, M, N, dt, dev)
+    with torch.cuda.device(dev):
+        _check(library().qmm_gemv_noalloc(_ptr(x), M, K, _ptr(qweight), _ptr(qweight_lo), _ptr(zeros), _ptr(scales),
+                                          _ptr(bias), N, bits, group_size, _ptr(y), _stream(dev)),
+               "qmm_gemv_noalloc")
     return y
 
 

@@ -4,6 +4,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "../../include/qmm.h"
 #include "common.h"
 #include "gptq.h"
@@ -121,6 +123,63 @@ qmm_status gemv_impl(const uint16_t* x, int M, int K, const int32_t* qweight, co
                   "qmm_gemv launch");
 }
 
+// ---- the decode product without a caller workspace ----------------------------
+// Device memory of a fixed size in the library's own code object, for callers
+// that cannot allocate. It holds what a workspace holds: the arrival counters
+// (zero when the code object is loaded, as every static device variable, and
+// left at zero by each call) and the split-K partial sums. Every GPU has its
+// own copy; in host code the array's name is only a stand-in for it, so its
+// device address is looked up once per device and used everywhere instead.
+constexpr size_t kScratchBytes = size_t(4) << 20;  // 4 MiB per device
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of the current device's scratch, looked up on the first
+// call on that device (with that device current).
+qmm_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(QMM_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(QMM_ERR_HIP, "device %d beyond the %d the library tracks", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(QMM_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return QMM_OK;
+}
+
+qmm_status gemv_noalloc_impl(const uint16_t* x, int M, int K, const int32_t* qweight, const int32_t* qweight_lo,
+                             const uint16_t* zeros, const uint16_t* scales, const uint16_t* bias, int N, int bits,
+                             int group_size, uint16_t* y, hipStream_t stream) {
+  qmm_status st = check_product(x, M, K, qweight, qweight_lo, zeros, scales, bias, N, bits, group_size, y, 16);
+  if (st != QMM_OK) return st;
+  if (N > qmm::kGemvMaxN) return fail(QMM_ERR_SHAPE, "N=%d exceeds the decode product's limit of %d", N, qmm::kGemvMaxN);
+  const qmm::GemvPlan plan = qmm::gemv_plan(M, K, N, bits, group_size);
+  if (!plan.valid)
+    return fail(QMM_ERR_SHAPE, "M=%d, K=%d, group_size=%d exceed the decode product's staging limits; use qmm_gemm",
+                M, K, group_size);
+  if (plan.workspace_bytes > kScratchBytes)
+    return fail(QMM_ERR_WORKSPACE, "this shape needs %zu bytes of scratch, more than the %zu the library holds; "
+                "use qmm_gemv with a workspace", plan.workspace_bytes, kScratchBytes);
+  void* ws = nullptr;
+  if (plan.workspace_bytes > 0) {
+    st = scratch_for_current_device(&ws);
+    if (st != QMM_OK) return st;
+  }
+  return from_hip(qmm::launch_gemv(plan, x, M, K, reinterpret_cast<const uint32_t*>(qweight),
+                                   reinterpret_cast<const uint32_t*>(qweight_lo), zeros, scales, bias, N, bits,
+                                   group_size, y, ws, false, stream),
+                  "qmm_gemv_noalloc launch");
+}
+
 qmm_status unpack_qzeros_impl(const int32_t* qzeros, int G, int N, int bits, uint16_t* zeros, bool bf16,
                               hipStream_t stream) {
   if (bits != 2 && bits != 3 && bits != 4 && bits != 8)
@@ -218,6 +277,12 @@ qmm_status qmm_gemv_bf16(const uint16_t* x, int M, int K, const int32_t* qweight
                          int group_size, uint16_t* y, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return gemv_impl(x, M, K, qweight, qweight_lo, zeros, scales, bias, N, bits, group_size, y, workspace,
                    workspace_bytes, true, stream);
+}
+
+qmm_status qmm_gemv_noalloc(const uint16_t* x, int M, int K, const int32_t* qweight, const int32_t* qweight_lo,
+                            const uint16_t* zeros, const uint16_t* scales, const uint16_t* bias, int N, int bits,
+                            int group_size, uint16_t* y, hipStream_t stream) {
+  return gemv_noalloc_impl(x, M, K, qweight, qweight_lo, zeros, scales, bias, N, bits, group_size, y, stream);
 }
 
 qmm_status qmm_gemm(const uint16_t* x, int M, int K, const int32_t* qweight, const int32_t* qweight_lo,
