@@ -132,6 +132,39 @@ qmm_status qmm_dequant_bf16(const int32_t* qweight, const int32_t* qweight_lo,
 size_t qmm_workspace_bytes(int M, int K, int N, int bits, int group_size);
 
 /*
+ * qmm_gemv_plan_info -- the launch plan qmm_gemv (and qmm_gemv_bf16,
+ * qmm_gemv_noalloc) uses for this problem on the current device, for tests
+ * and measurement. Host only: no work is enqueued. Writes min(n, 9) ints:
+ *   info[0] kernel: 0 = blocks split along K (partial sums through the
+ *           workspace when info[4] > 1), 1 = one block per column strip, each
+ *           wave over its own K range
+ *   info[1] adjacent columns per lane (1, 2 or 4); a wave covers 16 * info[1]
+ *   info[2] waves per block
+ *   info[3] blocks along N (column strips)
+ *   info[4] blocks along K
+ *   info[5] 32-row units of K per wave (kernel 1) or per block (kernel 0)
+ *   info[6] groups per wave (kernel 1), else 0
+ *   info[7] XCDs the strips are laid out for
+ *   info[8] compute units of the device
+ * Returns QMM_ERR_NULL for a NULL info with n > 0, QMM_ERR_SHAPE (etc.) for
+ * arguments qmm_gemv would reject on shape alone, else QMM_OK.
+ */
+qmm_status qmm_gemv_plan_info(int M, int K, int N, int bits, int group_size, int32_t* info, int n);
+
+/*
+ * qmm_gemm_plan_info -- the block tiling qmm_gemm (and qmm_gemm_bf16) uses
+ * for this problem on the current device, for tests and measurement. Host
+ * only: no work is enqueued. Writes min(n, 7) ints:
+ *   info[0] block tile rows     info[1] block tile columns
+ *   info[2] groups of waves splitting a block's K range
+ *   info[3] waves per block     info[4] blocks (capped at 2^31 - 1)
+ *   info[5] XCDs the tiles are laid out for   info[6] compute units
+ * Returns QMM_ERR_NULL for a NULL info with n > 0, QMM_ERR_SHAPE (etc.) for
+ * arguments qmm_gemm would reject on shape alone, else QMM_OK.
+ */
+qmm_status qmm_gemm_plan_info(int M, int K, int N, int bits, int group_size, int32_t* info, int n);
+
+/*
  * qmm_gemv -- y = x @ dequantize(W) for small M (1 <= M <= 16), the decode
  * product. dashq_kernel.py, _dashq_gemv_kernel and TritonQuantLinear.forward
  * (single-token path); GPTQModel-Compatible Triton Kernel README, "API

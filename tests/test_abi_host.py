@@ -33,7 +33,8 @@ def test_header_declares_the_boundary():
     assert _declared() == sorted(
         ["qmm_abi_version", "qmm_status_string", "qmm_last_error", "qmm_pack", "qmm_unpack", "qmm_dequant",
          "qmm_workspace_bytes", "qmm_gemv", "qmm_gemm", "qmm_dequant_bf16", "qmm_gemv_bf16", "qmm_gemm_bf16",
-         "qmm_unpack_qzeros", "qmm_unpack_qzeros_bf16", "qmm_repack_3bit10", "qmm_gemv_noalloc"])
+         "qmm_unpack_qzeros", "qmm_unpack_qzeros_bf16", "qmm_repack_3bit10", "qmm_gemv_noalloc",
+         "qmm_gemv_plan_info", "qmm_gemm_plan_info"])
 
 
 def test_library_exports_every_declared_symbol():

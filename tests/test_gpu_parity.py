@@ -403,9 +403,9 @@ def test_bias(gpu, path, M, K, N, bits, gs):
 
 @pytest.mark.parametrize("M,bits,gs", [(1, 4, -1), (16, 2, 32)])
 def test_gemv_max_n(gpu, M, bits, gs):
-    """The decode product at its largest N (2^20 columns: 16384 strips of 64 columns, the
-    most arrival counters any call uses), compared with the oracle on sampled columns: the
-    first and last 64 and 4000 drawn in between."""
+    """The decode product at its largest N (2^20 columns: the largest grid, 16384 strips of
+    64 columns; K = 64 is too short to split, so no workspace is used), compared with the
+    oracle on sampled columns: the first and last 64 and 4000 drawn in between."""
     K, N = 64, 1 << 20
     _say(f"gemv max N M={M} K={K} N={N} bits={bits} gs={gs}")
     d = datagen.small_case(M, K, N, bits, gs, seed=M + bits)
@@ -434,25 +434,6 @@ def test_workload_gemv_full(gpu, name):
     # the prefill kernel computes the same function
     y2 = gpu.qmm_gemm(g["x"], qw, qlo, g["zeros"], g["scales"], wl.bits, wl.group_size).cpu().numpy()
     _check(y2, y_ref, a, name + " via gemm")
-
-
-def test_workload_prefill_sampled_rows(gpu):
-    """The prefill product at full size, launched exactly as the benchmark launches it;
-    sampled rows (and every column) are compared with the oracle."""
-    wl = datagen.WORKLOADS["gemm_m2048_k4096_n14336_int8_gchan"]
-    _say(f"workload {wl.name} (sampled rows)")
-    d = datagen.generate(wl)
-    g = _to_gpu_case(d)
-    qw, qlo = _pack_gpu(gpu, d["codes"], wl.bits)
-    y = gpu.qmm_gemm(g["x"], qw, qlo, g["zeros"], g["scales"], wl.bits, wl.group_size)
-    torch.cuda.synchronize()
-    assert bool(torch.isfinite(y).all())
-    rng = np.random.default_rng(0)
-    rows = np.unique(np.concatenate([[0, 1, 255, 256, 1023, 2047], rng.choice(wl.M, 58, replace=False)]))
-    y_rows = y[torch.as_tensor(rows, device=DEV)].cpu().numpy()
-    w_ref = oracle.dequantize(d["codes"], d["scales"], d["zeros"], wl.group_size)
-    y_ref, a = oracle.matmul(d["x"][rows], w_ref)
-    _check(y_rows, y_ref, a, f"{wl.name} rows={len(rows)}")
 
 
 # Products wide enough for the 256 x 256 block tile, with partial tiles at the

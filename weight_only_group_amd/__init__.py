@@ -45,6 +45,7 @@ EXPORTS = (
     "qmm_abi_version", "qmm_status_string", "qmm_last_error", "qmm_pack", "qmm_unpack", "qmm_dequant",
     "qmm_workspace_bytes", "qmm_gemv", "qmm_gemm", "qmm_dequant_bf16", "qmm_gemv_bf16", "qmm_gemm_bf16",
     "qmm_unpack_qzeros", "qmm_unpack_qzeros_bf16", "qmm_repack_3bit10", "qmm_gemv_noalloc",
+    "qmm_gemv_plan_info", "qmm_gemm_plan_info",
 )
 ABI_VERSION = 4
 DTYPES = (torch.float16, torch.bfloat16)
@@ -88,6 +89,10 @@ def _declare(lib):
     lib.qmm_repack_3bit10.argtypes = [P, I, I, P, P, P]
     lib.qmm_gemv_noalloc.restype = I
     lib.qmm_gemv_noalloc.argtypes = [P, I, I, P, P, P, P, P, I, I, I, P, P]
+    lib.qmm_gemv_plan_info.restype = I
+    lib.qmm_gemv_plan_info.argtypes = [I, I, I, I, I, P, I]
+    lib.qmm_gemm_plan_info.restype = I
+    lib.qmm_gemm_plan_info.argtypes = [I, I, I, I, I, P, I]
     if lib.qmm_abi_version() != ABI_VERSION:
         raise RuntimeError(f"libqmm ABI version {lib.qmm_abi_version()} does not match the binding's {ABI_VERSION}")
     return lib
@@ -217,6 +222,28 @@ def qmm_dequant(qweight, qweight_lo, zeros, scales, K: int, bits: int, group_siz
 
 def workspace_bytes(M: int, K: int, N: int, bits: int, group_size: int) -> int:
     return int(library().qmm_workspace_bytes(M, K, N, bits, group_size))
+
+
+GEMV_PLAN_FIELDS = ("kernel", "vec", "waves", "strips", "ksplit", "units", "groups_per_wave", "xcds", "cus")
+
+
+def gemv_plan_info(M: int, K: int, N: int, bits: int, group_size: int) -> dict:
+    """The launch plan qmm_gemv takes for this shape on the current device (host only)."""
+    info = (ctypes.c_int32 * len(GEMV_PLAN_FIELDS))()
+    _check(library().qmm_gemv_plan_info(M, K, N, bits, group_size, ctypes.addressof(info), len(info)),
+           "qmm_gemv_plan_info")
+    return dict(zip(GEMV_PLAN_FIELDS, list(info)))
+
+
+GEMM_PLAN_FIELDS = ("bm", "bn", "kgroups", "waves", "blocks", "xcds", "cus")
+
+
+def gemm_plan_info(M: int, K: int, N: int, bits: int, group_size: int) -> dict:
+    """The block tiling qmm_gemm takes for this shape on the current device (host only)."""
+    info = (ctypes.c_int32 * len(GEMM_PLAN_FIELDS))()
+    _check(library().qmm_gemm_plan_info(M, K, N, bits, group_size, ctypes.addressof(info), len(info)),
+           "qmm_gemm_plan_info")
+    return dict(zip(GEMM_PLAN_FIELDS, list(info)))
 
 
 # Zero-filled GEMV workspaces, one per (device, stream); the kernels leave their

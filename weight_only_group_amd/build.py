@@ -15,7 +15,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ("api.hip", "pack.hip", "dequant.hip", "gemv.hip", "gemm.hip", "gptq.hip")
+SOURCES = ("api.hip", "pack.hip", "dequant.hip", "gemv.hip", "gemv_wave_b1.hip", "gemv_wave_b2.hip",
+           "gemv_wave_b3.hip", "gemv_wave_b4.hip", "gemv_wave_b8.hip", "gemm.hip", "gptq.hip")
 LIB_NAME = "libqmm.so"
 # Reference kernels for measurement (empty launch, streaming read, MFMA loop);
 # a library of their own, outside the qmm ABI.
@@ -73,7 +74,7 @@ def _compile_and_link(sources, out: str, defines, verbose: bool, jobs: int) -> s
     return out
 
 
-def build(out: str | None = None, defines=(), verbose: bool = False, jobs: int = 4) -> str:
+def build(out: str | None = None, defines=(), verbose: bool = False, jobs: int = 8) -> str:
     """Compile every source and link libqmm.so (and, for the default build, the
     measurement probes library); returns the path of libqmm.so."""
     default = out is None and not defines

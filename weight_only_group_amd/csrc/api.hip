@@ -10,6 +10,33 @@
 #include "common.h"
 #include "gptq.h"
 
+namespace qmm {
+
+// Read once per device: the plans size their grids by the CU count and lay
+// out strips by the XCD count. Without a device (host-only use of
+// qmm_workspace_bytes) the MI355X values are taken.
+DeviceTopo device_topology() {
+  constexpr int kMaxDev = 64;
+  static std::mutex mu;
+  static DeviceTopo cache[kMaxDev] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) {
+    (void)hipGetLastError();
+    return DeviceTopo{256, 8};
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache[dev].cus == 0) {
+    int cus = 0, xcds = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    if (hipDeviceGetAttribute(&xcds, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || xcds <= 0) xcds = 8;
+    (void)hipGetLastError();
+    cache[dev] = DeviceTopo{cus, xcds};
+  }
+  return cache[dev];
+}
+
+}  // namespace qmm
+
 namespace {
 
 thread_local char g_last_error[512] = "";
@@ -107,7 +134,7 @@ qmm_status gemv_impl(const uint16_t* x, int M, int K, const int32_t* qweight, co
   qmm_status st = check_product(x, M, K, qweight, qweight_lo, zeros, scales, bias, N, bits, group_size, y, 16);
   if (st != QMM_OK) return st;
   if (N > qmm::kGemvMaxN) return fail(QMM_ERR_SHAPE, "N=%d exceeds the decode product's limit of %d", N, qmm::kGemvMaxN);
-  const qmm::GemvPlan plan = qmm::gemv_plan(M, K, N, bits, group_size);
+  const qmm::GemvPlan plan = qmm::gemv_plan(M, K, N, bits, group_size, qmm::device_topology());
   if (!plan.valid)
     return fail(QMM_ERR_SHAPE, "M=%d, K=%d, group_size=%d exceed the decode product's staging limits; use qmm_gemm",
                 M, K, group_size);
@@ -162,7 +189,7 @@ qmm_status gemv_noalloc_impl(const uint16_t* x, int M, int K, const int32_t* qwe
   qmm_status st = check_product(x, M, K, qweight, qweight_lo, zeros, scales, bias, N, bits, group_size, y, 16);
   if (st != QMM_OK) return st;
   if (N > qmm::kGemvMaxN) return fail(QMM_ERR_SHAPE, "N=%d exceeds the decode product's limit of %d", N, qmm::kGemvMaxN);
-  const qmm::GemvPlan plan = qmm::gemv_plan(M, K, N, bits, group_size);
+  const qmm::GemvPlan plan = qmm::gemv_plan(M, K, N, bits, group_size, qmm::device_topology());
   if (!plan.valid)
     return fail(QMM_ERR_SHAPE, "M=%d, K=%d, group_size=%d exceed the decode product's staging limits; use qmm_gemm",
                 M, K, group_size);
@@ -201,7 +228,7 @@ qmm_status gemm_impl(const uint16_t* x, int M, int K, const int32_t* qweight, co
   if (st != QMM_OK) return st;
   return from_hip(qmm::launch_gemm(x, M, K, reinterpret_cast<const uint32_t*>(qweight),
                                    reinterpret_cast<const uint32_t*>(qweight_lo), zeros, scales, bias, N, bits,
-                                   group_size, y, bf16, stream),
+                                   group_size, y, bf16, qmm::device_topology(), stream),
                   "qmm_gemm launch");
 }
 
@@ -250,7 +277,42 @@ qmm_status qmm_unpack(const int32_t* qweight, const int32_t* qweight_lo, int K, 
 size_t qmm_workspace_bytes(int M, int K, int N, int bits, int group_size) {
   if (!bits_ok(bits) || M < 1 || M > 16 || K < 32 || K % 32 || N < 8 || N % 8 || N > qmm::kGemvMaxN) return 0;
   if (group_size != -1 && (group_size <= 0 || group_size % 32 || K % group_size)) return 0;
-  return qmm::gemv_plan(M, K, N, bits, group_size).workspace_bytes;
+  return qmm::gemv_plan(M, K, N, bits, group_size, qmm::device_topology()).workspace_bytes;
+}
+
+qmm_status qmm_gemv_plan_info(int M, int K, int N, int bits, int group_size, int32_t* info, int n) {
+  if (!bits_ok(bits)) return fail(QMM_ERR_BITS, "bits=%d is not one of 1, 2, 3, 4, 8", bits);
+  if (M < 1 || M > 16) return fail(QMM_ERR_SHAPE, "M=%d must be in [1, 16]", M);
+  if (K < 32 || K % 32) return fail(QMM_ERR_SHAPE, "K=%d must be a positive multiple of 32", K);
+  if (N < 8 || N % 8 || N > qmm::kGemvMaxN)
+    return fail(QMM_ERR_SHAPE, "N=%d must be a positive multiple of 8, at most %d", N, qmm::kGemvMaxN);
+  const qmm_status gs = check_group(K, group_size);
+  if (gs != QMM_OK) return gs;
+  if (n > 0 && !info) return fail(QMM_ERR_NULL, "info is NULL");
+  const qmm::DeviceTopo topo = qmm::device_topology();
+  const qmm::GemvPlan p = qmm::gemv_plan(M, K, N, bits, group_size, topo);
+  if (!p.valid)
+    return fail(QMM_ERR_SHAPE, "M=%d, K=%d, group_size=%d exceed the decode product's staging limits", M, K,
+                group_size);
+  const int32_t v[9] = {p.kind, p.vec, p.waves, p.nstrips, p.ksplit,
+                        p.kind == 1 ? p.upw : p.units_per_block, p.kind == 1 ? p.gpw : 0, p.xcds, topo.cus};
+  for (int i = 0; i < n && i < 9; ++i) info[i] = v[i];
+  return ok();
+}
+
+qmm_status qmm_gemm_plan_info(int M, int K, int N, int bits, int group_size, int32_t* info, int n) {
+  if (!bits_ok(bits)) return fail(QMM_ERR_BITS, "bits=%d is not one of 1, 2, 3, 4, 8", bits);
+  if (M < 1) return fail(QMM_ERR_SHAPE, "M=%d must be >= 1", M);
+  if (K < 32 || K % 32) return fail(QMM_ERR_SHAPE, "K=%d must be a positive multiple of 32", K);
+  if (N < 8 || N % 8) return fail(QMM_ERR_SHAPE, "N=%d must be a positive multiple of 8", N);
+  const qmm_status gs = check_group(K, group_size);
+  if (gs != QMM_OK) return gs;
+  if (n > 0 && !info) return fail(QMM_ERR_NULL, "info is NULL");
+  const qmm::GemmPlan p = qmm::gemm_plan(M, K, N, qmm::device_topology());
+  const int32_t v[7] = {p.bm, p.bn, p.kgroups, p.waves, (int32_t)(p.blocks < INT32_MAX ? p.blocks : INT32_MAX),
+                        p.xcds, p.cus};
+  for (int i = 0; i < n && i < 7; ++i) info[i] = v[i];
+  return ok();
 }
 
 qmm_status qmm_dequant(const int32_t* qweight, const int32_t* qweight_lo, const uint16_t* zeros,

@@ -52,6 +52,15 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 // Rows of the weight per group: group_size, or K for group_size == -1.
 inline int group_rows(int K, int group_size) { return group_size == -1 ? K : group_size; }
 
+// ---- device topology ----------------------------------------------------------
+// Compute units and XCDs (each XCD with its own L2) of the current device, read
+// once per device; the MI355X values (256, 8) when no device can be queried.
+struct DeviceTopo {
+  int cus;
+  int xcds;
+};
+DeviceTopo device_topology();
+
 // ---- decode GEMV (small M) ----------------------------------------------
 // The workspace header has one arrival counter per column strip. Strips are
 // 32 or 64 columns wide whenever there are more than 256 of them, so this
@@ -59,6 +68,7 @@ inline int group_rows(int K, int group_size) { return group_size == -1 ? K : gro
 constexpr int kGemvMaxN = 1 << 20;
 constexpr int kGemvMaxStrips = kGemvMaxN / 32;
 struct GemvPlan {
+  int kind;         // 0: blocks split K, waves sum through LDS, split-K hand-off; 1: wave kernel
   int vec;          // adjacent columns per lane (1, 2 or 4); a wave covers 16 * vec columns
   int waves;        // waves per block (4, 8 or 16), each taking a slice of the block's K range
   int strip_cols;   // columns per block
@@ -69,11 +79,15 @@ struct GemvPlan {
   int upg_log2;     // log2(upg) if upg is a power of two, else -1
   int ubp_log2;     // log2 of the activation slots staged per row and lane group
   int gp_log2;      // log2 of the rows of scales / zero points staged per block
+  int upw;          // wave kernel: 32-row units per wave (K / 32 = waves * upw)
+  int gl;           // wave kernel: log2 of the units per group (30: one group)
+  int gpw;          // wave kernel: groups per wave (1, 2 or 4)
+  int xcds;         // XCDs of the device
   size_t counters_bytes;  // arrival counters (one per strip), padded
   size_t workspace_bytes; // counters + split-K partial sums
   int valid;        // 0: the shape does not fit the decode product's staging limits
 };
-GemvPlan gemv_plan(int M, int K, int N, int bits, int group_size);
+GemvPlan gemv_plan(int M, int K, int N, int bits, int group_size, DeviceTopo topo);
 // bf16: x, zeros, scales, bias and y hold bfloat16 instead of fp16 bit patterns.
 hipError_t launch_gemv(const GemvPlan& p, const uint16_t* x, int M, int K, const uint32_t* qw,
                        const uint32_t* qlo, const uint16_t* zeros, const uint16_t* scales,
@@ -81,9 +95,18 @@ hipError_t launch_gemv(const GemvPlan& p, const uint16_t* x, int M, int K, const
                        void* workspace, bool bf16, hipStream_t stream);
 
 // ---- prefill GEMM ---------------------------------------------------------
+struct GemmPlan {
+  int tile;       // block shape: 0 = 256 x 256, 1 = 128 x 128 (2 K groups), 2 / 3 = 64 x 64 (6 / 4 K groups)
+  int bm, bn;     // block tile rows and columns
+  int kgroups;    // groups of waves splitting a block's K range
+  int waves;      // waves per block
+  long long blocks;
+  int xcds, cus;
+};
+GemmPlan gemm_plan(int M, int K, int N, DeviceTopo topo);
 hipError_t launch_gemm(const uint16_t* x, int M, int K, const uint32_t* qw, const uint32_t* qlo,
                        const uint16_t* zeros, const uint16_t* scales, const uint16_t* bias, int N,
-                       int bits, int group_size, uint16_t* y, bool bf16, hipStream_t stream);
+                       int bits, int group_size, uint16_t* y, bool bf16, DeviceTopo topo, hipStream_t stream);
 
 // ---- dequantize to fp16 -------------------------------------------------------
 hipError_t launch_dequant(const uint32_t* qw, const uint32_t* qlo, const uint16_t* zeros,

@@ -37,7 +37,7 @@
 //    registers are copied between sets.
 //  * The epilogue stores straight from the accumulators: a lane's two
 //    paired columns are adjacent, one 4-byte store each.
-//  * Each of the 8 XCDs (own L2 each) works on a contiguous range of tiles,
+//  * Each XCD (own L2 each) works on a contiguous range of tiles,
 //    walked in groups of row tiles so that the blocks in flight on it share
 //    weight and activation panels.
 #include <type_traits>
@@ -48,7 +48,6 @@ namespace qmm {
 namespace {
 
 constexpr int BK = 64;
-constexpr int kCUs = 256;
 
 struct GemmArgs {
   const uint16_t* x;
@@ -62,6 +61,8 @@ struct GemmArgs {
   int upg;       // 32-row units per group
   int upg_log2;  // log2(upg) if a power of two, else -1
   int mblocks, nblocks;
+  int xcds;      // XCDs of the device; blocks are dealt to them round-robin
+  int cus;       // compute units of the device
 };
 
 // Words one lane needs for one 32-column tile and one 16-k step: a 32 x 32 x 16
@@ -142,14 +143,14 @@ __device__ __forceinline__ void frag_codes(const uint32_t* w, const uint32_t* l,
 // in groups of 4 (or 2) row tiles across its columns, so that the blocks in
 // flight on an XCD share fewer activation panels and more weight panels:
 // about 15% fewer L2 misses per slab than one whole column after another.
-__device__ __forceinline__ void tile_of_block(int pid, int mblocks, int nblocks, int& mb, int& nb) {
+__device__ __forceinline__ void tile_of_block(int pid, int mblocks, int nblocks, int xcds, int& mb, int& nb) {
   const int n = mblocks * nblocks;
-  if (n % 8 != 0) {
+  if (xcds <= 1 || n % xcds != 0) {
     nb = pid / mblocks;
     mb = pid - nb * mblocks;
     return;
   }
-  const int per = n / 8, x = pid % 8, li = pid / 8;
+  const int per = n / xcds, x = pid % xcds, li = pid / xcds;
   const int rg = mblocks % 4 == 0 ? 4 : (mblocks % 2 == 0 ? 2 : 1);
   if (rg > 1 && per % mblocks == 0) {
     const int ncx = per / mblocks;  // columns of the XCD's range
@@ -233,7 +234,7 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
   const int kc = lane >> 5;  // k chunk of the lane in a fragment
 
   int mb, nb;
-  tile_of_block(blockIdx.x, g.mblocks, g.nblocks, mb, nb);
+  tile_of_block(blockIdx.x, g.mblocks, g.nblocks, g.xcds, mb, nb);
   const int m0 = mb * BM, n0 = nb * BN;
   const int nk = (g.K + BK - 1) / BK;
   const int ni = (nk + KG - 1) / KG;  // slabs per group (the last ones may pad)
@@ -704,6 +705,31 @@ hipError_t launch_tiles(GemmArgs a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int BITS, bool BF>
+hipError_t launch_bits(const GemmArgs& a, int tile, hipStream_t s) {
+  switch (tile) {
+    case 0: return launch_tiles<BITS, 2, 4, 4, 2, 1, BF>(a, s);
+    case 1: return launch_tiles<BITS, 2, 2, 2, 2, 2, BF>(a, s);
+    case 2: return launch_tiles<BITS, 1, 2, 2, 1, 6, BF>(a, s);
+    case 3: return launch_tiles<BITS, 2, 2, 1, 1, 4, BF>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <bool BF>
+hipError_t launch_dtype(const GemmArgs& a, int bits, int tile, hipStream_t s) {
+  switch (bits) {
+    case 1: return launch_bits<1, BF>(a, tile, s);
+    case 2: return launch_bits<2, BF>(a, tile, s);
+    case 3: return launch_bits<3, BF>(a, tile, s);
+    case 4: return launch_bits<4, BF>(a, tile, s);
+    case 8: return launch_bits<8, BF>(a, tile, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
 // The largest block tile whose grid still gives every CU a block: 256 x 256
 // (8 waves of 128 x 64), else 128 x 128 (two K groups of 4 waves of 64 x 64),
 // else 64 x 64. Smaller tiles have short slabs, so their blocks split K to
@@ -711,38 +737,41 @@ hipError_t launch_tiles(GemmArgs a, hipStream_t s) {
 // chain of slabs (run in pairs) times the latency of one, so it takes six
 // K groups of 2 waves of 64 x 32 where that chain is shorter than with four
 // groups of 4 waves of 32 x 32 (K of 2048 and more), else the four groups.
-template <int BITS, bool BF>
-hipError_t launch_bits(const GemmArgs& a, hipStream_t s) {
-  auto blocks = [&](int bm, int bn) { return (long long)((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn); };
-  if (blocks(256, 256) >= kCUs) return launch_tiles<BITS, 2, 4, 4, 2, 1, BF>(a, s);
-  if (blocks(128, 128) >= kCUs) return launch_tiles<BITS, 2, 2, 2, 2, 2, BF>(a, s);
-  const int nk = (a.K + BK - 1) / BK;
-  auto chain = [&](int kg) {
-    const int n = (nk + kg - 1) / kg;
-    return n + (n & 1);
-  };
-  if (chain(6) < chain(4)) return launch_tiles<BITS, 1, 2, 2, 1, 6, BF>(a, s);
-  return launch_tiles<BITS, 2, 2, 1, 1, 4, BF>(a, s);
-}
-
-template <bool BF>
-hipError_t launch_dtype(const GemmArgs& a, int bits, hipStream_t s) {
-  switch (bits) {
-    case 1: return launch_bits<1, BF>(a, s);
-    case 2: return launch_bits<2, BF>(a, s);
-    case 3: return launch_bits<3, BF>(a, s);
-    case 4: return launch_bits<4, BF>(a, s);
-    case 8: return launch_bits<8, BF>(a, s);
-    default: return hipErrorInvalidValue;
+GemmPlan gemm_plan(int M, int K, int N, DeviceTopo topo) {
+  static const int kShapes[4][3] = {{256, 256, 1}, {128, 128, 2}, {64, 64, 6}, {64, 64, 4}};
+  const int cus = topo.cus > 0 ? topo.cus : 256;
+  auto blocks = [&](int bm, int bn) { return (long long)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+  int tile = 3;
+  if (blocks(256, 256) >= cus) {
+    tile = 0;
+  } else if (blocks(128, 128) >= cus) {
+    tile = 1;
+  } else {
+    const int nk = (K + BK - 1) / BK;
+    auto chain = [&](int kg) {
+      const int n = (nk + kg - 1) / kg;
+      return n + (n & 1);
+    };
+    if (chain(6) < chain(4)) tile = 2;
   }
+  GemmPlan p;
+  p.tile = tile;
+  p.bm = kShapes[tile][0];
+  p.bn = kShapes[tile][1];
+  p.kgroups = kShapes[tile][2];
+  p.waves = tile == 0 ? 8 : (tile == 1 ? 8 : (tile == 2 ? 12 : 16));
+  p.blocks = blocks(p.bm, p.bn);
+  p.xcds = topo.xcds > 0 ? topo.xcds : 8;
+  p.cus = cus;
+  return p;
 }
-
-}  // namespace
 
 hipError_t launch_gemm(const uint16_t* x, int M, int K, const uint32_t* qw, const uint32_t* qlo,
                        const uint16_t* zeros, const uint16_t* scales, const uint16_t* bias, int N, int bits,
-                       int group_size, uint16_t* y, bool bf16, hipStream_t s) {
+                       int group_size, uint16_t* y, bool bf16, DeviceTopo topo, hipStream_t s) {
   GemmArgs a;
+  a.xcds = topo.xcds > 0 ? topo.xcds : 8;
+  a.cus = topo.cus > 0 ? topo.cus : 256;
   a.x = x;
   a.qw = qw;
   a.qlo = qlo;
@@ -757,7 +786,8 @@ hipError_t launch_gemm(const uint16_t* x, int M, int K, const uint32_t* qw, cons
   a.upg_log2 = -1;
   for (int l = 0; l < 31; ++l)
     if ((1 << l) == a.upg) a.upg_log2 = l;
-  return bf16 ? launch_dtype<true>(a, bits, s) : launch_dtype<false>(a, bits, s);
+  const int tile = gemm_plan(M, K, N, topo).tile;
+  return bf16 ? launch_dtype<true>(a, bits, tile, s) : launch_dtype<false>(a, bits, tile, s);
 }
 
 }  // namespace qmm

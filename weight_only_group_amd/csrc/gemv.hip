@@ -34,253 +34,25 @@
 //    partials in split order and writes fp16 (round to nearest even). The sum
 //    order never depends on arrival order, so results are bitwise repeatable,
 //    and the ticket is reset to zero by that block.
-#include <type_traits>
-
-#include "common.h"
-
-#ifndef QMM_GEMV_TARGET_WAVES
-#define QMM_GEMV_TARGET_WAVES 2048  // waves in flight to aim for (8 per CU)
-#endif
-#ifndef QMM_GEMV_VEC
-#define QMM_GEMV_VEC 0  // 0: chosen per shape
-#endif
-#ifndef QMM_GEMV_WAVES
-#define QMM_GEMV_WAVES 0  // 0: chosen per shape
-#endif
-#ifndef QMM_GEMV_XCD_REMAP
-#define QMM_GEMV_XCD_REMAP 1
-#endif
+#include "gemv_common.h"
 
 namespace qmm {
+
+hipError_t launch_gemv_wave_b1(const GemvPlan& p, const GemvArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_gemv_wave_b2(const GemvPlan& p, const GemvArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_gemv_wave_b3(const GemvPlan& p, const GemvArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_gemv_wave_b4(const GemvPlan& p, const GemvArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_gemv_wave_b8(const GemvPlan& p, const GemvArgs& a, bool bf16, hipStream_t s);
+
 namespace {
 
 constexpr int kMaxM = 16;
 constexpr int kMaxSplit = 16;  // blocks along K per column strip
-constexpr int kCUs = 256;      // compute units of an MI355X
 // Arrival counters live in a fixed header at the start of the workspace, one
 // per column strip, and partial sums start after it. The header never
 // overlaps any call's partial sums, so counters left at zero by one call are
 // still zero for the next call, whatever the two shapes are.
 constexpr size_t kCounterHeaderBytes = size_t(kGemvMaxStrips) * 4;
-
-// Words per lane per unit and column: 4-bit 1 row, 8-bit 2 rows, 2-bit 1 row
-// (two lane groups share it), 3-bit one word of each plane.
-template <int BITS> struct Bits;
-template <> struct Bits<4> { static constexpr int NW = 1; };
-template <> struct Bits<8> { static constexpr int NW = 2; };
-template <> struct Bits<2> { static constexpr int NW = 1; };
-template <> struct Bits<3> { static constexpr int NW = 2; };
-template <> struct Bits<1> { static constexpr int NW = 1; };
-
-template <int VEC> struct Vec;
-template <> struct Vec<1> { typedef uint32_t T; };
-template <> struct Vec<2> { typedef u32x2 T; };
-template <> struct Vec<4> { typedef u32x4 T; };
-
-template <int VEC>
-__device__ __forceinline__ uint32_t word_at(typename Vec<VEC>::T w, int v) {
-  if constexpr (VEC == 1) return w;
-  else return w[v];
-}
-
-// (w & m) | (c & ~m). With m and c held in registers (below) this is one
-// bitfield insert (v_bfi_b32) instead of an AND and an OR with literals.
-__device__ __forceinline__ uint32_t bfi(uint32_t m, uint32_t w, uint32_t c) { return (w & m) | (c & ~m); }
-
-// Masks of decode8, made once per kernel: the empty asm statements keep them
-// in registers (a vector register per mask, the magic 1024.0 pair in a scalar
-// one) instead of being folded back into literals.
-template <int BITS> struct DecodeMasks {
-  uint32_t m[4];
-  uint32_t magic;
-};
-template <int BITS> __device__ __forceinline__ DecodeMasks<BITS> decode_masks() {
-  DecodeMasks<BITS> d;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    d.m[p] = BITS == 4 ? (p & 1 ? 0x00F000F0u : 0x000F000Fu)
-           : BITS == 2 ? (p & 1 ? 0x000C000Cu : 0x00030003u)
-           : BITS == 3 ? (p & 1 ? 0x00020002u : 0x000C000Cu)  // 2-bit plane at bits 2-3, 1-bit plane at bit 1
-           : BITS == 1 ? ((1u << p) | (1u << (20 + p))) : 0u;
-    if (BITS == 1 || ((BITS == 2 || BITS == 3 || BITS == 4) && p < 2)) asm("" : "+v"(d.m[p]));
-  }
-  d.magic = kMagic1024x2;
-  asm("" : "+s"(d.magic));
-  return d;
-}
-
-// Place of a code in the fp16 mantissa after decode8: half `hi` of pair p
-// holds 1024 + 2^e q with e = code_exp(p, hi).
-template <int BITS> __host__ __device__ constexpr int code_exp(int p, int hi) {
-  return BITS == 4 ? 4 * (p & 1) : BITS == 2 ? 2 * (p & 1) : BITS == 1 ? p + 4 * hi : BITS == 3 ? 1 : 0;
-}
-
-// Four fp16 pairs 1024 + 2^e q for the 8 codes lane group j takes from its
-// word(s) of one column. Element order (pair p = elements 2p, 2p+1):
-//  4-bit: slots (p, p + 4) of the word          -> k = 8j + {p, p+4}
-//  1-bit: slots (8j + p, 8j + p + 4) of the word -> k = 8j + {p, p+4}
-//  8-bit: slots (0,1),(2,3) of word 0, then of 1 -> k = 8j + e
-//  2/3-bit: slots (i0 + p, i0 + p + 8), i0 = 4 (j & 1), of the plane-2 word
-//           -> k = 16 (j >> 1) + i0 + {p, p + 8}
-// 4-bit: odd pairs are masked 4 places up (one shift for all four pairs);
-// 2-bit: odd pairs 2 places up (two shifts); 1-bit: byte j is copied into
-// both halves and pair p masked at bit p of the low half and bit 4 + p of the
-// high half; 3-bit: q >> 1 (2-bit plane) goes to bits 2-3 and q & 1 (1-bit
-// plane, its bytes of this lane group copied into both halves) to bit 1, so
-// each half is 1024 + 2q.
-template <int BITS>
-__device__ __forceinline__ void decode8(uint32_t w0, uint32_t w1, int j, const DecodeMasks<BITS>& dm,
-                                        uint32_t (&b)[4]) {
-  const uint32_t magic = dm.magic;
-  if constexpr (BITS == 4) {
-    const uint32_t t = w0 >> 8;
-    b[0] = bfi(dm.m[0], w0, magic);
-    b[1] = bfi(dm.m[1], w0, magic);
-    b[2] = bfi(dm.m[0], t, magic);
-    b[3] = bfi(dm.m[1], t, magic);
-  } else if constexpr (BITS == 1) {
-    // bytes (j, 0, j, 0) of the word: 0x0C selects a zero byte
-    const uint32_t t = __builtin_amdgcn_perm(0u, w0, (uint32_t)j | 0x0C000C00u | ((uint32_t)j << 16));
-#pragma unroll
-    for (int p = 0; p < 4; ++p) b[p] = bfi(dm.m[p], t, magic);
-  } else if constexpr (BITS == 8) {
-    // byte permute: (byte0, 0x64, byte1, 0x64) = halves (1024 + q0, 1024 + q1)
-    b[0] = __builtin_amdgcn_perm(0x64646464u, w0, 0x04010400u);
-    b[1] = __builtin_amdgcn_perm(0x64646464u, w0, 0x04030402u);
-    b[2] = __builtin_amdgcn_perm(0x64646464u, w1, 0x04010400u);
-    b[3] = __builtin_amdgcn_perm(0x64646464u, w1, 0x04030402u);
-  } else if constexpr (BITS == 2) {
-    const uint32_t ws = w0 >> (8 * (j & 1));
-    const uint32_t t = ws >> 4;
-    b[0] = bfi(dm.m[0], ws, magic);
-    b[1] = bfi(dm.m[1], ws, magic);
-    b[2] = bfi(dm.m[0], t, magic);
-    b[3] = bfi(dm.m[1], t, magic);
-  } else {
-    // plane2 word w0 holds q >> 1 for 16 k (slot i0 + p of pair p at bits
-    // 2 (i0 + p) and 2 (i0 + p) + 16); plane1 word w1 holds q & 1 for the
-    // unit's 32 k (k = 16 (j >> 1) + i0 + p at that bit, and 8 more for the
-    // high half). After the shifts below, pair p's planes sit at bits 2p of
-    // hs and p of ls (low half) and 16 more (high half).
-    const int i0 = 4 * (j & 1);
-    const uint32_t hs = w0 >> (2 * i0);
-    const uint32_t t = w1 >> (16 * (j >> 1) + i0);
-    const uint32_t ls = __builtin_amdgcn_perm(0u, t, 0x0C010C00u);  // bytes (0, -, 1, -) of t
-    b[0] = bfi(dm.m[0], hs << 2, bfi(dm.m[1], ls << 1, magic));
-    b[1] = bfi(dm.m[0], hs, bfi(dm.m[1], ls, magic));
-    b[2] = bfi(dm.m[0], hs >> 2, bfi(dm.m[1], ls >> 1, magic));
-    b[3] = bfi(dm.m[0], hs >> 4, bfi(dm.m[1], ls >> 2, magic));
-  }
-}
-
-__device__ __forceinline__ f16x8 pack8(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3) {
-  u32x4 v = {a0, a1, a2, a3};
-  return __builtin_bit_cast(f16x8, v);
-}
-
-struct GemvArgs {
-  const uint16_t* x;
-  const uint32_t* qw;
-  const uint32_t* qlo;
-  const uint16_t* zeros;
-  const uint16_t* scales;
-  const uint16_t* bias;  // (N,) or null
-  uint16_t* y;
-  float* part;
-  uint32_t* counters;
-  int M, K, N;
-  int upg;       // 32-row units per group
-  int upg_log2;  // log2(upg) when upg is a power of two, else -1
-  int units_per_block;
-  int ksplit;
-  int ubp_log2;  // log2 of the activation slots per row and lane group (>= units_per_block)
-  int gp_log2;   // log2 of the rows of scales / zero points staged per block
-};
-
-// Units (32 rows of K) per batch of loads issued together, bounded by the
-// registers a wave may hold (128 with 16 waves per block).
-template <int BITS, int VEC, int WAVES> constexpr int chunk_units() {
-  return (Bits<BITS>::NW * VEC <= (WAVES >= 8 ? 2 : 4)) ? 8 : 4;
-}
-
-// Pair classes: pairs whose codes sit at the same mantissa places.
-template <int BITS> constexpr int kPairClasses = BITS == 1 ? 4 : ((BITS == 2 || BITS == 4) ? 2 : 1);
-template <int BITS> __device__ __forceinline__ constexpr int pair_class(int p) {
-  return BITS == 1 ? p : ((BITS == 2 || BITS == 4) ? (p & 1) : 0);
-}
-// 2^-e per half of pair p.
-template <int BITS> __device__ __forceinline__ f16x2 pair_scale(int p) {
-  return f16x2{(f16)(1.0f / (float)(1 << code_exp<BITS>(p, 0))), (f16)(1.0f / (float)(1 << code_exp<BITS>(p, 1)))};
-}
-// h 2^-e + c, one packed operation (an add where e is 0 in both halves).
-template <int BITS> __device__ __forceinline__ f16x2 scale_add(int p, f16x2 h, f16x2 c) {
-  if (code_exp<BITS>(p, 0) == 0 && code_exp<BITS>(p, 1) == 0) return h + c;
-  return __builtin_elementwise_fma(h, pair_scale<BITS>(p), c);
-}
-
-// First k (within a unit) of the activations lane group j feeds: 8 consecutive
-// k for 4- and 8-bit codes; for 2- and 3-bit codes two runs of 4, 8 apart.
-template <int BITS> __device__ __forceinline__ int x_first(int j) {
-  return (BITS == 1 || BITS == 4 || BITS == 8) ? 8 * j : 16 * (j >> 1) + 4 * (j & 1);
-}
-
-// A raw buffer resource over `bytes` bytes at p (out-of-range reads return 0).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, size_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)(uint32_t)bytes, 0x00020000);
-}
-constexpr int kNonTemporal = 2;  // buffer-load cache policy: streamed data
-
-template <int VEC>
-__device__ __forceinline__ typename Vec<VEC>::T load_words(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  if constexpr (VEC == 1) return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kNonTemporal);
-  else if constexpr (VEC == 2) return __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kNonTemporal);
-  else return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kNonTemporal);
-}
-
-// Raw activation bytes of one (row, unit, lane group) slot: 8 halves.
-template <int BITS>
-__device__ __forceinline__ u32x4 load_x_slot(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
-  if constexpr (BITS == 1 || BITS == 4 || BITS == 8) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
-  } else {
-    const u32x2 e = __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0);
-    const u32x2 f = __builtin_amdgcn_raw_buffer_load_b64(r, byte_off + 16, 0, 0);
-    return u32x4{e.x, e.y, f.x, f.y};
-  }
-}
-
-// The A operand (x[m, 32u + k] for the 8 k of lane group j, in decode8's
-// element order) from the raw registers.
-template <int BITS>
-__device__ __forceinline__ u32x4 x_operand(u32x4 d) {
-  if constexpr (BITS == 8) {
-    return d;
-  } else {
-    // 1/4-bit: d = x[0..7], pairs (k, k + 4); 2/3-bit: d = x[o..o+3], x[o+8..o+11], pairs (k, k + 8)
-    const uint32_t lo0 = d.x, lo1 = d.y, hi0 = d.z, hi1 = d.w;
-    return u32x4{__builtin_amdgcn_perm(hi0, lo0, 0x05040100u), __builtin_amdgcn_perm(hi0, lo0, 0x07060302u),
-                 __builtin_amdgcn_perm(hi1, lo1, 0x05040100u), __builtin_amdgcn_perm(hi1, lo1, 0x07060302u)};
-  }
-}
-
-// Word-row offset of lane group j's first word of plane w within a unit, and
-// the rows a unit spans in that plane.
-template <int BITS>
-__device__ __forceinline__ int lane_row(int j, int w) {
-  if constexpr (BITS == 1) return 0;
-  else if constexpr (BITS == 4) return j;
-  else if constexpr (BITS == 8) return 2 * j + w;
-  else if constexpr (BITS == 2) return j >> 1;
-  else return w == 0 ? (j >> 1) : 0;
-}
-template <int BITS>
-__device__ __forceinline__ int unit_rows(int w) {
-  if constexpr (BITS == 1) return 1;
-  else if constexpr (BITS == 4) return 4;
-  else if constexpr (BITS == 8) return 8;
-  else if constexpr (BITS == 2) return 2;
-  else return w == 0 ? 2 : 1;
-}
 
 // LDS of a block: staged activations and scales / zero points, 9 KiB per
 // wave (144 KiB for 16 waves, so that blocks of fewer waves can share a CU).
@@ -313,12 +85,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs g) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = lane >> 4;   // lane group: which 8 k of a unit
   const int cl = lane & 15;  // column group within the wave
-  // Workgroups are dealt to the 8 XCDs round-robin by linear id, and each
-  // XCD has its own L2. Narrow strips share 128-byte lines with their
-  // neighbours, so each XCD is given a contiguous run of strips: a line is
-  // then fetched into one L2 only.
-  int strip = blockIdx.x;
-  if (QMM_GEMV_XCD_REMAP && (gridDim.x & 7) == 0) strip = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  const int strip = xcd_strip(blockIdx.x, gridDim.x, g.xcd_log2);
   const int split = blockIdx.y;
   const int n0 = strip * COLS;
   const int nc = n0 + VEC * cl;  // first of this lane's VEC columns
@@ -667,6 +434,17 @@ hipError_t launch_dtype(const GemvPlan& p, const GemvArgs& a, int bits, hipStrea
   }
 }
 
+hipError_t launch_wave_any(const GemvPlan& p, const GemvArgs& a, int bits, bool bf16, hipStream_t s) {
+  switch (bits) {
+    case 1: return launch_gemv_wave_b1(p, a, bf16, s);
+    case 2: return launch_gemv_wave_b2(p, a, bf16, s);
+    case 3: return launch_gemv_wave_b3(p, a, bf16, s);
+    case 4: return launch_gemv_wave_b4(p, a, bf16, s);
+    case 8: return launch_gemv_wave_b8(p, a, bf16, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 int ceil_log2(int v) {
   int l = 0;
   while ((1 << l) < v) ++l;
@@ -675,21 +453,21 @@ int ceil_log2(int v) {
 
 }  // namespace
 
-GemvPlan gemv_plan(int M, int K, int N, int bits, int group_size) {
+GemvPlan gemv_plan(int M, int K, int N, int bits, int group_size, DeviceTopo topo) {
   GemvPlan p{};
-  // Narrowest column strip whose blocks fit in one round on the 256 CUs
-  // (16, 32 or 64 columns per wave). Every block then covers a strip with
-  // 16 waves splitting K; blocks along K are added only when the strips
-  // alone leave too few waves in flight, or when a block's activations and
-  // scales / zero points would not fit its staging area.
+  const int cus = topo.cus > 0 ? topo.cus : 256;
+  p.xcds = topo.xcds > 0 ? topo.xcds : 8;
+  // Narrowest column strip whose blocks fit in one round on the CUs (16, 32
+  // or 64 columns per wave).
   int vec = 4;
-  if ((N + 15) / 16 <= kCUs) vec = 1;
-  else if ((N + 31) / 32 <= kCUs) vec = 2;
+  if ((N + 15) / 16 <= cus) vec = 1;
+  else if ((N + 31) / 32 <= cus) vec = 2;
   if (QMM_GEMV_VEC != 0) vec = QMM_GEMV_VEC;
   p.vec = vec;
   p.strip_cols = 16 * vec;
   p.nstrips = (N + p.strip_cols - 1) / p.strip_cols;
   const int U = K / 32;
+  const int nw = bits == 3 || bits == 8 ? 2 : 1;  // words per lane per unit and column
   // 16 waves per block, except where two words per lane per unit (3-bit,
   // 8-bit) at 4 columns per lane need more registers than 16 waves allow.
   p.waves = (vec == 4 && (bits == 3 || bits == 8)) ? 8 : 16;
@@ -703,6 +481,41 @@ GemvPlan gemv_plan(int M, int K, int N, int bits, int group_size) {
   int max_ks = U / p.waves;  // at least one unit per wave
   max_ks = max_ks < 1 ? 1 : (max_ks > kMaxSplit ? kMaxSplit : max_ks);
   ks = ks < 1 ? 1 : (ks > max_ks ? max_ks : ks);
+
+  // The wave kernel: one block per strip over all of K (where no split along
+  // K is wanted), U = waves * upw with 8 waves (else 16), at most 32 weight
+  // words per lane, groups of a power-of-two number of units (or one group),
+  // at most 4 groups per wave, and the block's activations within its
+  // staging area (4 slots per thread, 64 KiB).
+  if (ks == 1 && QMM_GEMV_WAVES == 0) {
+    const bool one_group = group_size == -1;
+    const int gl = one_group ? 30 : p.upg_log2;
+    for (int w : {8, 16}) {
+      if (U % w) continue;
+      const int upw = U / w;
+      const bool upw_ok = (w == 8 && (upw == 2 || upw == 4 || upw == 8 || upw == 16)) ||
+                          (w == 16 && (upw == 8 || upw == 16));
+      if (!upw_ok || upw * nw * vec > 32 || gl < 0) continue;
+      // groups per wave: 1 when a group holds all of the wave's units
+      // (upw is a power of two, so a group of >= upw units aligns with it)
+      const int gpw = (one_group || p.upg >= upw) ? 1 : upw / p.upg;
+      const long long rbytes = (long long)w * M * 16 * vec * 4;
+      if (gpw > 4 || (long long)M * U * 4 > 4LL * 64 * w || rbytes > 65536) continue;
+      p.kind = 1;
+      p.waves = w;
+      p.upw = upw;
+      p.gl = gl;
+      p.gpw = gpw;
+      p.ksplit = 1;
+      p.units_per_block = U;
+      p.valid = 1;
+      return p;
+    }
+  }
+
+  // Otherwise the split kernel: blocks along K are added when the strips
+  // alone leave too few waves in flight, or when a block's activations and
+  // scales / zero points would not fit its staging area.
   const int threads = 64 * p.waves, cols = p.strip_cols;
   for (;; ++ks) {
     if (ks > kMaxSplit) return GemvPlan{};  // no valid plan: valid == 0
@@ -759,6 +572,11 @@ hipError_t launch_gemv(const GemvPlan& p, const uint16_t* x, int M, int K, const
   a.ksplit = p.ksplit;
   a.ubp_log2 = p.ubp_log2;
   a.gp_log2 = p.gp_log2;
+  a.xcd_log2 = -1;
+  for (int l = 1; l < 8; ++l)
+    if ((1 << l) == p.xcds && p.nstrips % p.xcds == 0) a.xcd_log2 = l;
+  a.gl = p.gl;
+  if (p.kind == 1) return launch_wave_any(p, a, bits, bf16, s);
   return bf16 ? launch_dtype<true>(p, a, bits, s) : launch_dtype<false>(p, a, bits, s);
 }
 

@@ -1,0 +1,390 @@
+// The wave-local decode product (see the description below), instantiated
+// per code width by gemv_wave_b<bits>.hip.
+#pragma once
+
+#include "gemv_common.h"
+
+namespace qmm {
+namespace {
+
+// ---- wave-local decode product ---------------------------------------------
+// The plan takes this kernel when one block per column strip covers all of K
+// (no split along K), every wave gets the same number UPW of 32-row units
+// (a compile-time constant, so the unit loop is unrolled and carries no
+// scalar bookkeeping per unit), groups hold a power-of-two number of units
+// (or one group spans K) and the block's activations fit its staging area:
+//
+//  * Every wave requests, in this order: its share of the block's activation
+//    slots, the raw scales and zero points of the groups its units touch
+//    (into registers), and the weight words of all its units.
+//  * The activations are written to LDS in the operand order of the matrix
+//    cores (one copy per block, where the lanes of a lane group would
+//    otherwise each permute the same 16 bytes) and the block meets at one
+//    barrier; the activations come from L2 and arrive well before the weight
+//    stream, so the barrier costs little.
+//  * Each wave then runs its units as their words arrive (loads complete in
+//    order). The wave's units form GPW (1, 2 or 4) groups of equal size, a
+//    compile-time structure: no scalar bookkeeping per unit.
+//  * One packed FMA per code pair dequantizes, exactly for integer zero
+//    points; a group whose zero points leave a remainder in that form takes
+//    one more matrix-core product per unit to remove it. The waves' fp32
+//    results are summed through LDS in wave order and rounded once.
+// LDS: the staged activations (M * K / 32 * 4 slots of 16 bytes, in an area
+// of 4 slots per thread), later reused for the per-wave results
+// (WAVES * M * 16 * VEC floats); sized at launch, at most 64 KiB.
+constexpr int kWaveXPerThread = 4; // activation slots one thread stages at most
+
+// VEC consecutive halves of a row of scales or zero points, as loaded: a
+// single half stays a 16-bit value (widening it right after the load would be
+// an instruction that waits for the load), two or four halves are 32-bit words.
+template <int VEC> struct HalfWords {
+  static constexpr int N = VEC == 4 ? 2 : 1;
+  typedef typename std::conditional<VEC == 1, uint16_t, uint32_t>::type T;
+};
+template <int VEC>
+__device__ __forceinline__ void load_halves(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                            typename HalfWords<VEC>::T (&h)[HalfWords<VEC>::N]) {
+  if constexpr (VEC == 1) {
+    h[0] = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+  } else if constexpr (VEC == 2) {
+    h[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  } else {
+    const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    h[0] = t.x;
+    h[1] = t.y;
+  }
+}
+template <int VEC>
+__device__ __forceinline__ uint16_t half_bits(const typename HalfWords<VEC>::T (&h)[HalfWords<VEC>::N], int v) {
+  if constexpr (VEC == 1) return h[0];
+  else return (uint16_t)(h[v >> 1] >> (16 * (v & 1)));
+}
+
+template <int BITS, int VEC, int WAVES, int UPW, int GPW, bool BF, bool M1>
+__global__ __launch_bounds__(64 * WAVES) void gemv_wave_kernel(GemvArgs g) {
+  constexpr int NW = Bits<BITS>::NW;
+  constexpr int NPC = kPairClasses<BITS>;
+  constexpr int COLS = 16 * VEC;
+  constexpr int THREADS = 64 * WAVES;
+  constexpr int HW = HalfWords<VEC>::N;
+  constexpr int GU = UPW / GPW;        // units per group within the wave
+  constexpr int U = WAVES * UPW;       // K / 32
+  constexpr bool SPLIT_E = BITS == 1;
+  typedef typename HalfWords<VEC>::T HT;
+  extern __shared__ __attribute__((aligned(16))) unsigned char dyn_lds[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = lane >> 4;
+  const int cl = lane & 15;
+  const int strip = xcd_strip(blockIdx.x, gridDim.x, g.xcd_log2);
+  const int n0 = strip * COLS;
+  const int nc = n0 + VEC * cl;
+  const int ncc = nc < g.N ? nc : 0;
+  const int m = M1 ? 0 : (cl < g.M ? cl : 0);
+  const int ua = wave * UPW;
+  // First group of the wave and the number of groups: GPW groups of GU units
+  // each, or (GPW == 1) the one group holding all of the wave's units.
+  const int g0 = GPW > 1 ? wave * GPW : (ua >> g.gl);
+  const int G = GPW > 1 ? WAVES * GPW : (U >> g.gl > 0 ? U >> g.gl : 1);
+  u32x4* xs = reinterpret_cast<u32x4*>(dyn_lds);
+  float* red = reinterpret_cast<float*>(dyn_lds);  // reused after the units
+
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(g.x, (size_t)g.M * g.K * 2);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(g.qw, (size_t)U * unit_rows<BITS>(0) * g.N * 4);
+  const __amdgpu_buffer_rsrc_t rl = make_rsrc(BITS == 3 ? g.qlo : g.qw, (size_t)U * unit_rows<BITS>(NW - 1) * g.N * 4);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(g.scales, (size_t)G * g.N * 2);
+  const __amdgpu_buffer_rsrc_t rz = make_rsrc(g.zeros, (size_t)G * g.N * 2);
+
+  // ---- 1. requests, all before the first wait: activation slots, the raw
+  // scales and zero points of the wave's groups, the weight words of its
+  // units.
+  constexpr int XROW = 4 * U;  // activation slots per row: (m, u, j) at m XROW + 4 u + j
+  // One row (M1): XROW <= THREADS slots, one per thread (threads past them
+  // repeat the last slot). Several rows: xpt <= 4 slots per thread.
+  const int xslots = M1 ? XROW : g.M * XROW;
+  const int xpt = M1 ? 1 : (xslots + THREADS - 1) / THREADS;  // wave-uniform
+  u32x4 xraw[kWaveXPerThread];
+#pragma unroll
+  for (int i = 0; i < kWaveXPerThread; ++i) {
+    if (i < xpt) {  // scalar (compile-time for one row)
+      const int sl = min(tid + THREADS * i, xslots - 1);
+      const int mm = M1 ? 0 : sl / XROW, rem = M1 ? sl : sl % XROW;
+      xraw[i] = load_x_slot<BITS>(rx, (uint32_t)(mm * g.K + 32 * (rem >> 2) + x_first<BITS>(rem & 3)) * 2u);
+    }
+  }
+  HT sraw[GPW][HW], zraw[GPW][HW];
+#pragma unroll
+  for (int gi = 0; gi < GPW; ++gi) {
+    const uint32_t off = ((uint32_t)(g0 + gi) * (uint32_t)g.N + (uint32_t)ncc) * 2u;
+    load_halves<VEC>(rs, off, sraw[gi]);
+    load_halves<VEC>(rz, off, zraw[gi]);
+  }
+  // The zero points checked for the exact one-operation dequantization: lane
+  // group j takes group slot j (its own copy, so that each lane checks VEC
+  // values instead of GPW * VEC).
+  HT zchk[HW];
+  if constexpr (!BF) {
+    const uint32_t off = ((uint32_t)(g0 + (j < GPW ? j : GPW - 1)) * (uint32_t)g.N + (uint32_t)ncc) * 2u;
+    load_halves<VEC>(rz, off, zchk);
+  }
+  uint32_t woff[NW];
+#pragma unroll
+  for (int w = 0; w < NW; ++w) woff[w] = (uint32_t)(lane_row<BITS>(j, w) * g.N + ncc) * 4u;
+  typename Vec<VEC>::T wv[UPW][NW];
+#pragma unroll
+  for (int c = 0; c < UPW; ++c) {
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const uint32_t soff = (uint32_t)((ua + c) * unit_rows<BITS>(w)) * (uint32_t)g.N * 4u;
+      wv[c][w] = load_words<VEC>((BITS == 3 && w == 1) ? rl : rw, woff[w], soff);
+    }
+  }
+
+  // ---- 2. activations into LDS in operand order; one barrier. Each thread
+  // writes its xpt slots under a wave-uniform condition only (slots past the
+  // activations, within the area of THREADS * kWaveXPerThread slots, receive
+  // copies that are never read): a write under a per-lane condition let the
+  // compiler move that slot's load after the weight requests and wait for
+  // all of them before the barrier.
+#pragma unroll
+  for (int i = 0; i < kWaveXPerThread; ++i)
+    if (i < xpt) xs[tid + THREADS * i] = x_operand<BITS>(xraw[i]);  // scalar condition
+  __syncthreads();
+  // Nothing below (the group constants wait for the scales and zero points,
+  // which come from HBM) may be scheduled above the barrier: the barrier
+  // should wait for the activations only, which come from L2.
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- 3. the wave's units, group by group (static).
+  // fp16 data: per pair class, c = -(1024 2^-e + z) rounded to fp16; one
+  // packed FMA h 2^-e + c then gives q - z - r with the remainder
+  // r = c + 1024 2^-e + z (exact in fp32), which is zero for integer zero
+  // points |z| <= 1024. The wave checks that once, here, while its weight
+  // words are still arriving (lane group j checks group slot j); a wave with any other zero point removes the
+  // remainders in one more pass after its units (x times a B operand of -r
+  // per group), so the unit loop itself has no branch. bf16 data: q - z is
+  // formed in fp32 (czf = 1024 2^-e + z, or z alone for 1-bit codes).
+  int fix = 0;
+  if constexpr (!BF) {
+    bool inexact = false;
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+      const float zf = half_bits_to_float(half_bits<VEC>(zchk, v));
+      inexact = inexact || zf != __builtin_rintf(zf) || __builtin_fabsf(zf) > 1024.f;
+    }
+    fix = __builtin_amdgcn_readfirstlane((int)__any(inexact));
+  }
+  const DecodeMasks<BITS> dm = decode_masks<BITS>();
+  f32x4 total[VEC];
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) total[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const u32x4* xrow = xs + (m * XROW + 4 * ua + j);  // unit ua + c at xrow[4 c]
+  // c per pair class and column for group slot gi, in fp16 arithmetic (one
+  // rounding of the exact -(1024 2^-e + z)).
+  auto group_zc = [&](int gi, f16x2 (&zc)[NPC][VEC]) {
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+      const f16 zh = __builtin_bit_cast(f16, half_bits<VEC>(zraw[gi], v));
+      const f16x2 zz = f16x2{zh, zh};
+#pragma unroll
+      for (int c = 0; c < NPC; ++c) {
+        const f16x2 base = f16x2{(f16)(1024.f / (float)(1 << code_exp<BITS>(c, 0))),
+                                 (f16)(1024.f / (float)(1 << code_exp<BITS>(c, 1)))};
+        zc[c][v] = -(base + zz);
+      }
+    }
+  };
+#pragma unroll
+  for (int gi = 0; gi < GPW; ++gi) {
+    float sc[VEC], czf[NPC][VEC];
+    f16x2 zc[NPC][VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+      sc[v] = bits_to_float<BF>(half_bits<VEC>(sraw[gi], v));
+      if constexpr (BF) {
+        const float zf = bits_to_float<BF>(half_bits<VEC>(zraw[gi], v));
+#pragma unroll
+        for (int c = 0; c < NPC; ++c) czf[c][v] = SPLIT_E ? zf : 1024.f / (float)(1 << code_exp<BITS>(c, 0)) + zf;
+      }
+    }
+    if constexpr (!BF) group_zc(gi, zc);
+    f32x4 acc[VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int cu = 0; cu < GU; ++cu) {
+      const int c = gi * GU + cu;
+      const u32x4 araw = xrow[4 * c];
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) {
+        uint32_t b[4];
+        decode8<BITS>(word_at<VEC>(wv[c][0], v), NW > 1 ? word_at<VEC>(wv[c][NW - 1], v) : 0u, j, dm, b);
+        uint32_t d[4];
+        if constexpr (BF) {
+          // A factor of 1 is kept opaque: the compiler would otherwise fold
+          // fma(h, 1, c) into a conversion and an add, where the
+          // mixed-precision FMA (v_fma_mix_f32) takes the fp16 half as is.
+          float one = 1.f;
+          asm("" : "+v"(one));
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const f16x2 h = as_f16x2(b[p]);
+            const int pc = pair_class<BITS>(p);
+            const float s_lo = code_exp<BITS>(p, 0) == 0 ? one : 1.0f / (float)(1 << code_exp<BITS>(p, 0));
+            const float s_hi = code_exp<BITS>(p, 1) == 0 ? one : 1.0f / (float)(1 << code_exp<BITS>(p, 1));
+            if constexpr (SPLIT_E) {
+              d[p] = pack_bf16(__builtin_fmaf((float)h.x, s_lo, -1024.f * s_lo) - czf[pc][v],
+                               __builtin_fmaf((float)h.y, s_hi, -1024.f * s_hi) - czf[pc][v]);
+            } else {
+              d[p] = pack_bf16(__builtin_fmaf((float)h.x, s_lo, -czf[pc][v]), __builtin_fmaf((float)h.y, s_hi, -czf[pc][v]));
+            }
+          }
+          const bf16x8 A = __builtin_bit_cast(bf16x8, araw);
+          const bf16x8 B = __builtin_bit_cast(bf16x8, u32x4{d[0], d[1], d[2], d[3]});
+          acc[v] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[v], 0, 0, 0);
+        } else {
+#pragma unroll
+          for (int p = 0; p < 4; ++p) d[p] = as_u32(scale_add<BITS>(p, as_f16x2(b[p]), zc[pair_class<BITS>(p)][v]));
+          const f16x8 A = __builtin_bit_cast(f16x8, araw);
+          acc[v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, pack8(d[0], d[1], d[2], d[3]), acc[v], 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) total[v] += sc[v] * acc[v];
+  }
+  if constexpr (!BF) {
+    if (fix) {  // scalar, once per wave: groups whose zero points leave a remainder
+#pragma unroll
+      for (int gi = 0; gi < GPW; ++gi) {
+        // The group's scales and zero points are requested again (from L2
+        // by now), so that their registers need not live through the units.
+        HT sh[HW], zh[HW];
+        const uint32_t off = ((uint32_t)(g0 + gi) * (uint32_t)g.N + (uint32_t)ncc) * 2u;
+        load_halves<VEC>(rs, off, sh);
+        load_halves<VEC>(rz, off, zh);
+        f16x2 zc[NPC][VEC];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+          const f16 zhh = __builtin_bit_cast(f16, half_bits<VEC>(zh, v));
+          const f16x2 zz = f16x2{zhh, zhh};
+#pragma unroll
+          for (int c = 0; c < NPC; ++c) {
+            const f16x2 base = f16x2{(f16)(1024.f / (float)(1 << code_exp<BITS>(c, 0))),
+                                     (f16)(1024.f / (float)(1 << code_exp<BITS>(c, 1)))};
+            zc[c][v] = -(base + zz);
+          }
+        }
+        uint32_t rn[4][VEC];  // B operand halves: -r = -(c + 1024 2^-e) - z, each step exact in fp32
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+          const float zf = half_bits_to_float(half_bits<VEC>(zh, v));
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const int c = pair_class<BITS>(p);
+            const float blo = 1024.f / (float)(1 << code_exp<BITS>(c, 0)), bhi = 1024.f / (float)(1 << code_exp<BITS>(c, 1));
+            rn[p][v] = as_u32(f16x2{(f16)((-(float)zc[c][v].x - blo) - zf), (f16)((-(float)zc[c][v].y - bhi) - zf)});
+          }
+        }
+        f32x4 acc[VEC];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int cu = 0; cu < GU; ++cu) {
+          const f16x8 A = __builtin_bit_cast(f16x8, xrow[4 * (gi * GU + cu)]);
+#pragma unroll
+          for (int v = 0; v < VEC; ++v)
+            acc[v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, pack8(rn[0][v], rn[1][v], rn[2][v], rn[3][v]), acc[v], 0, 0, 0);
+        }
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) total[v] += bits_to_float<false>(half_bits<VEC>(sh, v)) * acc[v];
+      }
+    }
+  }
+
+  // ---- 4. the block's waves summed in wave order, in the LDS that held the
+  // activations (hence the barrier first); bias; one rounding.
+  // D layout: lane holds rows 4 j + i (i < 4) of column VEC * cl + v.
+  __syncthreads();
+  const int rows = M1 ? 1 : g.M;
+  if constexpr (M1) {
+    if (j == 0) {
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) red[wave * COLS + VEC * cl + v] = total[v][0];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * j + i;
+      if (row < rows) {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) red[(wave * rows + row) * COLS + VEC * cl + v] = total[v][i];
+      }
+    }
+  }
+  __syncthreads();
+  const int entries = rows * COLS;
+  for (int e = tid; e < entries; e += THREADS) {
+    const int row = e / COLS, col = e - row * COLS;
+    if (n0 + col < g.N) {
+      float sum = red[e];
+#pragma unroll
+      for (int w = 1; w < WAVES; ++w) sum += red[w * entries + e];
+      if (g.bias) sum += bits_to_float<BF>(g.bias[n0 + col]);
+      g.y[(size_t)row * g.N + n0 + col] = float_to_bits<BF>(sum);
+    }
+  }
+}
+
+template <int BITS, int VEC, int WAVES, int UPW, int GPW, bool BF>
+hipError_t launch_wave_typed(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
+  const size_t lds = cmax(64 * WAVES * kWaveXPerThread * 16, WAVES * a.M * 16 * VEC * 4);
+  if (a.M == 1) gemv_wave_kernel<BITS, VEC, WAVES, UPW, GPW, BF, true><<<p.nstrips, 64 * WAVES, lds, s>>>(a);
+  else gemv_wave_kernel<BITS, VEC, WAVES, UPW, GPW, BF, false><<<p.nstrips, 64 * WAVES, lds, s>>>(a);
+  return hipGetLastError();
+}
+
+// Weight words a lane holds: UPW * NW * VEC <= 32 (the plan only picks such shapes).
+template <int BITS, int VEC, int UPW> constexpr bool wave_fits() { return UPW * Bits<BITS>::NW * VEC <= 32; }
+
+template <int BITS, int VEC, int WAVES, int UPW, bool BF>
+hipError_t launch_wave_if(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
+  if constexpr (wave_fits<BITS, VEC, UPW>()) {
+    switch (p.gpw) {
+      case 1: return launch_wave_typed<BITS, VEC, WAVES, UPW, 1, BF>(p, a, s);
+      case 2: return launch_wave_typed<BITS, VEC, WAVES, UPW, 2, BF>(p, a, s);
+      case 4: if constexpr (UPW >= 4) return launch_wave_typed<BITS, VEC, WAVES, UPW, 4, BF>(p, a, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int BITS, int VEC, bool BF>
+hipError_t launch_wave_vec(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
+  if (p.waves == 8) {
+    switch (p.upw) {
+      case 2: return launch_wave_if<BITS, VEC, 8, 2, BF>(p, a, s);
+      case 4: return launch_wave_if<BITS, VEC, 8, 4, BF>(p, a, s);
+      case 8: return launch_wave_if<BITS, VEC, 8, 8, BF>(p, a, s);
+      case 16: return launch_wave_if<BITS, VEC, 8, 16, BF>(p, a, s);
+    }
+  } else if (p.waves == 16) {
+    switch (p.upw) {
+      case 8: return launch_wave_if<BITS, VEC, 16, 8, BF>(p, a, s);
+      case 16: return launch_wave_if<BITS, VEC, 16, 16, BF>(p, a, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int BITS, bool BF>
+hipError_t launch_wave_bits(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
+  if (p.vec == 1) return launch_wave_vec<BITS, 1, BF>(p, a, s);
+  if (p.vec == 2) return launch_wave_vec<BITS, 2, BF>(p, a, s);
+  return launch_wave_vec<BITS, 4, BF>(p, a, s);
+}
+
+}  // namespace
+}  // namespace qmm

@@ -1,0 +1,10 @@
+// The wave-local decode product for 1-bit codes (instances of gemv_wave.h).
+#include "gemv_wave.h"
+
+namespace qmm {
+
+hipError_t launch_gemv_wave_b1(const GemvPlan& p, const GemvArgs& a, bool bf16, hipStream_t s) {
+  return bf16 ? launch_wave_bits<1, true>(p, a, s) : launch_wave_bits<1, false>(p, a, s);
+}
+
+}  // namespace qmm
