@@ -3,6 +3,7 @@
 // made for an invalid request.
 #include <stdarg.h>
 #include <stdio.h>
+#include <string.h>
 
 #include <mutex>
 
@@ -77,9 +78,8 @@ qmm_status check_group(int K, int group_size) {
   return QMM_OK;
 }
 
-qmm_status check_product(const uint16_t* x, int M, int K, const int32_t* qweight, const int32_t* qweight_lo,
-                         const uint16_t* zeros, const uint16_t* scales, const uint16_t* bias, int N, int bits,
-                         int group_size, const uint16_t* y, int max_m) {
+// The shape rules every product applies (and the plan queries with them).
+qmm_status check_product_shape(int M, int K, int N, int bits, int group_size, int max_m) {
   if (!bits_ok(bits)) return fail(QMM_ERR_BITS, "bits=%d is not one of 1, 2, 3, 4, 8", bits);
   if (M < 1 || M > max_m) return fail(QMM_ERR_SHAPE, "M=%d must be in [1, %d]", M, max_m);
   if (K < 32 || K % 32) return fail(QMM_ERR_SHAPE, "K=%d must be a positive multiple of 32", K);
@@ -95,6 +95,14 @@ qmm_status check_product(const uint16_t* x, int M, int K, const int32_t* qweight
   if ((unsigned long long)M * K * 2 >= lim || (unsigned long long)K * N * (bits == 3 ? 2 : bits) / 8 >= lim ||
       groups * N * 2 >= lim)
     return fail(QMM_ERR_SHAPE, "x, qweight, zeros and scales must each be smaller than 4 GiB");
+  return QMM_OK;
+}
+
+qmm_status check_product(const uint16_t* x, int M, int K, const int32_t* qweight, const int32_t* qweight_lo,
+                         const uint16_t* zeros, const uint16_t* scales, const uint16_t* bias, int N, int bits,
+                         int group_size, const uint16_t* y, int max_m) {
+  const qmm_status st = check_product_shape(M, K, N, bits, group_size, max_m);
+  if (st != QMM_OK) return st;
   if (!x || !qweight || !zeros || !scales || !y) return fail(QMM_ERR_NULL, "a required pointer is NULL");
   if (bits == 3 && !qweight_lo) return fail(QMM_ERR_NULL, "qweight_lo (1-bit plane) is NULL for 3-bit codes");
   if (!aligned16(x) || !aligned16(qweight) || !aligned16(zeros) || !aligned16(scales) || !aligned16(y) ||
@@ -275,19 +283,19 @@ qmm_status qmm_unpack(const int32_t* qweight, const int32_t* qweight_lo, int K, 
 }
 
 size_t qmm_workspace_bytes(int M, int K, int N, int bits, int group_size) {
-  if (!bits_ok(bits) || M < 1 || M > 16 || K < 32 || K % 32 || N < 8 || N % 8 || N > qmm::kGemvMaxN) return 0;
-  if (group_size != -1 && (group_size <= 0 || group_size % 32 || K % group_size)) return 0;
+  // A size query reports nothing: the last error message stays as it was.
+  char saved[sizeof g_last_error];
+  memcpy(saved, g_last_error, sizeof saved);
+  const qmm_status st = check_product_shape(M, K, N, bits, group_size, 16);
+  memcpy(g_last_error, saved, sizeof saved);
+  if (st != QMM_OK || N > qmm::kGemvMaxN) return 0;
   return qmm::gemv_plan(M, K, N, bits, group_size, qmm::device_topology()).workspace_bytes;
 }
 
 qmm_status qmm_gemv_plan_info(int M, int K, int N, int bits, int group_size, int32_t* info, int n) {
-  if (!bits_ok(bits)) return fail(QMM_ERR_BITS, "bits=%d is not one of 1, 2, 3, 4, 8", bits);
-  if (M < 1 || M > 16) return fail(QMM_ERR_SHAPE, "M=%d must be in [1, 16]", M);
-  if (K < 32 || K % 32) return fail(QMM_ERR_SHAPE, "K=%d must be a positive multiple of 32", K);
-  if (N < 8 || N % 8 || N > qmm::kGemvMaxN)
-    return fail(QMM_ERR_SHAPE, "N=%d must be a positive multiple of 8, at most %d", N, qmm::kGemvMaxN);
-  const qmm_status gs = check_group(K, group_size);
-  if (gs != QMM_OK) return gs;
+  const qmm_status st = check_product_shape(M, K, N, bits, group_size, 16);
+  if (st != QMM_OK) return st;
+  if (N > qmm::kGemvMaxN) return fail(QMM_ERR_SHAPE, "N=%d exceeds the decode product's limit of %d", N, qmm::kGemvMaxN);
   if (n > 0 && !info) return fail(QMM_ERR_NULL, "info is NULL");
   const qmm::DeviceTopo topo = qmm::device_topology();
   const qmm::GemvPlan p = qmm::gemv_plan(M, K, N, bits, group_size, topo);
@@ -301,12 +309,8 @@ qmm_status qmm_gemv_plan_info(int M, int K, int N, int bits, int group_size, int
 }
 
 qmm_status qmm_gemm_plan_info(int M, int K, int N, int bits, int group_size, int32_t* info, int n) {
-  if (!bits_ok(bits)) return fail(QMM_ERR_BITS, "bits=%d is not one of 1, 2, 3, 4, 8", bits);
-  if (M < 1) return fail(QMM_ERR_SHAPE, "M=%d must be >= 1", M);
-  if (K < 32 || K % 32) return fail(QMM_ERR_SHAPE, "K=%d must be a positive multiple of 32", K);
-  if (N < 8 || N % 8) return fail(QMM_ERR_SHAPE, "N=%d must be a positive multiple of 8", N);
-  const qmm_status gs = check_group(K, group_size);
-  if (gs != QMM_OK) return gs;
+  const qmm_status st = check_product_shape(M, K, N, bits, group_size, 1 << 30);
+  if (st != QMM_OK) return st;
   if (n > 0 && !info) return fail(QMM_ERR_NULL, "info is NULL");
   const qmm::GemmPlan p = qmm::gemm_plan(M, K, N, qmm::device_topology());
   const int32_t v[7] = {p.bm, p.bn, p.kgroups, p.waves, (int32_t)(p.blocks < INT32_MAX ? p.blocks : INT32_MAX),

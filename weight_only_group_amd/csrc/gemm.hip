@@ -236,7 +236,7 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
   int mb, nb;
   tile_of_block(blockIdx.x, g.mblocks, g.nblocks, g.xcds, mb, nb);
   const int m0 = mb * BM, n0 = nb * BN;
-  const int nk = (g.K + BK - 1) / BK;
+  const int nk = (int)(((uint32_t)g.K + BK - 1) / BK);
   const int ni = (nk + KG - 1) / KG;  // slabs per group (the last ones may pad)
   auto gslab = [&](int i) { return kg + KG * i; };  // global slab of the group's i-th
 
@@ -327,13 +327,13 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
           const int row0 = past ? 0 : frag_row<BITS>(ks, s, 0, w);
-          const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rw, p_voff[p] + kcoff, row0 * g.N * 4, kWeightPolicy);
+          const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rw, p_voff[p] + kcoff, (uint32_t)row0 * (uint32_t)g.N * 4u, kWeightPolicy);
           S.w[2 * p][w] = v.x;
           S.w[2 * p + 1][w] = v.y;
         }
         if constexpr (NL > 0) {
           const int lrow = past ? 0 : ks * 2 + (s >> 1);
-          const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rl, p_voff[p], lrow * g.N * 4, kWeightPolicy);
+          const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rl, p_voff[p], (uint32_t)lrow * (uint32_t)g.N * 4u, kWeightPolicy);
           S.l[2 * p][0] = v.x;
           S.l[2 * p + 1][0] = v.y;
         }
@@ -345,11 +345,11 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
         const int row0 = past ? 0 : frag_row<BITS>(ks, s, 0, w);
-        S.w[t][w] = __builtin_amdgcn_raw_buffer_load_b32(rw, b_voff[t] + kcoff, row0 * g.N * 4, kWeightPolicy);
+        S.w[t][w] = __builtin_amdgcn_raw_buffer_load_b32(rw, b_voff[t] + kcoff, (uint32_t)row0 * (uint32_t)g.N * 4u, kWeightPolicy);
       }
       if constexpr (NL > 0) {
         const int lrow = past ? 0 : ks * 2 + (s >> 1);
-        S.l[t][0] = __builtin_amdgcn_raw_buffer_load_b32(rl, b_voff[t], lrow * g.N * 4, kWeightPolicy);
+        S.l[t][0] = __builtin_amdgcn_raw_buffer_load_b32(rl, b_voff[t], (uint32_t)lrow * (uint32_t)g.N * 4u, kWeightPolicy);
       }
     }
   };
@@ -369,11 +369,11 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
 #pragma unroll
       for (int q = 0; q < NZ; ++q) {
         if constexpr (PAIR) {
-          Z.z[q][h] = __builtin_amdgcn_raw_buffer_load_b32(rz, p_voff[q] / 2u, grp * g.N * 2, 0);
-          Z.s[q][h] = __builtin_amdgcn_raw_buffer_load_b32(rs, p_voff[q] / 2u, grp * g.N * 2, 0);
+          Z.z[q][h] = __builtin_amdgcn_raw_buffer_load_b32(rz, p_voff[q] / 2u, (uint32_t)grp * (uint32_t)g.N * 2u, 0);
+          Z.s[q][h] = __builtin_amdgcn_raw_buffer_load_b32(rs, p_voff[q] / 2u, (uint32_t)grp * (uint32_t)g.N * 2u, 0);
         } else {
-          Z.z[q][h] = __builtin_amdgcn_raw_buffer_load_b16(rz, b_voff[q] / 2u, grp * g.N * 2, 0);
-          Z.s[q][h] = __builtin_amdgcn_raw_buffer_load_b16(rs, b_voff[q] / 2u, grp * g.N * 2, 0);
+          Z.z[q][h] = __builtin_amdgcn_raw_buffer_load_b16(rz, b_voff[q] / 2u, (uint32_t)grp * (uint32_t)g.N * 2u, 0);
+          Z.s[q][h] = __builtin_amdgcn_raw_buffer_load_b16(rs, b_voff[q] / 2u, (uint32_t)grp * (uint32_t)g.N * 2u, 0);
         }
       }
     }
@@ -740,14 +740,14 @@ hipError_t launch_dtype(const GemmArgs& a, int bits, int tile, hipStream_t s) {
 GemmPlan gemm_plan(int M, int K, int N, DeviceTopo topo) {
   static const int kShapes[4][3] = {{256, 256, 1}, {128, 128, 2}, {64, 64, 6}, {64, 64, 4}};
   const int cus = topo.cus > 0 ? topo.cus : 256;
-  auto blocks = [&](int bm, int bn) { return (long long)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+  auto blocks = [&](int bm, int bn) { return (((long long)M + bm - 1) / bm) * (((long long)N + bn - 1) / bn); };
   int tile = 3;
   if (blocks(256, 256) >= cus) {
     tile = 0;
   } else if (blocks(128, 128) >= cus) {
     tile = 1;
   } else {
-    const int nk = (K + BK - 1) / BK;
+    const int nk = (int)(((long long)K + BK - 1) / BK);
     auto chain = [&](int kg) {
       const int n = (nk + kg - 1) / kg;
       return n + (n & 1);

@@ -365,25 +365,28 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs g) {
     return;
   }
 
-  // Blocks along K hand over through the workspace. Partial sums are written
-  // and read with device-scope atomic accesses, which go to the
-  // device-coherent level of the memory hierarchy rather than an XCD's own
-  // L2; each thread waits until its stores are acknowledged before the block
-  // takes its ticket, so the last block to arrive sees every partial.
+  // Blocks along K hand over through the workspace, in the pattern of a
+  // ticketed reduction: every thread publishes its partial sums (device-scope
+  // atomic stores) and then issues a release fence at device scope; the block
+  // meets at a barrier, after which one thread takes the strip's ticket with
+  // an acquire-release read-modify-write. The block that draws the last
+  // ticket therefore follows every other block's release, and each of its
+  // threads issues an acquire fence before reading the partials.
   float* mypart = g.part + (size_t)split * g.M * g.N;
   for (int e = tid; e < entries; e += THREADS) {
     const int row = e / COLS, col = e - row * COLS;
     if (n0 + col < g.N)
       __hip_atomic_store(mypart + (size_t)row * g.N + n0 + col, block_sum(e), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) expcnt(0) lgkmcnt(0): stores acknowledged
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   __syncthreads();
   if (tid == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(&g.counters[strip], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t prev = __hip_atomic_fetch_add(&g.counters[strip], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     last_flag = (prev == (uint32_t)(g.ksplit - 1));
   }
   __syncthreads();
   if (!last_flag) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   for (int e = tid; e < entries; e += THREADS) {
     const int row = e / COLS, col = e - row * COLS;
     if (n0 + col < g.N) {
