@@ -17,6 +17,9 @@
 #ifndef QMM_GEMV_WAVES
 #define QMM_GEMV_WAVES 0  // 0: chosen per shape
 #endif
+#ifndef QMM_GEMV_WAVE_X
+#define QMM_GEMV_WAVE_X 1  // wave kernel, several rows: each wave stages its own activations (0: the block, one barrier)
+#endif
 #ifndef QMM_GEMV_XCD_REMAP
 #define QMM_GEMV_XCD_REMAP 1
 #endif

@@ -101,17 +101,33 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_wave_kernel(GemvArgs g) {
   // scales and zero points of the wave's groups, the weight words of its
   // units.
   constexpr int XROW = 4 * U;  // activation slots per row: (m, u, j) at m XROW + 4 u + j
-  // One row (M1): XROW <= THREADS slots, one per thread (threads past them
-  // repeat the last slot). Several rows: xpt <= 4 slots per thread.
-  const int xslots = M1 ? XROW : g.M * XROW;
-  const int xpt = M1 ? 1 : (xslots + THREADS - 1) / THREADS;  // wave-uniform
+  // One row (M1): the block stages XROW <= THREADS slots, one per thread
+  // (threads past them repeat the last slot), and meets at a barrier.
+  // Several rows (OWN): each wave stages its own slots (its units, every
+  // row: M * UPW * 4 <= 256 of them, a limit of the plan, so at most 4 per
+  // lane) in an area of its own and waits for nothing else: a wave whose
+  // activations arrive early starts its units while the other waves' still
+  // come in (later waves' requests queue behind the earlier waves' weight
+  // words).
+  constexpr bool OWN = !M1 && QMM_GEMV_WAVE_X;
+  constexpr int WSLOTS = 64 * kWaveXPerThread;  // slots of a wave's own area
+  constexpr int WROW = 4 * UPW;                 // a wave's slots per row: (m, c, j) at m WROW + 4 c + j
+  const int xslots = OWN ? g.M * WROW : (M1 ? XROW : g.M * XROW);
+  const int xpt = M1 ? 1 : (OWN ? (xslots + 63) / 64 : (xslots + THREADS - 1) / THREADS);  // wave-uniform
+  const int xbase = OWN ? wave * WSLOTS : 0;  // first slot of the thread's writes
   u32x4 xraw[kWaveXPerThread];
 #pragma unroll
   for (int i = 0; i < kWaveXPerThread; ++i) {
     if (i < xpt) {  // scalar (compile-time for one row)
-      const int sl = min(tid + THREADS * i, xslots - 1);
-      const int mm = M1 ? 0 : sl / XROW, rem = M1 ? sl : sl % XROW;
-      xraw[i] = load_x_slot<BITS>(rx, (uint32_t)(mm * g.K + 32 * (rem >> 2) + x_first<BITS>(rem & 3)) * 2u);
+      if constexpr (OWN) {
+        const int sl = min(lane + 64 * i, xslots - 1);
+        const int mm = sl / WROW, rem = sl % WROW;
+        xraw[i] = load_x_slot<BITS>(rx, (uint32_t)(mm * g.K + 32 * (ua + (rem >> 2)) + x_first<BITS>(rem & 3)) * 2u);
+      } else {
+        const int sl = min(tid + THREADS * i, xslots - 1);
+        const int mm = M1 ? 0 : sl / XROW, rem = M1 ? sl : sl % XROW;
+        xraw[i] = load_x_slot<BITS>(rx, (uint32_t)(mm * g.K + 32 * (rem >> 2) + x_first<BITS>(rem & 3)) * 2u);
+      }
     }
   }
   HT sraw[GPW][HW], zraw[GPW][HW];
@@ -150,11 +166,17 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_wave_kernel(GemvArgs g) {
   // all of them before the barrier.
 #pragma unroll
   for (int i = 0; i < kWaveXPerThread; ++i)
-    if (i < xpt) xs[tid + THREADS * i] = x_operand<BITS>(xraw[i]);  // scalar condition
-  __syncthreads();
+    if (i < xpt) xs[xbase + (OWN ? lane + 64 * i : tid + THREADS * i)] = x_operand<BITS>(xraw[i]);  // scalar condition
+  if constexpr (OWN) {
+    // The wave reads back only what it wrote itself: LDS operations of one
+    // wave take effect in order, so a compiler-level fence is enough.
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  } else {
+    __syncthreads();
+  }
   // Nothing below (the group constants wait for the scales and zero points,
-  // which come from HBM) may be scheduled above the barrier: the barrier
-  // should wait for the activations only, which come from L2.
+  // which come from HBM) may be scheduled above this point: the wait here
+  // should be for the activations only, which come from L2.
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- 3. the wave's units, group by group (static).
@@ -180,7 +202,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_wave_kernel(GemvArgs g) {
   f32x4 total[VEC];
 #pragma unroll
   for (int v = 0; v < VEC; ++v) total[v] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const u32x4* xrow = xs + (m * XROW + 4 * ua + j);  // unit ua + c at xrow[4 c]
+  const u32x4* xrow = OWN ? xs + (wave * WSLOTS + m * WROW + j) : xs + (m * XROW + 4 * ua + j);  // unit ua + c at xrow[4 c]
   // c per pair class and column for group slot gi, in fp16 arithmetic (one
   // rounding of the exact -(1024 2^-e + z)).
   auto group_zc = [&](int gi, f16x2 (&zc)[NPC][VEC]) {
