@@ -18,7 +18,7 @@
 #define QMM_GEMV_WAVES 0  // 0: chosen per shape
 #endif
 #ifndef QMM_GEMV_WAVE_X
-#define QMM_GEMV_WAVE_X 1  // wave kernel, several rows: each wave stages its own activations (0: the block, one barrier)
+#define QMM_GEMV_WAVE_X 1  // wave kernel: waves stage their own activations (0: the block, one barrier)
 #endif
 #ifndef QMM_GEMV_XCD_REMAP
 #define QMM_GEMV_XCD_REMAP 1

@@ -14,14 +14,18 @@ namespace {
 // scalar bookkeeping per unit), groups hold a power-of-two number of units
 // (or one group spans K) and the block's activations fit its staging area:
 //
-//  * Every wave requests, in this order: its share of the block's activation
-//    slots, the raw scales and zero points of the groups its units touch
-//    (into registers), and the weight words of all its units.
+//  * Every wave requests, in this order: activation slots, the raw scales
+//    and zero points of the groups its units touch (into registers), and
+//    the weight words of all its units.
 //  * The activations are written to LDS in the operand order of the matrix
-//    cores (one copy per block, where the lanes of a lane group would
-//    otherwise each permute the same 16 bytes) and the block meets at one
-//    barrier; the activations come from L2 and arrive well before the weight
-//    stream, so the barrier costs little.
+//    cores (once per wave or block, where the lanes of a lane group would
+//    otherwise each permute the same 16 bytes). Each wave stages the slots
+//    of its own units in an area of its own and waits for those only,
+//    except for one row at 16 units per wave, where the block stages them
+//    and meets at one barrier. Activations come from L2, but a later wave's
+//    requests queue behind the earlier waves' weight words, so a block-wide
+//    barrier can wait long for the last wave's (4 us against 1.3 us for the
+//    first wave's at M = 8).
 //  * Each wave then runs its units as their words arrive (loads complete in
 //    order). The wave's units form GPW (1, 2 or 4) groups of equal size, a
 //    compile-time structure: no scalar bookkeeping per unit.
@@ -30,8 +34,8 @@ namespace {
 //    one more matrix-core product per unit to remove it. The waves' fp32
 //    results are summed through LDS in wave order and rounded once.
 // LDS: the staged activations (M * K / 32 * 4 slots of 16 bytes, in an area
-// of 4 slots per thread), later reused for the per-wave results
-// (WAVES * M * 16 * VEC floats); sized at launch, at most 64 KiB.
+// of 4 slots per thread, 256 per wave), later reused for the per-wave
+// results (WAVES * M * 16 * VEC floats); sized at launch, at most 64 KiB.
 constexpr int kWaveXPerThread = 4; // activation slots one thread stages at most
 
 // VEC consecutive halves of a row of scales or zero points, as loaded: a
@@ -109,11 +113,16 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_wave_kernel(GemvArgs g) {
   // activations arrive early starts its units while the other waves' still
   // come in (later waves' requests queue behind the earlier waves' weight
   // words).
-  constexpr bool OWN = !M1 && QMM_GEMV_WAVE_X;
+  // One row with fewer than 16 units per wave: the block-wide staging would
+  // leave the activation requests to the first waves only (one slot per
+  // thread), so the waves stage their own there too (measured faster; with
+  // 16 units per wave each wave's threads already hold its own slots, and
+  // the block's barrier measured faster than none).
+  constexpr bool OWN = QMM_GEMV_WAVE_X && (!M1 || UPW < 16);
   constexpr int WSLOTS = 64 * kWaveXPerThread;  // slots of a wave's own area
   constexpr int WROW = 4 * UPW;                 // a wave's slots per row: (m, c, j) at m WROW + 4 c + j
   const int xslots = OWN ? g.M * WROW : (M1 ? XROW : g.M * XROW);
-  const int xpt = M1 ? 1 : (OWN ? (xslots + 63) / 64 : (xslots + THREADS - 1) / THREADS);  // wave-uniform
+  const int xpt = OWN ? (xslots + 63) / 64 : (M1 ? 1 : (xslots + THREADS - 1) / THREADS);  // wave-uniform
   const int xbase = OWN ? wave * WSLOTS : 0;  // first slot of the thread's writes
   u32x4 xraw[kWaveXPerThread];
 #pragma unroll
