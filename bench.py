@@ -177,7 +177,7 @@ class Product:
     """One product's device inputs, rotated weight copies and launch functions."""
 
     def __init__(self, w, torch, datagen, M, K, N, bits, gs, seed, zero_range, scale_range, bf16=False,
-                 name=None):
+                 name=None, copies=None):
         self.w, self.torch = w, torch
         self.M, self.K, self.N, self.bits, self.gs, self.bf16 = M, K, N, bits, gs, bf16
         self.name = name or f"m{M}_k{K}_n{N}_int{bits}_g{gs}"
@@ -193,7 +193,7 @@ class Product:
             x, z0, s0 = (torch.from_numpy(d[k]).to(dev) for k in ("x", "zeros", "scales"))
         qw0, qlo0 = w.qmm_pack(torch.from_numpy(d["codes"]).to(dev), bits)
         per = qw0.nbytes + z0.nbytes + s0.nbytes + (0 if qlo0 is None else qlo0.nbytes)
-        self.R = max(1, math.ceil(COLD_BYTES / per))
+        self.R = max(1, math.ceil(COLD_BYTES / per)) if copies is None else copies
         self.copies = [(qw0, qlo0, z0, s0)] + [
             (qw0.clone(), None if qlo0 is None else qlo0.clone(), z0.clone(), s0.clone()) for _ in range(self.R - 1)]
         self.x = x
@@ -480,17 +480,20 @@ def copy_calibration(torch, mib: int):
           flush=True)
 
 
-def workload_product(w, torch, datagen, wl, bf16=False):
+def workload_product(w, torch, datagen, wl, bf16=False, copies=None):
     return Product(w, torch, datagen, wl.M, wl.K, wl.N, wl.bits, wl.group_size, wl.seed, wl.zero_range,
-                   wl.scale_range, bf16=bf16, name=wl.name)
+                   wl.scale_range, bf16=bf16, name=wl.name, copies=copies)
 
 
 def run_only(args, torch, datagen, w):
-    """A few cold launches of one workload (counters are read per dispatch)."""
+    """A few cold launches of one workload, for counters that are read per dispatch: one copy of the
+    weights, and a 640 MiB fill before each launch evicts it from the caches (few dispatches in all)."""
     wl = datagen.WORKLOADS[args.only]
-    p = workload_product(w, torch, datagen, wl)
+    p = workload_product(w, torch, datagen, wl, copies=1)
+    scrub = torch.empty(SCRUB_BYTES, dtype=torch.uint8, device="cuda:0")
     sp = torch.cuda.current_stream().cuda_stream
     for i in range(20):
+        scrub.zero_()
         p.launch(i, sp)
     torch.cuda.synchronize()
     print(json.dumps({"workload": wl.name, "launches": 20, "kernel": p.kernel_name(),
