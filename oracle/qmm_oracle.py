@@ -22,7 +22,10 @@ What it computes, step by step, in the order the sources state it:
   (GPTQModel-Compatible Triton Kernel README, "Dequantization Formula";
   dashq_kernel.py, ``dequantize_weight``.)
 * Product: ``y = x @ w`` with x of shape (M, K). (GPTQModel-Compatible Triton
-  Kernel README, "API Reference", ``gptqmodel_quantized_matmul``.) An optional
+  Kernel README, "API Reference", ``gptqmodel_quantized_matmul``.) ``matmul``
+  takes numpy's float64 product (a library primitive, for the sizes of the
+  workloads); ``matmul_triple_loop`` is the same sum written out as three
+  loops, and the pins hold the two together on small products. An optional
   bias row is added to every row of y (dashq_kernel.py, ``TritonQuantLinear``:
   the accumulator starts from the bias).
 * The dequantized weight as fp16 (dashq_kernel.py, ``dequantize_weight``): the
@@ -190,6 +193,30 @@ def matmul(x: np.ndarray, w: np.ndarray, bias: np.ndarray | None = None) -> tupl
     if bias is not None:
         b = np.asarray(bias).astype(np.float64).reshape(1, -1)
         y, a = y + b, a + np.abs(b)
+    return y, a
+
+
+def matmul_triple_loop(x: np.ndarray, w: np.ndarray, bias: np.ndarray | None = None) -> tuple[np.ndarray, np.ndarray]:
+    """The product written out as the definition reads: for every (m, n), the sum over k of
+    x[m, k] * w[k, n] in float64, k ascending (bias first when given), and the tolerance reference
+    a alongside. Plain Python loops, for small cases (the pins hold ``matmul`` to it)."""
+    x64 = np.asarray(x).astype(np.float64)
+    w64 = np.asarray(w, dtype=np.float64)
+    M, K = x64.shape
+    N = w64.shape[1]
+    b = None if bias is None else np.asarray(bias).astype(np.float64).reshape(-1)
+    y = np.zeros((M, N), dtype=np.float64)
+    a = np.zeros((M, N), dtype=np.float64)
+    xl, wl = x64.tolist(), w64.tolist()
+    for m in range(M):
+        for n in range(N):
+            acc = 0.0 if b is None else float(b[n])
+            aa = 0.0 if b is None else abs(float(b[n]))
+            for k in range(K):
+                t = xl[m][k] * wl[k][n]
+                acc += t
+                aa += abs(t)
+            y[m, n], a[m, n] = acc, aa
     return y, a
 
 

@@ -281,6 +281,26 @@ def check_rational_brute_force(seed=3):
                     assert abs(a[m, n] - float(ae[m][n])) <= tol, (bits, K, gs, m, n)
 
 
+def check_matmul_is_the_triple_loop(seed=13):
+    """numpy's float64 product against the sum written out as three loops (k ascending), on small
+    products with and without a bias, and on the whole small decode workload (1 x 512 x 256)."""
+    rng = np.random.default_rng(seed)
+    for M, K, N in ((1, 32, 8), (3, 96, 5), (2, 256, 17)):
+        x = rng.standard_normal((M, K)).astype(np.float16)
+        w = rng.standard_normal((K, N))
+        for bias in (None, rng.standard_normal(N).astype(np.float16)):
+            y, a = oracle.matmul(x, w, bias)
+            yl, al = oracle.matmul_triple_loop(x, w, bias)
+            assert np.all(np.abs(y - yl) <= 1e-12 * al), (M, K, N)
+            assert np.allclose(a, al, rtol=1e-12, atol=0)
+    wl = datagen.WORKLOADS["gemv_m1_k512_n256_int4_g128"]
+    d = datagen.generate(wl)
+    qw, qlo = oracle.pack(d["codes"], wl.bits)
+    y, a = oracle.quantized_matmul(d["x"], qw, qlo, d["zeros"], d["scales"], wl.bits, wl.group_size)
+    yl, al = oracle.matmul_triple_loop(d["x"], oracle.dequantize(d["codes"], d["scales"], d["zeros"], wl.group_size))
+    assert np.all(np.abs(y - yl) <= 1e-12 * al)
+
+
 def check_exact_integer_recomputation(seed=11):
     """K = 4096 products with integer zero points, recomputed exactly in int64.
 
@@ -542,7 +562,8 @@ CHECKS = [
     check_out_of_range_codes_masked, check_three_bit_identity, check_dequant_examples_hand_worked,
     check_dequant_fp16_hand_worked, check_dequant_fp16_against_exact_rounding, check_bias_row,
     check_bf16_decode_every_pattern, check_bf16_encode_hand_worked, check_bf16_encode_against_exact_rounding,
-    check_rational_brute_force, check_exact_integer_recomputation, check_closed_form_constant_scale_zero,
+    check_rational_brute_force, check_matmul_is_the_triple_loop, check_exact_integer_recomputation,
+    check_closed_form_constant_scale_zero,
     check_group_minus_one_is_single_group, check_widths_agree_on_small_codes, check_one_hot_rows,
     check_parity_rule, check_tolerance_covers_the_rounding_model,
     check_gptq_qzeros_hand_worked, check_gptq_3bit10_hand_worked, check_gptq_round_trips_and_padding,
