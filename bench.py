@@ -12,15 +12,18 @@ Protocol, the same for every product below:
     scales and zero points, and the copies together span at least 512 MiB
     (twice the 256 MB Infinity Cache), so each launch streams its weights
     from HBM.
-  * Time per step: the timed launches are captured into one HIP graph (one
-    kernel node per step). The graph is replayed once untimed, a 640 MiB fill
-    then evicts every cache, a sleep kernel keeps the GPU busy while the host
-    records the start event and launches the graph, and events on the launch
-    stream bracket the replay: the average launch duration over the timed
-    region, which includes each node's dispatch but no host overhead (a
-    rocprofv3 kernel trace of the same nodes reports the same durations, to
-    about 1 %). `roofline.achieved` is the algorithmic bytes (or flops) of
-    one launch over it.
+  * Time per step: the timed launches run back to back as kernel nodes of one
+    HIP graph, behind a lead-in of the same launch on a copy of its own (about
+    300 us, so that they start on a busy GPU at its working clocks). That graph
+    and one of the lead-in alone are each replayed after a 640 MiB fill that
+    evicts every cache, between events on the launch stream; their difference
+    is the time of exactly the timed launches, free of the fixed cost of a
+    graph launch (~10 us, which would otherwise weigh on short runs): the
+    average launch duration over the timed region, each node's dispatch
+    included, no host overhead (a rocprofv3 kernel trace of the same nodes
+    reports the same durations, to a few %). Median of three.
+    `roofline.achieved` is the algorithmic bytes (or flops) of one launch
+    over it.
   * Floors: a plain streaming read of the same byte count, cold, timed the
     same way (best of a few launch shapes), an empty kernel, and a dense
     MFMA loop.
@@ -62,6 +65,7 @@ COLD_BYTES = 512 * 1024 * 1024  # twice the Infinity Cache
 SCRUB_BYTES = 640 * 1024 * 1024
 METRIC = "M=1 GEMV achieved HBM GB/s (% of peak); M=2048 GEMM TOPS (% MFMA peak)"
 GEMV_STEPS = 200
+LEAD_MAX_NODES, LEAD_US = 64, 300.0  # lead-in before the timed launches
 GEMM_STEPS, GEMM_WARMUP = 40, 100
 CSRC = os.path.join(ROOT, "weight_only_group_amd", "csrc")
 
@@ -139,36 +143,54 @@ class Clock:
     def __init__(self, torch):
         self.torch = torch
         self.scrub = torch.empty(SCRUB_BYTES, dtype=torch.uint8, device="cuda:0")
-        # cycles of torch's sleep kernel per microsecond, measured once
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda._sleep(100000)
-        e0.record()
-        torch.cuda._sleep(2000000)
-        e1.record()
-        torch.cuda.synchronize()
-        self.cycles_per_us = 2000000 / max(e0.elapsed_time(e1) * 1e3, 1.0)
-
-    def busy(self, us: float):
-        self.torch.cuda._sleep(int(us * self.cycles_per_us))
 
     def per_step_us(self, launch, steps: int, first: int = 0) -> float:
-        """`launch(i, stream)` for i in [first, first + steps) as one graph; time per node."""
+        """`launch(i, stream)` for i in [first, first + steps), back to back: time per launch.
+
+        The timed launches run in one graph behind a lead-in of the same launch on a copy of
+        its own (`launch(-1, stream)`, about LEAD_US long), so that they start on a busy GPU at
+        its working clocks. That graph and one of the lead-in alone are each replayed after a
+        640 MiB fill that evicts the caches, between events on the launch stream; the
+        difference of the two is the time of exactly `steps` launches, free of the fixed cost of
+        a graph launch (which would otherwise weigh on short runs). Median of three."""
         torch = self.torch
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            sp = torch.cuda.current_stream().cuda_stream
-            for i in range(first, first + steps):
-                launch(i, sp)
-        g.replay()  # untimed: the first replay of a graph carries one-time work
-        self.scrub.zero_()  # evict what that replay left in the caches
+        sp = torch.cuda.current_stream().cuda_stream
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        self.busy(400)
+        launch(-1, sp)
         e0.record()
-        g.replay()
+        for _ in range(3):
+            launch(-1, sp)
         e1.record()
         torch.cuda.synchronize()
-        del g
-        return e0.elapsed_time(e1) * 1e3 / steps
+        rough = max(e0.elapsed_time(e1) * 1e3 / 3, 0.5)
+        nlead = max(2, min(LEAD_MAX_NODES, math.ceil(LEAD_US / rough)))
+
+        def capture(n_timed):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                s_ = torch.cuda.current_stream().cuda_stream
+                for _ in range(nlead):
+                    launch(-1, s_)
+                for i in range(first, first + n_timed):
+                    launch(i, s_)
+            return g
+
+        full, lead = capture(steps), capture(0)
+        full.replay()  # untimed: the first replay of a graph carries one-time work
+        lead.replay()
+        torch.cuda.synchronize()
+
+        def timed(g):
+            self.scrub.zero_()
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3
+
+        diffs = sorted((timed(full) - timed(lead)) / steps for _ in range(3))
+        del full, lead
+        return diffs[1]
 
 
 # ------------------------------------------------------------------ products
@@ -196,6 +218,8 @@ class Product:
         self.R = max(1, math.ceil(COLD_BYTES / per)) if copies is None else copies
         self.copies = [(qw0, qlo0, z0, s0)] + [
             (qw0.clone(), None if qlo0 is None else qlo0.clone(), z0.clone(), s0.clone()) for _ in range(self.R - 1)]
+        # a copy of its own for the lead-in launches before a timed replay
+        self.lead = (qw0.clone(), None if qlo0 is None else qlo0.clone(), z0.clone(), s0.clone())
         self.x = x
         self.y = torch.empty((M, N), dtype=x.dtype, device=dev)
         self.gemv = M <= 16
@@ -214,7 +238,7 @@ class Product:
         self.flops = 2.0 * M * K * N
 
     def launch(self, i: int, sp: int):
-        qw, qlo, z, s = self.copies[i % self.R]
+        qw, qlo, z, s = self.lead if i < 0 else self.copies[i % self.R]
         args = [self.x.data_ptr(), self.M, self.K, qw.data_ptr(), None if qlo is None else qlo.data_ptr(),
                 z.data_ptr(), s.data_ptr(), None, self.N, self.bits, self.gs, self.y.data_ptr()]
         if self.gemv:
@@ -235,6 +259,7 @@ class Product:
 
     def free(self):
         self.copies = None
+        self.lead = None
         self.torch.cuda.empty_cache()
 
 
@@ -550,8 +575,9 @@ def run(args, torch, datagen, w):
             "workload": head_wl.name, "M": head_wl.M, "K": head_wl.K, "N": head_wl.N, "bits": head_wl.bits,
             "group_size": head_wl.group_size, "seed": head_wl.seed, "weight_copies_rotated": head.R,
             "algorithmic_bytes_per_step": head.bytes, "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
-            "timing": "one HIP graph replay of the timed steps behind a sleep kernel, events around it; cold "
-                      "weights (rotated copies over 512 MiB, caches evicted before the replay)",
+            "timing": "the timed steps as graph nodes behind a lead-in, minus the lead-in alone, events on the "
+                      "launch stream, median of three; cold weights (rotated copies over 512 MiB, caches evicted "
+                      "before each replay)",
             "plan": head.plan,
         },
         "roofline": {
@@ -559,8 +585,8 @@ def run(args, torch, datagen, w):
             "frac": round(ach / HBM_PEAK_GBS, 4),
             "traffic": committed_traffic(head_wl.name, "gemv", head_wl.bits),
             "kernel": head.kernel_name(), "us_per_launch": round(h_step, 3),
-            "duration_from": "events on the launch stream around the timed graph replay (one kernel node per "
-                             "step), divided by the steps",
+            "duration_from": "events on the launch stream around the graph replays (one kernel node per step; "
+                             "the replay with the timed steps minus the one without), divided by the steps",
         },
         "configs": configs,
     }
