@@ -139,20 +139,31 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_wave_kernel(GemvArgs g) {
       }
     }
   }
+  // Scales and zero points of the wave's groups. With several rows and
+  // several groups, lane group j requests those of group slot j % GPW only
+  // and the lanes exchange them after the staging (a cross-lane permute per
+  // value): two small requests per lane instead of 2 GPW, each a separate
+  // trip to memory (measured faster there, slower for one row). The zero
+  // points a lane requests for itself are the ones it checks for the exact
+  // one-operation dequantization (VEC values per lane instead of GPW * VEC).
+  constexpr bool SHARE = QMM_GEMV_SZ_SHARE && GPW > 1 && !M1;
   HT sraw[GPW][HW], zraw[GPW][HW];
-#pragma unroll
-  for (int gi = 0; gi < GPW; ++gi) {
-    const uint32_t off = ((uint32_t)(g0 + gi) * (uint32_t)g.N + (uint32_t)ncc) * 2u;
-    load_halves<VEC>(rs, off, sraw[gi]);
-    load_halves<VEC>(rz, off, zraw[gi]);
-  }
-  // The zero points checked for the exact one-operation dequantization: lane
-  // group j takes group slot j (its own copy, so that each lane checks VEC
-  // values instead of GPW * VEC).
-  HT zchk[HW];
-  if constexpr (!BF) {
-    const uint32_t off = ((uint32_t)(g0 + (j < GPW ? j : GPW - 1)) * (uint32_t)g.N + (uint32_t)ncc) * 2u;
+  HT sown[HW], zchk[HW];
+  if constexpr (SHARE) {
+    const uint32_t off = ((uint32_t)(g0 + (j & (GPW - 1))) * (uint32_t)g.N + (uint32_t)ncc) * 2u;
+    load_halves<VEC>(rs, off, sown);
     load_halves<VEC>(rz, off, zchk);
+  } else {
+#pragma unroll
+    for (int gi = 0; gi < GPW; ++gi) {
+      const uint32_t off = ((uint32_t)(g0 + gi) * (uint32_t)g.N + (uint32_t)ncc) * 2u;
+      load_halves<VEC>(rs, off, sraw[gi]);
+      load_halves<VEC>(rz, off, zraw[gi]);
+    }
+    if constexpr (!BF) {
+      const uint32_t off = ((uint32_t)(g0 + (j < GPW ? j : GPW - 1)) * (uint32_t)g.N + (uint32_t)ncc) * 2u;
+      load_halves<VEC>(rz, off, zchk);
+    }
   }
   uint32_t woff[NW];
 #pragma unroll
@@ -187,6 +198,18 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_wave_kernel(GemvArgs g) {
   // which come from HBM) may be scheduled above this point: the wait here
   // should be for the activations only, which come from L2.
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (SHARE) {
+    // group slot gi of column cl: from lane cl of lane group gi
+#pragma unroll
+    for (int gi = 0; gi < GPW; ++gi) {
+      const int src = ((lane & 15) | (gi << 4)) << 2;
+#pragma unroll
+      for (int h = 0; h < HW; ++h) {
+        sraw[gi][h] = (HT)__builtin_amdgcn_ds_bpermute(src, (int)sown[h]);
+        zraw[gi][h] = (HT)__builtin_amdgcn_ds_bpermute(src, (int)zchk[h]);
+      }
+    }
+  }
 
   // ---- 3. the wave's units, group by group (static).
   // fp16 data: per pair class, c = -(1024 2^-e + z) rounded to fp16; one
