@@ -3,7 +3,10 @@
 
 One step is one decode product y = x @ dequant(W) at M=1, K=4096, N=4096,
 4-bit codes, group size 128 (one transformer projection), on seeded synthetic
-inputs already resident in HBM. `value` is the achieved HBM bandwidth in GB/s
+inputs already resident in HBM, the packed words in the library's load-time
+layout (16-column strips: the same words, reordered once by qmm_to_strips so
+that each block streams its strip in order; the K-major time of the same
+workload is reported beside it). `value` is the achieved HBM bandwidth in GB/s
 of the K timed steps: the algorithmic bytes of a step (packed words, scales,
 zero points, x and y) over the time per step.
 
@@ -33,10 +36,11 @@ The JSON line holds the headline (`value`, exactly --steps steps after
 of steps independent of --steps (200 per decode product, 40 per prefill
 product after 100 untimed launches, past a clock transient of back-to-back
 prefill launches):
-  configs[*]    per workload: time per step, GB/s and TFLOP/s, the roofline of
-                its kernel (traffic from the committed counter summary of that
-                kernel source, else null), the streaming-read floor of its
-                bytes, and the launch plan
+  configs[*]    per workload (weights K-major, as packed): time per step, GB/s
+                and TFLOP/s, the roofline of its kernel (traffic from the
+                committed counter summary of that kernel source, else null),
+                the streaming-read floor of its bytes, and the launch plan
+  strips[*]     the same workloads with the weights in 16-column strips
   gemm_int4_g128  the prefill shape again with 4-bit codes in groups of 128
   bf16          the headline decode and the prefill products with bf16 data
   readme_shapes the prefill kernel at the README's benchmark shapes (4-bit g128)
@@ -199,10 +203,11 @@ class Product:
     """One product's device inputs, rotated weight copies and launch functions."""
 
     def __init__(self, w, torch, datagen, M, K, N, bits, gs, seed, zero_range, scale_range, bf16=False,
-                 name=None, copies=None):
+                 name=None, copies=None, strips=False):
         self.w, self.torch = w, torch
         self.M, self.K, self.N, self.bits, self.gs, self.bf16 = M, K, N, bits, gs, bf16
-        self.name = name or f"m{M}_k{K}_n{N}_int{bits}_g{gs}"
+        self.strips = strips
+        self.name = (name or f"m{M}_k{K}_n{N}_int{bits}_g{gs}") + ("_strips" if strips else "")
         dev = torch.device("cuda:0")
         wl = datagen.Workload(self.name, M, K, N, bits, gs, zero_range, scale_range, seed)
         d = datagen.generate(wl)
@@ -220,12 +225,19 @@ class Product:
             (qw0.clone(), None if qlo0 is None else qlo0.clone(), z0.clone(), s0.clone()) for _ in range(self.R - 1)]
         # a copy of its own for the lead-in launches before a timed replay
         self.lead = (qw0.clone(), None if qlo0 is None else qlo0.clone(), z0.clone(), s0.clone())
+        if strips:  # the load-time re-layout of every copy into 16-column strips
+            conv = lambda t: None if t is None else w.qmm_to_strips(t)
+            self.copies = [(conv(a), conv(b), c, e) for a, b, c, e in self.copies]
+            self.lead = (conv(self.lead[0]), conv(self.lead[1]), self.lead[2], self.lead[3])
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
         self.x = x
         self.y = torch.empty((M, N), dtype=x.dtype, device=dev)
         self.gemv = M <= 16
         lib = w.library()
         self.lib = lib
-        sfx = "_bf16" if bf16 else ""
+        sfx = "_ex" if strips else ("_bf16" if bf16 else "")
+        self.flags = ((w.QMM_BF16 if bf16 else 0) | w.QMM_STRIPS) if strips else None
         if self.gemv:
             nb = w.workspace_bytes(M, K, N, bits, gs)
             self.ws = torch.zeros(max(nb, 16), dtype=torch.uint8, device=dev)
@@ -240,7 +252,10 @@ class Product:
     def launch(self, i: int, sp: int):
         qw, qlo, z, s = self.lead if i < 0 else self.copies[i % self.R]
         args = [self.x.data_ptr(), self.M, self.K, qw.data_ptr(), None if qlo is None else qlo.data_ptr(),
-                z.data_ptr(), s.data_ptr(), None, self.N, self.bits, self.gs, self.y.data_ptr()]
+                z.data_ptr(), s.data_ptr(), None, self.N, self.bits, self.gs]
+        if self.flags is not None:
+            args.append(self.flags)
+        args.append(self.y.data_ptr())
         if self.gemv:
             args += [self.ws.data_ptr(), self.ws.numel()]
         st = self.fn(*args, sp)
@@ -310,7 +325,8 @@ def probes_library():
 def product_entry(prod: Product, steps: int, step_us: float, floor):
     kind = "gemv" if prod.gemv else "gemm"
     e = {
-        "workload": prod.name, "path": "qmm_gemv" if prod.gemv else "qmm_gemm",
+        "workload": prod.name, "path": ("qmm_gemv" if prod.gemv else "qmm_gemm") + ("_ex" if prod.strips else ""),
+        "weight_layout": "16-column strips" if prod.strips else "K-major",
         "M": prod.M, "K": prod.K, "N": prod.N, "bits": prod.bits, "group_size": prod.gs,
         "dtype": "bf16" if prod.bf16 else "f16", "steps": steps, "weight_copies_rotated": prod.R,
         "algorithmic_bytes": prod.bytes, "flops": prod.flops,
@@ -464,6 +480,7 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="only the five workloads and the headline")
     ap.add_argument("--only", default=None, metavar="WORKLOAD",
                     help="a few launches of one workload's product, its own short line (for counter profiles)")
+    ap.add_argument("--strips", action="store_true", help="with --only: the weights in 16-column strips")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the products, 4 plain device copies of MIB MiB each (outside every timed region), "
                          "so that a counter profile can scale FETCH_SIZE / WRITE_SIZE by a copy of known size")
@@ -505,23 +522,23 @@ def copy_calibration(torch, mib: int):
           flush=True)
 
 
-def workload_product(w, torch, datagen, wl, bf16=False, copies=None):
+def workload_product(w, torch, datagen, wl, bf16=False, copies=None, strips=False):
     return Product(w, torch, datagen, wl.M, wl.K, wl.N, wl.bits, wl.group_size, wl.seed, wl.zero_range,
-                   wl.scale_range, bf16=bf16, name=wl.name, copies=copies)
+                   wl.scale_range, bf16=bf16, name=wl.name, copies=copies, strips=strips)
 
 
 def run_only(args, torch, datagen, w):
     """A few cold launches of one workload, for counters that are read per dispatch: one copy of the
     weights, and a 640 MiB fill before each launch evicts it from the caches (few dispatches in all)."""
     wl = datagen.WORKLOADS[args.only]
-    p = workload_product(w, torch, datagen, wl, copies=1)
+    p = workload_product(w, torch, datagen, wl, copies=1, strips=args.strips)
     scrub = torch.empty(SCRUB_BYTES, dtype=torch.uint8, device="cuda:0")
     sp = torch.cuda.current_stream().cuda_stream
     for i in range(20):
         scrub.zero_()
         p.launch(i, sp)
     torch.cuda.synchronize()
-    print(json.dumps({"workload": wl.name, "launches": 20, "kernel": p.kernel_name(),
+    print(json.dumps({"workload": p.name, "launches": 20, "kernel": p.kernel_name(),
                       "algorithmic_bytes": p.bytes}), flush=True)
     p.free()
 
@@ -531,8 +548,9 @@ def run(args, torch, datagen, w):
     probes = probes_library()
     head_wl = datagen.WORKLOADS[datagen.HEADLINE_GEMV]
 
-    # the headline: exactly --steps steps after --warmup untimed ones
-    head = workload_product(w, torch, datagen, head_wl)
+    # the headline: exactly --steps steps after --warmup untimed ones, the
+    # weights in the decode product's load-time layout (16-column strips)
+    head = workload_product(w, torch, datagen, head_wl, strips=True)
     say(f"headline {head.name}: {args.steps} steps after {args.warmup}")
     h_step = measure(clock, head, args.steps, args.warmup)
     head_d = head.d
@@ -554,6 +572,18 @@ def run(args, torch, datagen, w):
         say(f"{name}: {step_us:.3f} us per launch, streaming-read floor {floor['us']:.3f} us, "
             f"frac {e['roofline']['frac']}")
         configs.append(e)
+        p.free()
+
+    # the same workloads with their weights re-laid out into 16-column strips
+    # at load time (the same words: qmm_gemv_ex / qmm_gemm_ex with QMM_STRIPS)
+    strips = []
+    for name, wl in datagen.WORKLOADS.items():
+        p = workload_product(w, torch, datagen, wl, strips=True)
+        steps, warm = (GEMV_STEPS, 20) if p.gemv else (GEMM_STEPS, GEMM_WARMUP)
+        step_us = measure(clock, p, steps, warm)
+        e = product_entry(p, steps, step_us, None)
+        say(f"{p.name}: {step_us:.3f} us per launch, frac {e['roofline']['frac']}")
+        strips.append(e)
         p.free()
 
     value = head.bytes / h_step / 1e3
@@ -579,16 +609,20 @@ def run(args, torch, datagen, w):
                       "launch stream, median of three; cold weights (rotated copies over 512 MiB, caches evicted "
                       "before each replay)",
             "plan": head.plan,
+            "weight_layout": "16-column strips (qmm_to_strips once at load time; the same packed words, "
+                             "qmm_gemv_ex with QMM_STRIPS)",
+            "k_major_us_per_launch": next(e["us_per_launch"] for e in configs if e["workload"] == head_wl.name),
         },
         "roofline": {
             "bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(ach / HBM_PEAK_GBS, 4),
-            "traffic": committed_traffic(head_wl.name, "gemv", head_wl.bits),
+            "traffic": committed_traffic(head.name, "gemv", head_wl.bits),
             "kernel": head.kernel_name(), "us_per_launch": round(h_step, 3),
             "duration_from": "events on the launch stream around the graph replays (one kernel node per step; "
                              "the replay with the timed steps minus the one without), divided by the steps",
         },
         "configs": configs,
+        "strips": strips,
     }
     if not args.no_extras:
         c5 = datagen.WORKLOADS[datagen.HEADLINE_GEMM]

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define QMM_ABI_VERSION 4
+#define QMM_ABI_VERSION 5
 
 typedef enum qmm_status {
   QMM_OK = 0,
@@ -58,7 +58,8 @@ typedef enum qmm_status {
   QMM_ERR_GROUP = 4,     /* group_size neither -1 nor a positive multiple of 32 dividing K */
   QMM_ERR_ALIGN = 5,     /* a pointer is not aligned as its argument requires        */
   QMM_ERR_WORKSPACE = 6, /* workspace missing or smaller than qmm_workspace_bytes() */
-  QMM_ERR_HIP = 7        /* the HIP runtime reported an error                       */
+  QMM_ERR_HIP = 7,       /* the HIP runtime reported an error                       */
+  QMM_ERR_FLAGS = 8      /* a flags argument has bits other than QMM_BF16 | QMM_STRIPS */
 } qmm_status;
 
 /* QMM_ABI_VERSION of the built library. */
@@ -246,6 +247,67 @@ qmm_status qmm_gemm_bf16(const uint16_t* x, int M, int K,
                          const uint16_t* zeros, const uint16_t* scales, const uint16_t* bias,
                          int N, int bits, int group_size,
                          uint16_t* y, hipStream_t stream);
+
+/*
+ * 16-column strip-major weights. The products read a plane of packed words
+ * (rows x N int32: qweight, and qweight_lo for 3 bits) one column strip at a
+ * time; the decode product gives each block 16 columns over all of K. In the
+ * K-major layout above such a strip is a 64-byte piece of every word row;
+ * qmm_to_strips reorders a plane once, at load time, so that every 16-column
+ * strip is one contiguous run:
+ *   word (r, n) of the plane at index ((n / 16) * rows + r) * 16 + n % 16,
+ * a (ceil(N / 16), rows, 16) int32 array whose columns past N (in the last
+ * strip, when N % 16 != 0) are zero. The words are the same (a permutation),
+ * so the products return the same bits from either layout. Not a layout of
+ * the pages: the packing they define (K-major words) stays the input format;
+ * this is a storage order of the same words for the decode product's reads
+ * (a strip is then streamed in order; 4096 x 4096 at 4 bits: ~8% less time).
+ * qmm_gemv_ex / qmm_gemm_ex take it with QMM_STRIPS; qmm_dequant, qmm_unpack
+ * and qmm_gemv_noalloc take the K-major layout only.
+ */
+
+/* Bytes of a plane of `rows` word rows and N columns in strip-major order:
+ * rows * ceil(N / 16) * 16 * 4; 0 if rows < 1, N < 1 or the plane would
+ * reach 4 GiB. */
+size_t qmm_strips_bytes(int rows, int N);
+
+/*
+ * qmm_to_strips -- K-major plane -> strip-major plane.
+ *   words   (rows, N) int32, e.g. qweight as written by qmm_pack (rows = K / eps;
+ *           for 3 bits qweight has K / 16 rows and qweight_lo K / 32)
+ *   strips  qmm_strips_bytes(rows, N) bytes, written completely
+ * qmm_from_strips is the inverse (the padding columns are dropped).
+ * Requirements: rows, N >= 1 and the strip-major plane below 4 GiB
+ * (QMM_ERR_SHAPE); both pointers non-NULL (QMM_ERR_NULL) and 4-byte aligned
+ * (QMM_ERR_ALIGN); the two planes must not overlap.
+ */
+qmm_status qmm_to_strips(const int32_t* words, int rows, int N, int32_t* strips, hipStream_t stream);
+qmm_status qmm_from_strips(const int32_t* strips, int rows, int N, int32_t* words, hipStream_t stream);
+
+/* Flags of the _ex products. */
+#define QMM_BF16 1u   /* x, zeros, scales, bias and y are bf16 (as the _bf16 entry points) */
+#define QMM_STRIPS 2u /* qweight and qweight_lo are in the strip-major layout (qmm_to_strips) */
+
+/*
+ * qmm_gemv_ex, qmm_gemm_ex -- qmm_gemv and qmm_gemm with a flags argument
+ * (QMM_BF16, QMM_STRIPS, or both; other bits: QMM_ERR_FLAGS). With flags 0
+ * they are qmm_gemv and qmm_gemm, with QMM_BF16 qmm_gemv_bf16 and
+ * qmm_gemm_bf16. With QMM_STRIPS each packed plane is read in the
+ * strip-major layout, which must hold below 4 GiB (QMM_ERR_SHAPE); every
+ * other argument, requirement and result is as for the K-major call, and the
+ * workspace is the same (qmm_workspace_bytes).
+ */
+qmm_status qmm_gemv_ex(const uint16_t* x, int M, int K,
+                       const int32_t* qweight, const int32_t* qweight_lo,
+                       const uint16_t* zeros, const uint16_t* scales, const uint16_t* bias,
+                       int N, int bits, int group_size, unsigned flags,
+                       uint16_t* y, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+qmm_status qmm_gemm_ex(const uint16_t* x, int M, int K,
+                       const int32_t* qweight, const int32_t* qweight_lo,
+                       const uint16_t* zeros, const uint16_t* scales, const uint16_t* bias,
+                       int N, int bits, int group_size, unsigned flags,
+                       uint16_t* y, hipStream_t stream);
 
 /*
  * GPTQModel-format inputs. GPTQModel-Compatible Triton Kernel README, "API

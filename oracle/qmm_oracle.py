@@ -45,6 +45,13 @@ exactly; for the workloads' integer zero points every product ``x * w`` is exact
 in float64, so the only rounding is in the K-term sums (relative error about
 K * 2**-53). The matrix product uses numpy's float64 matmul as a library step.
 
+* The 16-column strip-major order of a word plane (a storage order of the
+  library, not of the pages: the same words, reordered once at load time so
+  that each 16-column strip is contiguous): word ``(r, n)`` of a (rows, N)
+  plane goes to ``[n // 16, r, n % 16]`` of a (ceil(N / 16), rows, 16) array,
+  the last strip's columns past N zero. ``to_strips`` / ``from_strips`` write
+  that definition out element by element.
+
 Parity pins: every function here is pinned by CPU tests (hand-worked words and
 products from the definitions, exact integer and rational recomputation,
 invariants). The GPTQModel-format functions at the end (packed zero points,
@@ -325,6 +332,27 @@ def parity_report(y_dev: np.ndarray, y_ref: np.ndarray, a: np.ndarray, rel_tol: 
 #    ("Dequantization Formula").
 
 GPTQ_BITS = (2, 3, 4, 8)
+
+
+STRIP_COLS = 16
+
+
+def to_strips(words: np.ndarray) -> np.ndarray:
+    """(rows, N) word plane -> (ceil(N / 16), rows, 16): word (r, n) at [n // 16, r, n % 16], zero padding."""
+    rows, N = words.shape
+    out = np.zeros(((N + STRIP_COLS - 1) // STRIP_COLS, rows, STRIP_COLS), dtype=words.dtype)
+    for n in range(N):
+        out[n // STRIP_COLS, :, n % STRIP_COLS] = words[:, n]
+    return out
+
+
+def from_strips(strips: np.ndarray, N: int) -> np.ndarray:
+    """Inverse of ``to_strips``: (ceil(N / 16), rows, 16) -> (rows, N)."""
+    rows = strips.shape[1]
+    out = np.empty((rows, N), dtype=strips.dtype)
+    for n in range(N):
+        out[:, n] = strips[n // STRIP_COLS, :, n % STRIP_COLS]
+    return out
 
 
 def gptq_values_per_word(bits: int) -> int:

@@ -82,6 +82,25 @@ static void products(void) {
   }
   EXPECT(qmm_gemv_noalloc(x, 1, 256, qw, qw, z, z, nullptr, 64, 5, 128, y, nullptr), QMM_ERR_BITS);
   EXPECT(qmm_gemv_noalloc(x, 1, 256, qw, qw, z, z, nullptr, 64, 4, 128, nullptr, nullptr), QMM_ERR_NULL);
+
+  // The flags entry points: unknown bits first, then the checks of the plain calls.
+  for (unsigned fl : {4u, 8u, 0x80000000u, 0xffffffffu}) {
+    EXPECT(qmm_gemv_ex(x, 1, 256, qw, qw, z, z, nullptr, 64, 4, 128, fl, y, A, 1 << 30, nullptr), QMM_ERR_FLAGS);
+    EXPECT(qmm_gemm_ex(x, 300, 256, qw, qw, z, z, nullptr, 64, 4, 128, fl, y, nullptr), QMM_ERR_FLAGS);
+  }
+  for (unsigned fl : {0u, QMM_BF16, QMM_STRIPS, QMM_BF16 | QMM_STRIPS}) {
+    EXPECT(qmm_gemv_ex(x, 1, 256, qw, qw, z, z, nullptr, 64, 5, 128, fl, y, A, 1 << 30, nullptr), QMM_ERR_BITS);
+    EXPECT(qmm_gemv_ex(x, 17, 256, qw, qw, z, z, nullptr, 64, 4, 128, fl, y, A, 1 << 30, nullptr), QMM_ERR_SHAPE);
+    EXPECT(qmm_gemv_ex(x, 1, 256, qw, qw, z, z, nullptr, 64, 4, 128, fl, nullptr, A, 1 << 30, nullptr), QMM_ERR_NULL);
+    EXPECT(qmm_gemv_ex(x, 1, 8192, qw, qw, z, z, nullptr, 64, 4, 128, fl, y, nullptr, 0, nullptr), QMM_ERR_WORKSPACE);
+    EXPECT(qmm_gemm_ex(x, 300, 256, qw, qw, z, z, nullptr, 64, 4, 0, fl, y, nullptr), QMM_ERR_GROUP);
+    EXPECT(qmm_gemm_ex(x, 300, 256, qw, qw, PM(const uint16_t), z, nullptr, 64, 4, 128, fl, y, nullptr), QMM_ERR_ALIGN);
+  }
+  // A plane that fits K-major (K * N bytes < 4 GiB) but not once N = 8 is
+  // padded to a 16-column strip.
+  EXPECT(qmm_gemm_ex(x, 1, 1 << 28, qw, qw, z, z, nullptr, 8, 8, -1, QMM_STRIPS, y, nullptr), QMM_ERR_SHAPE);
+  EXPECT(qmm_gemv_ex(x, 1, 1 << 28, qw, qw, z, z, nullptr, 8, 8, -1, QMM_STRIPS, y, A, 1 << 30, nullptr),
+         QMM_ERR_SHAPE);
 }
 
 static void conversions(void) {
@@ -104,6 +123,17 @@ static void conversions(void) {
   EXPECT(qmm_repack_3bit10(qw, 48, 64, qw, qw, nullptr), QMM_ERR_SHAPE);
   EXPECT(qmm_repack_3bit10(qw, INT_MAX - 31, INT_MAX, qw, qw, nullptr), QMM_ERR_SHAPE);
   EXPECT(qmm_repack_3bit10(qw, 64, 64, qw, nullptr, nullptr), QMM_ERR_NULL);
+  int32_t* st = P(int32_t);
+  for (int dir = 0; dir < 2; ++dir) {
+    auto f = dir == 0 ? qmm_to_strips : qmm_from_strips;
+    EXPECT(f(qw, 0, 64, st, nullptr), QMM_ERR_SHAPE);
+    EXPECT(f(qw, 16, INT_MIN, st, nullptr), QMM_ERR_SHAPE);
+    EXPECT(f(qw, INT_MAX, INT_MAX, st, nullptr), QMM_ERR_SHAPE);
+    EXPECT(f(qw, 1 << 26, 24, st, nullptr), QMM_ERR_SHAPE);  // 2^26 * 32 * 4 bytes = 8 GiB
+    EXPECT(f(nullptr, 16, 64, st, nullptr), QMM_ERR_NULL);
+    EXPECT(f(qw, 16, 64, nullptr, nullptr), QMM_ERR_NULL);
+    EXPECT(f(qw, 16, 64, (int32_t*)((char*)A + 2), nullptr), QMM_ERR_ALIGN);
+  }
 }
 
 static void queries(void) {
@@ -149,6 +179,17 @@ static void queries(void) {
   EXPECT(qmm_gemm_plan_info(2048, 4096, 14336, 8, -1, nullptr, 7), QMM_ERR_NULL);
   EXPECT(qmm_gemv_plan_info(1, 4096, 4096, 4, 128, info, 9), QMM_OK);
   EXPECT(qmm_gemm_plan_info(2048, 4096, 14336, 8, -1, info, 7), QMM_OK);
+  const int rws[] = {INT_MIN, -1, 0, 1, 2, 255, 1 << 20, 1 << 26, INT_MAX};
+  const int cols[] = {INT_MIN, -1, 0, 1, 8, 15, 16, 17, 4104, 1 << 20, INT_MAX - 14, INT_MAX};
+  for (int r : rws)
+    for (int c : cols) {
+      const size_t b = qmm_strips_bytes(r, c);
+      const bool fits = r >= 1 && c >= 1 && (unsigned long long)r * ((c + 15ull) / 16 * 16) * 4 < (1ull << 32);
+      if (fits != (b > 0) || (fits && b != (size_t)r * ((c + 15ull) / 16 * 16) * 4)) {
+        fprintf(stderr, "strips bytes %d %d: %zu\n", r, c, b);
+        ++failures;
+      }
+    }
   printf("workspace bytes summed over the sweep: %zu\n", total);
 }
 

@@ -34,7 +34,8 @@ def test_header_declares_the_boundary():
         ["qmm_abi_version", "qmm_status_string", "qmm_last_error", "qmm_pack", "qmm_unpack", "qmm_dequant",
          "qmm_workspace_bytes", "qmm_gemv", "qmm_gemm", "qmm_dequant_bf16", "qmm_gemv_bf16", "qmm_gemm_bf16",
          "qmm_unpack_qzeros", "qmm_unpack_qzeros_bf16", "qmm_repack_3bit10", "qmm_gemv_noalloc",
-         "qmm_gemv_plan_info", "qmm_gemm_plan_info"])
+         "qmm_gemv_plan_info", "qmm_gemm_plan_info", "qmm_strips_bytes", "qmm_to_strips", "qmm_from_strips",
+         "qmm_gemv_ex", "qmm_gemm_ex"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -51,10 +52,10 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = _lib()
-    assert lib.qmm_abi_version() == 4
-    names = [lib.qmm_status_string(i).decode() for i in range(8)]
+    assert lib.qmm_abi_version() == 5
+    names = [lib.qmm_status_string(i).decode() for i in range(9)]
     assert names == ["QMM_OK", "QMM_ERR_NULL", "QMM_ERR_BITS", "QMM_ERR_SHAPE", "QMM_ERR_GROUP",
-                     "QMM_ERR_ALIGN", "QMM_ERR_WORKSPACE", "QMM_ERR_HIP"]
+                     "QMM_ERR_ALIGN", "QMM_ERR_WORKSPACE", "QMM_ERR_HIP", "QMM_ERR_FLAGS"]
     assert lib.qmm_status_string(99).decode() == "QMM_ERR_UNKNOWN"
 
 

@@ -557,7 +557,43 @@ def check_gptq_product_hand_worked():
     assert used >= 5
 
 
+def check_strips_hand_worked():
+    # A (2, 24) plane with word (r, n) = 100 r + n, laid out by hand: strip 0
+    # holds columns 0-15 of row 0, then of row 1; strip 1 holds columns 16-23
+    # of each row followed by 8 zero words of padding.
+    words = np.array([[100 * r + n for n in range(24)] for r in range(2)], dtype=np.int32)
+    want = np.array([
+        [[0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15],
+         [100, 101, 102, 103, 104, 105, 106, 107, 108, 109, 110, 111, 112, 113, 114, 115]],
+        [[16, 17, 18, 19, 20, 21, 22, 23, 0, 0, 0, 0, 0, 0, 0, 0],
+         [116, 117, 118, 119, 120, 121, 122, 123, 0, 0, 0, 0, 0, 0, 0, 0]],
+    ], dtype=np.int32)
+    got = oracle.to_strips(words)
+    assert got.shape == (2, 2, 16) and np.array_equal(got, want)
+    # flat index of word (r, n): ((n // 16) * rows + r) * 16 + n % 16
+    flat = got.reshape(-1)
+    assert flat[(1 * 2 + 1) * 16 + 5] == 121 and flat[(0 * 2 + 1) * 16 + 15] == 115
+    assert np.array_equal(oracle.from_strips(want, 24), words)
+
+
+def check_strips_round_trip_and_padding():
+    rng = np.random.default_rng(5)
+    for rows, N in ((1, 8), (3, 16), (5, 40), (64, 136)):
+        w = rng.integers(-2**31, 2**31, size=(rows, N), dtype=np.int64).astype(np.int32)
+        t = oracle.to_strips(w)
+        assert t.shape == ((N + 15) // 16, rows, 16)
+        assert np.array_equal(oracle.from_strips(t, N), w)
+        # a permutation of the words plus zero padding: the multisets agree
+        pad = t.size - w.size
+        assert np.array_equal(np.sort(t.reshape(-1)), np.sort(np.concatenate([w.reshape(-1), np.zeros(pad, np.int32)])))
+        # each strip of the output is contiguous: its rows are the plane's 16 columns
+        for s_ in range(t.shape[0]):
+            cols = slice(16 * s_, min(16 * s_ + 16, N))
+            assert np.array_equal(t[s_, :, : cols.stop - cols.start], w[:, cols])
+
+
 CHECKS = [
+    check_strips_hand_worked, check_strips_round_trip_and_padding,
     check_pack_words_hand_worked, check_ascending_nibbles, check_word_bijection,
     check_out_of_range_codes_masked, check_three_bit_identity, check_dequant_examples_hand_worked,
     check_dequant_fp16_hand_worked, check_dequant_fp16_against_exact_rounding, check_bias_row,
@@ -685,7 +721,27 @@ def _mut_3bit10_as_eleven(codes):
     return words.view(np.int32)
 
 
+def _mut_strips_rows_major(words):
+    rows, N = words.shape  # strips ordered column-major inside a strip
+    out = np.zeros(((N + 15) // 16, 16, rows), dtype=words.dtype)
+    for n in range(N):
+        out[n // 16, n % 16, :] = words[:, n]
+    return out.reshape((N + 15) // 16, rows, 16)
+
+
+def _mut_strips_width_8(words):
+    rows, N = words.shape
+    out = np.zeros(((N + 15) // 16, rows, 16), dtype=words.dtype)
+    flat = out.reshape(-1)
+    for r in range(rows):
+        for n in range(N):
+            flat[((n // 8) * rows + r) * 8 + n % 8] = words[r, n]
+    return out
+
+
 MUTATIONS = {
+    "strips_rows_major": ("to_strips", _mut_strips_rows_major),
+    "strips_width_8": ("to_strips", _mut_strips_width_8),
     "pack_slot_reversed": ("pack_kmajor", _mut_pack_slot_reversed),
     "unpack_arith_shift": ("unpack_kmajor", _mut_unpack_arith_shift),
     "dequant_no_zero": ("dequantize", _mut_dequant_no_zero),

@@ -38,16 +38,19 @@ LIB_PATH = os.path.join(HERE, "libqmm.so")
 QMM_OK = 0
 STATUS_NAMES = {
     0: "QMM_OK", 1: "QMM_ERR_NULL", 2: "QMM_ERR_BITS", 3: "QMM_ERR_SHAPE", 4: "QMM_ERR_GROUP",
-    5: "QMM_ERR_ALIGN", 6: "QMM_ERR_WORKSPACE", 7: "QMM_ERR_HIP",
+    5: "QMM_ERR_ALIGN", 6: "QMM_ERR_WORKSPACE", 7: "QMM_ERR_HIP", 8: "QMM_ERR_FLAGS",
 }
 # Every symbol the header declares.
 EXPORTS = (
     "qmm_abi_version", "qmm_status_string", "qmm_last_error", "qmm_pack", "qmm_unpack", "qmm_dequant",
     "qmm_workspace_bytes", "qmm_gemv", "qmm_gemm", "qmm_dequant_bf16", "qmm_gemv_bf16", "qmm_gemm_bf16",
     "qmm_unpack_qzeros", "qmm_unpack_qzeros_bf16", "qmm_repack_3bit10", "qmm_gemv_noalloc",
-    "qmm_gemv_plan_info", "qmm_gemm_plan_info",
+    "qmm_gemv_plan_info", "qmm_gemm_plan_info", "qmm_strips_bytes", "qmm_to_strips", "qmm_from_strips",
+    "qmm_gemv_ex", "qmm_gemm_ex",
 )
-ABI_VERSION = 4
+ABI_VERSION = 5
+QMM_BF16, QMM_STRIPS = 1, 2  # flags of qmm_gemv_ex / qmm_gemm_ex
+STRIP_COLS = 16
 DTYPES = (torch.float16, torch.bfloat16)
 BITS = (1, 2, 3, 4, 8)
 GEMV_MAX_M = 16
@@ -93,6 +96,16 @@ def _declare(lib):
     lib.qmm_gemv_plan_info.argtypes = [I, I, I, I, I, P, I]
     lib.qmm_gemm_plan_info.restype = I
     lib.qmm_gemm_plan_info.argtypes = [I, I, I, I, I, P, I]
+    lib.qmm_strips_bytes.restype = SZ
+    lib.qmm_strips_bytes.argtypes = [I, I]
+    for name in ("qmm_to_strips", "qmm_from_strips"):
+        f = getattr(lib, name)
+        f.restype, f.argtypes = I, [P, I, I, P, P]
+    U = ctypes.c_uint
+    lib.qmm_gemv_ex.restype = I
+    lib.qmm_gemv_ex.argtypes = [P, I, I, P, P, P, P, P, I, I, I, U, P, P, SZ, P]
+    lib.qmm_gemm_ex.restype = I
+    lib.qmm_gemm_ex.argtypes = [P, I, I, P, P, P, P, P, I, I, I, U, P, P]
     if lib.qmm_abi_version() != ABI_VERSION:
         raise RuntimeError(f"libqmm ABI version {lib.qmm_abi_version()} does not match the binding's {ABI_VERSION}")
     return lib
@@ -272,22 +285,31 @@ def _check_bias(bias, N, dtype):
         raise ValueError(f"bias must have N={N} elements")
 
 
-def _check_product_args(x, qweight, qweight_lo, zeros, scales, bits):
+def strips_shape(rows: int, N: int):
+    """Shape of a (rows, N) word plane in the 16-column strip-major layout."""
+    return ((N + STRIP_COLS - 1) // STRIP_COLS, rows, STRIP_COLS)
+
+
+def _check_product_args(x, qweight, qweight_lo, zeros, scales, bits, strips=False):
     dt = _data_dtype(x, "x")
     _gpu(x, "x", dt)
-    _gpu(qweight, "qweight", torch.int32)
+    wdim = 3 if strips else 2
+    _gpu(qweight, "qweight", torch.int32, ndim=wdim)
     if bits == 3:
         if qweight_lo is None:
             raise ValueError("3-bit weights need qweight_lo (the 1-bit plane)")
-        _gpu(qweight_lo, "qweight_lo", torch.int32)
+        _gpu(qweight_lo, "qweight_lo", torch.int32, ndim=wdim)
     _gpu(zeros, "zeros", dt)
     _gpu(scales, "scales", dt)
     M, K = x.shape
-    N = qweight.shape[1]
+    N = zeros.shape[1] if strips else qweight.shape[1]
     if bits in BITS:
         shp, shp_lo = packed_shapes(K, N, bits)
+        if strips:
+            shp, shp_lo = strips_shape(shp[0], N), (strips_shape(shp_lo[0], N) if shp_lo else None)
         if tuple(qweight.shape) != shp or (shp_lo and tuple(qweight_lo.shape) != shp_lo):
-            raise ValueError(f"packed weight shapes {tuple(qweight.shape)} do not match K={K}, N={N}, bits={bits}")
+            raise ValueError(f"packed weight shapes {tuple(qweight.shape)} do not match K={K}, N={N}, bits={bits}"
+                             + (" in 16-column strips" if strips else ""))
     if zeros.shape != scales.shape or zeros.shape[1] != N:
         raise ValueError("zeros and scales must both be (G, N)")
     return M, K, N, dt
@@ -302,20 +324,28 @@ def _output(out, M, N, dt, dev):
     return out
 
 
+def _flags(dt, strips):
+    return (QMM_BF16 if dt == torch.bfloat16 else 0) | (QMM_STRIPS if strips else 0)
+
+
 def qmm_gemv(x, qweight, qweight_lo, zeros, scales, bits: int, group_size: int, out=None, workspace=None,
-             bias=None):
-    """y = x @ dequantize(W) (+ bias) for 1 <= M <= 16; returns (M, N) in x's dtype."""
-    M, K, N, dt = _check_product_args(x, qweight, qweight_lo, zeros, scales, bits)
+             bias=None, strips: bool = False):
+    """y = x @ dequantize(W) (+ bias) for 1 <= M <= 16; returns (M, N) in x's dtype. With
+    ``strips=True`` the packed planes are in the 16-column strip-major layout of qmm_to_strips."""
+    M, K, N, dt = _check_product_args(x, qweight, qweight_lo, zeros, scales, bits, strips)
     _check_bias(bias, N, dt)
     dev = x.device
     y = _output(out, M, N, dt, dev)
     nbytes = workspace_bytes(M, K, N, bits, group_size) if M <= GEMV_MAX_M else 0
     ws = workspace if workspace is not None else gemv_workspace(dev, nbytes)
     with torch.cuda.device(dev):
-        _check(_entry("qmm_gemv", dt)(_ptr(x), M, K, _ptr(qweight), _ptr(qweight_lo), _ptr(zeros), _ptr(scales),
-                                  _ptr(bias), N, bits, group_size, _ptr(y), _ptr(ws), 0 if ws is None else ws.numel(),
-                                  _stream(dev)),
-               "qmm_gemv")
+        args = (_ptr(x), M, K, _ptr(qweight), _ptr(qweight_lo), _ptr(zeros), _ptr(scales), _ptr(bias), N, bits,
+                group_size)
+        tail = (_ptr(y), _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev))
+        if strips:
+            _check(library().qmm_gemv_ex(*args, _flags(dt, True), *tail), "qmm_gemv_ex")
+        else:
+            _check(_entry("qmm_gemv", dt)(*args, *tail), "qmm_gemv")
     return y
 
 
@@ -336,17 +366,51 @@ def qmm_gemv_noalloc(x, qweight, qweight_lo, zeros, scales, bits: int, group_siz
     return y
 
 
-def qmm_gemm(x, qweight, qweight_lo, zeros, scales, bits: int, group_size: int, out=None, bias=None):
-    """y = x @ dequantize(W) (+ bias) for any M on the matrix cores; returns (M, N) in x's dtype."""
-    M, K, N, dt = _check_product_args(x, qweight, qweight_lo, zeros, scales, bits)
+def qmm_gemm(x, qweight, qweight_lo, zeros, scales, bits: int, group_size: int, out=None, bias=None,
+             strips: bool = False):
+    """y = x @ dequantize(W) (+ bias) for any M on the matrix cores; returns (M, N) in x's dtype.
+    ``strips=True``: the packed planes are in the strip-major layout of qmm_to_strips."""
+    M, K, N, dt = _check_product_args(x, qweight, qweight_lo, zeros, scales, bits, strips)
     _check_bias(bias, N, dt)
     dev = x.device
     y = _output(out, M, N, dt, dev)
     with torch.cuda.device(dev):
-        _check(_entry("qmm_gemm", dt)(_ptr(x), M, K, _ptr(qweight), _ptr(qweight_lo), _ptr(zeros), _ptr(scales),
-                                  _ptr(bias), N, bits, group_size, _ptr(y), _stream(dev)),
-               "qmm_gemm")
+        args = (_ptr(x), M, K, _ptr(qweight), _ptr(qweight_lo), _ptr(zeros), _ptr(scales), _ptr(bias), N, bits,
+                group_size)
+        if strips:
+            _check(library().qmm_gemm_ex(*args, _flags(dt, True), _ptr(y), _stream(dev)), "qmm_gemm_ex")
+        else:
+            _check(_entry("qmm_gemm", dt)(*args, _ptr(y), _stream(dev)), "qmm_gemm")
     return y
+
+
+def qmm_to_strips(words: torch.Tensor, out=None) -> torch.Tensor:
+    """A (rows, N) int32 word plane -> its 16-column strip-major form (ceil(N / 16), rows, 16):
+    word (r, n) at [n // 16, r, n % 16], the last strip's columns past N zero. Load-time work."""
+    _gpu(words, "words", torch.int32)
+    rows, N = words.shape
+    shape = strips_shape(rows, N)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.int32, device=words.device)
+    else:
+        _gpu(out, "out", torch.int32, ndim=3)
+        if tuple(out.shape) != shape:
+            raise ValueError(f"out must be {shape}")
+    with torch.cuda.device(words.device):
+        _check(library().qmm_to_strips(_ptr(words), rows, N, _ptr(out), _stream(words.device)), "qmm_to_strips")
+    return out
+
+
+def qmm_from_strips(strips: torch.Tensor, N: int) -> torch.Tensor:
+    """Inverse of qmm_to_strips: (ceil(N / 16), rows, 16) -> (rows, N)."""
+    _gpu(strips, "strips", torch.int32, ndim=3)
+    S, rows, c = strips.shape
+    if (S, c) != strips_shape(rows, N)[::2]:
+        raise ValueError(f"strips {tuple(strips.shape)} do not hold a plane of N={N} columns")
+    out = torch.empty((rows, N), dtype=torch.int32, device=strips.device)
+    with torch.cuda.device(strips.device):
+        _check(library().qmm_from_strips(_ptr(strips), rows, N, _ptr(out), _stream(strips.device)), "qmm_from_strips")
+    return out
 
 
 def quantized_matmul(x, qweight, qzeros, scales, bits: int, group_size: int, qweight_lo=None, bias=None):

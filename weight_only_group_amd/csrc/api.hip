@@ -112,6 +112,29 @@ qmm_status check_product(const uint16_t* x, int M, int K, const int32_t* qweight
   return QMM_OK;
 }
 
+// Planes in the strip-major layout hold N rounded up to a multiple of 16
+// columns; each must stay below 4 GiB, as the kernels' byte offsets are 32-bit.
+qmm_status check_strips_planes(int K, int N, int bits) {
+  const unsigned long long cols = (unsigned long long)qmm::plane_cols(N, 1);
+  if ((unsigned long long)K * cols * (bits == 3 ? 2 : bits) / 8 >= (1ull << 32))
+    return fail(QMM_ERR_SHAPE, "qweight in 16-column strips must be smaller than 4 GiB");
+  return QMM_OK;
+}
+
+qmm_status check_flags(unsigned flags) {
+  if (flags & ~(unsigned)(QMM_BF16 | QMM_STRIPS)) return fail(QMM_ERR_FLAGS, "flags=0x%x: unknown bits", flags);
+  return QMM_OK;
+}
+
+qmm_status check_strips_call(const void* in, int rows, int N, const void* out) {
+  if (rows < 1 || N < 1) return fail(QMM_ERR_SHAPE, "rows=%d and N=%d must be >= 1", rows, N);
+  if ((unsigned long long)rows * (unsigned long long)qmm::plane_cols(N, 1) * 4 >= (1ull << 32))
+    return fail(QMM_ERR_SHAPE, "a plane of %d rows and %d columns in strips must be smaller than 4 GiB", rows, N);
+  if (!in || !out) return fail(QMM_ERR_NULL, "the input and output planes must not be NULL");
+  if (!aligned(in, 4) || !aligned(out, 4)) return fail(QMM_ERR_ALIGN, "the planes must be 4-byte aligned");
+  return QMM_OK;
+}
+
 qmm_status from_hip(hipError_t e, const char* what) {
   if (e == hipSuccess) return ok();
   return fail(QMM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -138,9 +161,10 @@ qmm_status dequant_impl(const int32_t* qweight, const int32_t* qweight_lo, const
 qmm_status gemv_impl(const uint16_t* x, int M, int K, const int32_t* qweight, const int32_t* qweight_lo,
                     const uint16_t* zeros, const uint16_t* scales, const uint16_t* bias, int N, int bits,
                     int group_size, uint16_t* y, void* workspace, size_t workspace_bytes, bool bf16,
-                    hipStream_t stream) {
+                    bool strips, hipStream_t stream) {
   qmm_status st = check_product(x, M, K, qweight, qweight_lo, zeros, scales, bias, N, bits, group_size, y, 16);
   if (st != QMM_OK) return st;
+  if (strips && (st = check_strips_planes(K, N, bits)) != QMM_OK) return st;
   if (N > qmm::kGemvMaxN) return fail(QMM_ERR_SHAPE, "N=%d exceeds the decode product's limit of %d", N, qmm::kGemvMaxN);
   const qmm::GemvPlan plan = qmm::gemv_plan(M, K, N, bits, group_size, qmm::device_topology());
   if (!plan.valid)
@@ -154,7 +178,7 @@ qmm_status gemv_impl(const uint16_t* x, int M, int K, const int32_t* qweight, co
   }
   return from_hip(qmm::launch_gemv(plan, x, M, K, reinterpret_cast<const uint32_t*>(qweight),
                                    reinterpret_cast<const uint32_t*>(qweight_lo), zeros, scales, bias, N, bits,
-                                   group_size, y, workspace, bf16, stream),
+                                   group_size, y, workspace, bf16, strips, stream),
                   "qmm_gemv launch");
 }
 
@@ -211,7 +235,7 @@ qmm_status gemv_noalloc_impl(const uint16_t* x, int M, int K, const int32_t* qwe
   }
   return from_hip(qmm::launch_gemv(plan, x, M, K, reinterpret_cast<const uint32_t*>(qweight),
                                    reinterpret_cast<const uint32_t*>(qweight_lo), zeros, scales, bias, N, bits,
-                                   group_size, y, ws, false, stream),
+                                   group_size, y, ws, false, false, stream),
                   "qmm_gemv_noalloc launch");
 }
 
@@ -231,12 +255,13 @@ qmm_status unpack_qzeros_impl(const int32_t* qzeros, int G, int N, int bits, uin
 
 qmm_status gemm_impl(const uint16_t* x, int M, int K, const int32_t* qweight, const int32_t* qweight_lo,
                     const uint16_t* zeros, const uint16_t* scales, const uint16_t* bias, int N, int bits,
-                    int group_size, uint16_t* y, bool bf16, hipStream_t stream) {
+                    int group_size, uint16_t* y, bool bf16, bool strips, hipStream_t stream) {
   qmm_status st = check_product(x, M, K, qweight, qweight_lo, zeros, scales, bias, N, bits, group_size, y, 1 << 30);
   if (st != QMM_OK) return st;
+  if (strips && (st = check_strips_planes(K, N, bits)) != QMM_OK) return st;
   return from_hip(qmm::launch_gemm(x, M, K, reinterpret_cast<const uint32_t*>(qweight),
                                    reinterpret_cast<const uint32_t*>(qweight_lo), zeros, scales, bias, N, bits,
-                                   group_size, y, bf16, qmm::device_topology(), stream),
+                                   group_size, y, bf16, strips, qmm::device_topology(), stream),
                   "qmm_gemm launch");
 }
 
@@ -256,6 +281,7 @@ const char* qmm_status_string(int status) {
     case QMM_ERR_ALIGN: return "QMM_ERR_ALIGN";
     case QMM_ERR_WORKSPACE: return "QMM_ERR_WORKSPACE";
     case QMM_ERR_HIP: return "QMM_ERR_HIP";
+    case QMM_ERR_FLAGS: return "QMM_ERR_FLAGS";
     default: return "QMM_ERR_UNKNOWN";
   }
 }
@@ -335,14 +361,14 @@ qmm_status qmm_gemv(const uint16_t* x, int M, int K, const int32_t* qweight, con
                     const uint16_t* zeros, const uint16_t* scales, const uint16_t* bias, int N, int bits,
                     int group_size, uint16_t* y, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return gemv_impl(x, M, K, qweight, qweight_lo, zeros, scales, bias, N, bits, group_size, y, workspace,
-                   workspace_bytes, false, stream);
+                   workspace_bytes, false, false, stream);
 }
 
 qmm_status qmm_gemv_bf16(const uint16_t* x, int M, int K, const int32_t* qweight, const int32_t* qweight_lo,
                          const uint16_t* zeros, const uint16_t* scales, const uint16_t* bias, int N, int bits,
                          int group_size, uint16_t* y, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return gemv_impl(x, M, K, qweight, qweight_lo, zeros, scales, bias, N, bits, group_size, y, workspace,
-                   workspace_bytes, true, stream);
+                   workspace_bytes, true, false, stream);
 }
 
 qmm_status qmm_gemv_noalloc(const uint16_t* x, int M, int K, const int32_t* qweight, const int32_t* qweight_lo,
@@ -354,13 +380,54 @@ qmm_status qmm_gemv_noalloc(const uint16_t* x, int M, int K, const int32_t* qwei
 qmm_status qmm_gemm(const uint16_t* x, int M, int K, const int32_t* qweight, const int32_t* qweight_lo,
                     const uint16_t* zeros, const uint16_t* scales, const uint16_t* bias, int N, int bits,
                     int group_size, uint16_t* y, hipStream_t stream) {
-  return gemm_impl(x, M, K, qweight, qweight_lo, zeros, scales, bias, N, bits, group_size, y, false, stream);
+  return gemm_impl(x, M, K, qweight, qweight_lo, zeros, scales, bias, N, bits, group_size, y, false, false, stream);
 }
 
 qmm_status qmm_gemm_bf16(const uint16_t* x, int M, int K, const int32_t* qweight, const int32_t* qweight_lo,
                          const uint16_t* zeros, const uint16_t* scales, const uint16_t* bias, int N, int bits,
                          int group_size, uint16_t* y, hipStream_t stream) {
-  return gemm_impl(x, M, K, qweight, qweight_lo, zeros, scales, bias, N, bits, group_size, y, true, stream);
+  return gemm_impl(x, M, K, qweight, qweight_lo, zeros, scales, bias, N, bits, group_size, y, true, false, stream);
+}
+
+qmm_status qmm_gemv_ex(const uint16_t* x, int M, int K, const int32_t* qweight, const int32_t* qweight_lo,
+                       const uint16_t* zeros, const uint16_t* scales, const uint16_t* bias, int N, int bits,
+                       int group_size, unsigned flags, uint16_t* y, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  const qmm_status st = check_flags(flags);
+  if (st != QMM_OK) return st;
+  return gemv_impl(x, M, K, qweight, qweight_lo, zeros, scales, bias, N, bits, group_size, y, workspace,
+                   workspace_bytes, (flags & QMM_BF16) != 0, (flags & QMM_STRIPS) != 0, stream);
+}
+
+qmm_status qmm_gemm_ex(const uint16_t* x, int M, int K, const int32_t* qweight, const int32_t* qweight_lo,
+                       const uint16_t* zeros, const uint16_t* scales, const uint16_t* bias, int N, int bits,
+                       int group_size, unsigned flags, uint16_t* y, hipStream_t stream) {
+  const qmm_status st = check_flags(flags);
+  if (st != QMM_OK) return st;
+  return gemm_impl(x, M, K, qweight, qweight_lo, zeros, scales, bias, N, bits, group_size, y,
+                   (flags & QMM_BF16) != 0, (flags & QMM_STRIPS) != 0, stream);
+}
+
+size_t qmm_strips_bytes(int rows, int N) {
+  if (rows < 1 || N < 1) return 0;
+  const unsigned long long b = (unsigned long long)rows * (unsigned long long)qmm::plane_cols(N, 1) * 4;
+  return b >= (1ull << 32) ? 0 : (size_t)b;
+}
+
+qmm_status qmm_to_strips(const int32_t* words, int rows, int N, int32_t* strips, hipStream_t stream) {
+  const qmm_status st = check_strips_call(words, rows, N, strips);
+  if (st != QMM_OK) return st;
+  return from_hip(qmm::launch_to_strips(reinterpret_cast<const uint32_t*>(words), rows, N,
+                                        reinterpret_cast<uint32_t*>(strips), stream),
+                  "qmm_to_strips launch");
+}
+
+qmm_status qmm_from_strips(const int32_t* strips, int rows, int N, int32_t* words, hipStream_t stream) {
+  const qmm_status st = check_strips_call(strips, rows, N, words);
+  if (st != QMM_OK) return st;
+  return from_hip(qmm::launch_from_strips(reinterpret_cast<const uint32_t*>(strips), rows, N,
+                                          reinterpret_cast<uint32_t*>(words), stream),
+                  "qmm_from_strips launch");
 }
 
 qmm_status qmm_unpack_qzeros(const int32_t* qzeros, int G, int N, int bits, uint16_t* zeros, hipStream_t stream) {

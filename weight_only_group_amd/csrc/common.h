@@ -61,6 +61,22 @@ struct DeviceTopo {
 };
 DeviceTopo device_topology();
 
+// ---- weight layouts ----------------------------------------------------------
+// A plane of packed words (rows x N int32) is read in one of two layouts:
+// K-major (word (r, n) at r * N + n, the packing of the products' inputs)
+// or 16-column strip-major (word (r, n) at ((n / 16) * rows + r) * 16 +
+// n % 16: every 16-column strip stored whole, row after row, the columns past
+// N of the last strip padded). In both, word (r, n) sits at
+// plane_col(n) + r * row stride.
+constexpr int kStripCols = 16;
+__host__ __device__ __forceinline__ int plane_row_stride(int N, int strips) { return strips ? kStripCols : N; }
+__host__ __device__ __forceinline__ long long plane_cols(int N, int strips) {  // words per row as stored
+  return strips ? ((long long)N + kStripCols - 1) / kStripCols * kStripCols : (long long)N;
+}
+__host__ __device__ __forceinline__ uint32_t plane_col(int n, int rows, int strips) {
+  return strips ? (uint32_t)(n >> 4) * (uint32_t)rows * (uint32_t)kStripCols + (uint32_t)(n & 15) : (uint32_t)n;
+}
+
 // ---- decode GEMV (small M) ----------------------------------------------
 // The workspace header has one arrival counter per column strip. Strips are
 // 32 or 64 columns wide whenever there are more than 256 of them, so this
@@ -92,7 +108,7 @@ GemvPlan gemv_plan(int M, int K, int N, int bits, int group_size, DeviceTopo top
 hipError_t launch_gemv(const GemvPlan& p, const uint16_t* x, int M, int K, const uint32_t* qw,
                        const uint32_t* qlo, const uint16_t* zeros, const uint16_t* scales,
                        const uint16_t* bias, int N, int bits, int group_size, uint16_t* y,
-                       void* workspace, bool bf16, hipStream_t stream);
+                       void* workspace, bool bf16, bool strips, hipStream_t stream);
 
 // ---- prefill GEMM ---------------------------------------------------------
 struct GemmPlan {
@@ -106,7 +122,12 @@ struct GemmPlan {
 GemmPlan gemm_plan(int M, int K, int N, DeviceTopo topo);
 hipError_t launch_gemm(const uint16_t* x, int M, int K, const uint32_t* qw, const uint32_t* qlo,
                        const uint16_t* zeros, const uint16_t* scales, const uint16_t* bias, int N,
-                       int bits, int group_size, uint16_t* y, bool bf16, DeviceTopo topo, hipStream_t stream);
+                       int bits, int group_size, uint16_t* y, bool bf16, bool strips, DeviceTopo topo,
+                       hipStream_t stream);
+
+// ---- strip-major re-layout (load time) ----------------------------------------
+hipError_t launch_to_strips(const uint32_t* words, int rows, int N, uint32_t* strips, hipStream_t stream);
+hipError_t launch_from_strips(const uint32_t* strips, int rows, int N, uint32_t* words, hipStream_t stream);
 
 // ---- dequantize to fp16 -------------------------------------------------------
 hipError_t launch_dequant(const uint32_t* qw, const uint32_t* qlo, const uint16_t* zeros,

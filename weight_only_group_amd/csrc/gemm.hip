@@ -63,6 +63,7 @@ struct GemmArgs {
   int mblocks, nblocks;
   int xcds;      // XCDs of the device; blocks are dealt to them round-robin
   int cus;       // compute units of the device
+  int strips;    // packed words in the 16-column strip-major layout (else K-major)
 };
 
 // Words one lane needs for one 32-column tile and one 16-k step: a 32 x 32 x 16
@@ -244,8 +245,11 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
   // plus a scalar offset, which keeps address arithmetic out of the vector
   // registers.
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(g.x, (size_t)g.M * g.K * 2);
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(g.qw, (size_t)(g.K / Frag<BITS>::EPS) * g.N * 4);
-  const __amdgpu_buffer_rsrc_t rl = make_rsrc(NL > 0 ? g.qlo : g.qw, NL > 0 ? (size_t)(g.K / 32) * g.N * 4 : 4);
+  const int wrs = plane_row_stride(g.N, g.strips);
+  const long long wcols = plane_cols(g.N, g.strips);
+  const int rows0 = g.K / Frag<BITS>::EPS, rows1 = g.K / 32;  // word rows of the planes
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(g.qw, (size_t)rows0 * wcols * 4);
+  const __amdgpu_buffer_rsrc_t rl = make_rsrc(NL > 0 ? g.qlo : g.qw, NL > 0 ? (size_t)rows1 * wcols * 4 : 4);
   const __amdgpu_buffer_rsrc_t rz = make_rsrc(g.zeros, (size_t)(g.K / 32 / g.upg) * g.N * 2);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(g.scales, (size_t)(g.K / 32 / g.upg) * g.N * 2);
 
@@ -278,12 +282,26 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
   auto tile_col = [&](int t) {  // the lane's column of tile t, within the block
     return PAIR ? (BN / WN) * wn + 64 * (t >> 1) + 2 * (lane & 31) + (t & 1) : (BN / WN) * wn + 32 * t + (lane & 31);
   };
-  uint32_t b_voff[TN];  // per tile: byte offset of the lane's column in a word row
-  uint32_t p_voff[NP];  // per pair: the same for its even column (clamped to N - 2, 8-byte aligned)
+  // Per tile the lane's column (clamped to N - 1), per pair its even column
+  // (clamped to N - 2): 2-byte offsets into rows of zero points and scales,
+  // and byte offsets of the column's words in each plane (both columns of a
+  // pair are adjacent words in either layout).
+  uint32_t b_zoff[TN], p_zoff[NP];
+  uint32_t b_voff[TN], p_voff[NP], b_loff[TN], p_loff[NP];
 #pragma unroll
-  for (int t = 0; t < TN; ++t) b_voff[t] = (uint32_t)min(n0 + tile_col(t), g.N - 1) * 4u;
+  for (int t = 0; t < TN; ++t) {
+    const int n = min(n0 + tile_col(t), g.N - 1);
+    b_zoff[t] = (uint32_t)n * 2u;
+    b_voff[t] = plane_col(n, rows0, g.strips) * 4u;
+    b_loff[t] = plane_col(n, rows1, g.strips) * 4u;
+  }
 #pragma unroll
-  for (int p = 0; p < NP; ++p) p_voff[p] = (uint32_t)min(n0 + tile_col(2 * p), g.N - 2) * 4u;
+  for (int p = 0; p < NP; ++p) {
+    const int n = min(n0 + tile_col(2 * p), g.N - 2);
+    p_zoff[p] = (uint32_t)n * 2u;
+    p_voff[p] = plane_col(n, rows0, g.strips) * 4u;
+    p_loff[p] = plane_col(n, rows1, g.strips) * 4u;
+  }
 
   // Slab ks into buffer buf. Slabs past the end of K (which pad the group's
   // slab count) and chunks past it are zeros: their lanes read out of range,
@@ -320,20 +338,20 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
     const int ks = min(ks_in, nk - 1);
     const bool past = KTAIL && ks * BK + 16 * s >= g.K;  // this step is past the end of K: read row 0
     // kc is a lane property: it goes in the per-lane offset
-    const uint32_t kcoff = past ? 0u : (BITS == 8 ? 2u * kc : (BITS == 4 ? (uint32_t)kc : 0u)) * (uint32_t)g.N * 4u;
+    const uint32_t kcoff = past ? 0u : (BITS == 8 ? 2u * kc : (BITS == 4 ? (uint32_t)kc : 0u)) * (uint32_t)wrs * 4u;
     if constexpr (PAIR) {
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
           const int row0 = past ? 0 : frag_row<BITS>(ks, s, 0, w);
-          const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rw, p_voff[p] + kcoff, (uint32_t)row0 * (uint32_t)g.N * 4u, kWeightPolicy);
+          const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rw, p_voff[p] + kcoff, (uint32_t)row0 * (uint32_t)wrs * 4u, kWeightPolicy);
           S.w[2 * p][w] = v.x;
           S.w[2 * p + 1][w] = v.y;
         }
         if constexpr (NL > 0) {
           const int lrow = past ? 0 : ks * 2 + (s >> 1);
-          const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rl, p_voff[p], (uint32_t)lrow * (uint32_t)g.N * 4u, kWeightPolicy);
+          const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rl, p_loff[p], (uint32_t)lrow * (uint32_t)wrs * 4u, kWeightPolicy);
           S.l[2 * p][0] = v.x;
           S.l[2 * p + 1][0] = v.y;
         }
@@ -345,11 +363,11 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
         const int row0 = past ? 0 : frag_row<BITS>(ks, s, 0, w);
-        S.w[t][w] = __builtin_amdgcn_raw_buffer_load_b32(rw, b_voff[t] + kcoff, (uint32_t)row0 * (uint32_t)g.N * 4u, kWeightPolicy);
+        S.w[t][w] = __builtin_amdgcn_raw_buffer_load_b32(rw, b_voff[t] + kcoff, (uint32_t)row0 * (uint32_t)wrs * 4u, kWeightPolicy);
       }
       if constexpr (NL > 0) {
         const int lrow = past ? 0 : ks * 2 + (s >> 1);
-        S.l[t][0] = __builtin_amdgcn_raw_buffer_load_b32(rl, b_voff[t], (uint32_t)lrow * (uint32_t)g.N * 4u, kWeightPolicy);
+        S.l[t][0] = __builtin_amdgcn_raw_buffer_load_b32(rl, b_loff[t], (uint32_t)lrow * (uint32_t)wrs * 4u, kWeightPolicy);
       }
     }
   };
@@ -369,11 +387,11 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
 #pragma unroll
       for (int q = 0; q < NZ; ++q) {
         if constexpr (PAIR) {
-          Z.z[q][h] = __builtin_amdgcn_raw_buffer_load_b32(rz, p_voff[q] / 2u, (uint32_t)grp * (uint32_t)g.N * 2u, 0);
-          Z.s[q][h] = __builtin_amdgcn_raw_buffer_load_b32(rs, p_voff[q] / 2u, (uint32_t)grp * (uint32_t)g.N * 2u, 0);
+          Z.z[q][h] = __builtin_amdgcn_raw_buffer_load_b32(rz, p_zoff[q], (uint32_t)grp * (uint32_t)g.N * 2u, 0);
+          Z.s[q][h] = __builtin_amdgcn_raw_buffer_load_b32(rs, p_zoff[q], (uint32_t)grp * (uint32_t)g.N * 2u, 0);
         } else {
-          Z.z[q][h] = __builtin_amdgcn_raw_buffer_load_b16(rz, b_voff[q] / 2u, (uint32_t)grp * (uint32_t)g.N * 2u, 0);
-          Z.s[q][h] = __builtin_amdgcn_raw_buffer_load_b16(rs, b_voff[q] / 2u, (uint32_t)grp * (uint32_t)g.N * 2u, 0);
+          Z.z[q][h] = __builtin_amdgcn_raw_buffer_load_b16(rz, b_zoff[q], (uint32_t)grp * (uint32_t)g.N * 2u, 0);
+          Z.s[q][h] = __builtin_amdgcn_raw_buffer_load_b16(rs, b_zoff[q], (uint32_t)grp * (uint32_t)g.N * 2u, 0);
         }
       }
     }
@@ -768,8 +786,9 @@ GemmPlan gemm_plan(int M, int K, int N, DeviceTopo topo) {
 
 hipError_t launch_gemm(const uint16_t* x, int M, int K, const uint32_t* qw, const uint32_t* qlo,
                        const uint16_t* zeros, const uint16_t* scales, const uint16_t* bias, int N, int bits,
-                       int group_size, uint16_t* y, bool bf16, DeviceTopo topo, hipStream_t s) {
+                       int group_size, uint16_t* y, bool bf16, bool strips, DeviceTopo topo, hipStream_t s) {
   GemmArgs a;
+  a.strips = strips ? 1 : 0;
   a.xcds = topo.xcds > 0 ? topo.xcds : 8;
   a.cus = topo.cus > 0 ? topo.cus : 256;
   a.x = x;

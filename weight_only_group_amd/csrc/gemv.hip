@@ -107,8 +107,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs g) {
   const int G = U / g.upg;
 
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(g.x, (size_t)g.M * g.K * 2);
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(g.qw, (size_t)U * unit_rows<BITS>(0) * g.N * 4);
-  const __amdgpu_buffer_rsrc_t rl = make_rsrc(BITS == 3 ? g.qlo : g.qw, (size_t)U * unit_rows<BITS>(NW - 1) * g.N * 4);
+  const long long wcols = plane_cols(g.N, g.strips);
+  const int wrs = plane_row_stride(g.N, g.strips);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(g.qw, (size_t)U * unit_rows<BITS>(0) * wcols * 4);
+  const __amdgpu_buffer_rsrc_t rl = make_rsrc(BITS == 3 ? g.qlo : g.qw, (size_t)U * unit_rows<BITS>(NW - 1) * wcols * 4);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(g.scales, (size_t)G * g.N * 2);
   const __amdgpu_buffer_rsrc_t rz = make_rsrc(g.zeros, (size_t)G * g.N * 2);
 
@@ -137,7 +139,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs g) {
   // past the wave's range repeat its last unit and are not used.
   uint32_t woff[NW];
 #pragma unroll
-  for (int w = 0; w < NW; ++w) woff[w] = (uint32_t)(lane_row<BITS>(j, w) * g.N + ncc) * 4u;
+  for (int w = 0; w < NW; ++w)
+    woff[w] = (plane_col(ncc, U * unit_rows<BITS>(w), g.strips) + (uint32_t)(lane_row<BITS>(j, w) * wrs)) * 4u;
   typename Vec<VEC>::T wv[CH][NW];
   auto load_batch = [&](int base) {
 #pragma unroll
@@ -145,7 +148,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs g) {
       const int u = min(base + c, uz - 1);  // uz >= 1
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        const uint32_t soff = (uint32_t)(u * unit_rows<BITS>(w)) * (uint32_t)g.N * 4u;
+        const uint32_t soff = (uint32_t)(u * unit_rows<BITS>(w)) * (uint32_t)wrs * 4u;
         wv[c][w] = load_words<VEC>((BITS == 3 && w == 1) ? rl : rw, woff[w], soff);
       }
     }
@@ -554,7 +557,7 @@ GemvPlan gemv_plan(int M, int K, int N, int bits, int group_size, DeviceTopo top
 hipError_t launch_gemv(const GemvPlan& p, const uint16_t* x, int M, int K, const uint32_t* qw,
                        const uint32_t* qlo, const uint16_t* zeros, const uint16_t* scales,
                        const uint16_t* bias, int N, int bits, int group_size, uint16_t* y,
-                       void* workspace, bool bf16, hipStream_t s) {
+                       void* workspace, bool bf16, bool strips, hipStream_t s) {
   if (!p.valid) return hipErrorInvalidValue;
   GemvArgs a;
   a.x = x;
@@ -579,6 +582,7 @@ hipError_t launch_gemv(const GemvPlan& p, const uint16_t* x, int M, int K, const
   for (int l = 1; l < 8; ++l)
     if ((1 << l) == p.xcds && p.nstrips % p.xcds == 0) a.xcd_log2 = l;
   a.gl = p.gl;
+  a.strips = strips ? 1 : 0;
   if (p.kind == 1) return launch_wave_any(p, a, bits, bf16, s);
   return bf16 ? launch_dtype<true>(p, a, bits, s) : launch_dtype<false>(p, a, bits, s);
 }

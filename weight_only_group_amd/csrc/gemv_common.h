@@ -48,6 +48,7 @@ struct GemvArgs {
   int gp_log2;   // log2 of the rows of scales / zero points staged per block
   int xcd_log2;  // log2 of the XCD count when that is a power of two dividing the grid's x size, else -1
   int gl;        // wave kernel: log2 of the units per group (30 for one group over all of K)
+  int strips;    // packed words in the 16-column strip-major layout (else K-major)
 };
 
 namespace {

@@ -96,8 +96,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_wave_kernel(GemvArgs g) {
   float* red = reinterpret_cast<float*>(dyn_lds);  // reused after the units
 
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(g.x, (size_t)g.M * g.K * 2);
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(g.qw, (size_t)U * unit_rows<BITS>(0) * g.N * 4);
-  const __amdgpu_buffer_rsrc_t rl = make_rsrc(BITS == 3 ? g.qlo : g.qw, (size_t)U * unit_rows<BITS>(NW - 1) * g.N * 4);
+  const long long wcols = plane_cols(g.N, g.strips);
+  const int wrs = plane_row_stride(g.N, g.strips);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(g.qw, (size_t)U * unit_rows<BITS>(0) * wcols * 4);
+  const __amdgpu_buffer_rsrc_t rl = make_rsrc(BITS == 3 ? g.qlo : g.qw, (size_t)U * unit_rows<BITS>(NW - 1) * wcols * 4);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(g.scales, (size_t)G * g.N * 2);
   const __amdgpu_buffer_rsrc_t rz = make_rsrc(g.zeros, (size_t)G * g.N * 2);
 
@@ -167,13 +169,14 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_wave_kernel(GemvArgs g) {
   }
   uint32_t woff[NW];
 #pragma unroll
-  for (int w = 0; w < NW; ++w) woff[w] = (uint32_t)(lane_row<BITS>(j, w) * g.N + ncc) * 4u;
+  for (int w = 0; w < NW; ++w)
+    woff[w] = (plane_col(ncc, U * unit_rows<BITS>(w), g.strips) + (uint32_t)(lane_row<BITS>(j, w) * wrs)) * 4u;
   typename Vec<VEC>::T wv[UPW][NW];
 #pragma unroll
   for (int c = 0; c < UPW; ++c) {
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      const uint32_t soff = (uint32_t)((ua + c) * unit_rows<BITS>(w)) * (uint32_t)g.N * 4u;
+      const uint32_t soff = (uint32_t)((ua + c) * unit_rows<BITS>(w)) * (uint32_t)wrs * 4u;
       wv[c][w] = load_words<VEC>((BITS == 3 && w == 1) ? rl : rw, woff[w], soff);
     }
   }
