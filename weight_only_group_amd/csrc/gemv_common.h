@@ -84,7 +84,10 @@ template <int BITS> struct DecodeMasks {
   uint32_t m[4];
   uint32_t magic;
 };
-template <int BITS> __device__ __forceinline__ DecodeMasks<BITS> decode_masks() {
+// SUB: the codes become fp16 subnormals (exponent field 0, value 2^e q 2^-24)
+// instead of 1024 + 2^e q: the same inserts into a zero word, which the
+// compiler reduces to ANDs.
+template <int BITS, bool SUB = false> __device__ __forceinline__ DecodeMasks<BITS> decode_masks() {
   DecodeMasks<BITS> d;
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
@@ -94,8 +97,8 @@ template <int BITS> __device__ __forceinline__ DecodeMasks<BITS> decode_masks() 
            : BITS == 1 ? ((1u << p) | (1u << (20 + p))) : 0u;
     if (BITS == 1 || ((BITS == 2 || BITS == 3 || BITS == 4) && p < 2)) asm("" : "+v"(d.m[p]));
   }
-  d.magic = kMagic1024x2;
-  asm("" : "+s"(d.magic));
+  d.magic = SUB ? 0u : kMagic1024x2;
+  if (!SUB) asm("" : "+s"(d.magic));
   return d;
 }
 
@@ -118,10 +121,13 @@ template <int BITS> __host__ __device__ constexpr int code_exp(int p, int hi) {
 // high half; 3-bit: q >> 1 (2-bit plane) goes to bits 2-3 and q & 1 (1-bit
 // plane, its bytes of this lane group copied into both halves) to bit 1, so
 // each half is 1024 + 2q.
-template <int BITS>
+// With SUB (decode_masks<BITS, true>) the same places hold the codes as fp16
+// subnormals: half `hi` of pair p is 2^e q 2^-24, exactly.
+template <int BITS, bool SUB = false>
 __device__ __forceinline__ void decode8(uint32_t w0, uint32_t w1, int j, const DecodeMasks<BITS>& dm,
                                         uint32_t (&b)[4]) {
-  const uint32_t magic = dm.magic;
+  const uint32_t magic = SUB ? 0u : dm.magic;
+  const uint32_t mag8 = SUB ? 0u : 0x64646464u;
   if constexpr (BITS == 4) {
     const uint32_t t = w0 >> 8;
     b[0] = bfi(dm.m[0], w0, magic);
@@ -135,10 +141,11 @@ __device__ __forceinline__ void decode8(uint32_t w0, uint32_t w1, int j, const D
     for (int p = 0; p < 4; ++p) b[p] = bfi(dm.m[p], t, magic);
   } else if constexpr (BITS == 8) {
     // byte permute: (byte0, 0x64, byte1, 0x64) = halves (1024 + q0, 1024 + q1)
-    b[0] = __builtin_amdgcn_perm(0x64646464u, w0, 0x04010400u);
-    b[1] = __builtin_amdgcn_perm(0x64646464u, w0, 0x04030402u);
-    b[2] = __builtin_amdgcn_perm(0x64646464u, w1, 0x04010400u);
-    b[3] = __builtin_amdgcn_perm(0x64646464u, w1, 0x04030402u);
+    // (with SUB zero bytes in place of 0x64: halves q0 2^-24, q1 2^-24)
+    b[0] = __builtin_amdgcn_perm(mag8, w0, 0x04010400u);
+    b[1] = __builtin_amdgcn_perm(mag8, w0, 0x04030402u);
+    b[2] = __builtin_amdgcn_perm(mag8, w1, 0x04010400u);
+    b[3] = __builtin_amdgcn_perm(mag8, w1, 0x04030402u);
   } else if constexpr (BITS == 2) {
     const uint32_t ws = w0 >> (8 * (j & 1));
     const uint32_t t = ws >> 4;

@@ -29,10 +29,11 @@ namespace {
 //  * Each wave then runs its units as their words arrive (loads complete in
 //    order). The wave's units form GPW (1, 2 or 4) groups of equal size, a
 //    compile-time structure: no scalar bookkeeping per unit.
-//  * One packed FMA per code pair dequantizes, exactly for integer zero
-//    points; a group whose zero points leave a remainder in that form takes
-//    one more matrix-core product per unit to remove it. The waves' fp32
-//    results are summed through LDS in wave order and rounded once.
+//  * fp16 data: the codes become fp16 subnormals with bit operations only
+//    (no zero point, no offset), the matrix cores form sum x q and sum x per
+//    group, and s (q - z) is applied to those two fp32 sums (any fp16 zero
+//    point). The waves' fp32 results are summed through LDS in wave order
+//    and rounded once.
 // LDS: the staged activations (M * K / 32 * 4 slots of 16 bytes, in an area
 // of 4 slots per thread, 256 per wave), later reused for the per-wave
 // results (WAVES * M * 16 * VEC floats); sized at launch, at most 64 KiB.
@@ -62,6 +63,34 @@ template <int VEC>
 __device__ __forceinline__ uint16_t half_bits(const typename HalfWords<VEC>::T (&h)[HalfWords<VEC>::N], int v) {
   if constexpr (VEC == 1) return h[0];
   else return (uint16_t)(h[v >> 1] >> (16 * (v & 1)));
+}
+
+// fp16 data: the codes enter the matrix cores as fp16 subnormals 2^e q 2^-24
+// (decode8 with SUB; e = code_exp, the code's place in the mantissa), which
+// the matrix cores take exactly. The activations are staged with element
+// (p, hi) scaled by 2^-e, so every product is x q 2^-24 whatever the place,
+// and a B operand of 2^e gives the sum of x over the same k. Per group, the
+// dequantization s (q - z) is then applied to the two sums:
+// s 2^24 (sum x q 2^-24 - z 2^-24 sum x), any fp16 zero point, no offset.
+template <int BITS>
+__device__ __forceinline__ u32x4 x_prescaled(u32x4 a) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    if (code_exp<BITS>(p, 0) != 0 || code_exp<BITS>(p, 1) != 0)
+      a[p] = as_u32(as_f16x2(a[p]) * f16x2{(f16)(1.0f / (float)(1 << code_exp<BITS>(p, 0))),
+                                           (f16)(1.0f / (float)(1 << code_exp<BITS>(p, 1)))});
+  }
+  return a;
+}
+template <int BITS>
+__device__ __forceinline__ f16x8 place_ones() {
+  f16x8 o;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    o[2 * p] = (f16)(float)(1 << code_exp<BITS>(p, 0));
+    o[2 * p + 1] = (f16)(float)(1 << code_exp<BITS>(p, 1));
+  }
+  return o;
 }
 
 template <int BITS, int VEC, int WAVES, int UPW, int GPW, bool BF, bool M1>
@@ -162,10 +191,6 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_wave_kernel(GemvArgs g) {
       load_halves<VEC>(rs, off, sraw[gi]);
       load_halves<VEC>(rz, off, zraw[gi]);
     }
-    if constexpr (!BF) {
-      const uint32_t off = ((uint32_t)(g0 + (j < GPW ? j : GPW - 1)) * (uint32_t)g.N + (uint32_t)ncc) * 2u;
-      load_halves<VEC>(rz, off, zchk);
-    }
   }
   uint32_t woff[NW];
 #pragma unroll
@@ -189,7 +214,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_wave_kernel(GemvArgs g) {
   // all of them before the barrier.
 #pragma unroll
   for (int i = 0; i < kWaveXPerThread; ++i)
-    if (i < xpt) xs[xbase + (OWN ? lane + 64 * i : tid + THREADS * i)] = x_operand<BITS>(xraw[i]);  // scalar condition
+    if (i < xpt) {  // scalar condition
+      const u32x4 a = x_operand<BITS>(xraw[i]);
+      xs[xbase + (OWN ? lane + 64 * i : tid + THREADS * i)] = BF ? a : x_prescaled<BITS>(a);
+    }
   if constexpr (OWN) {
     // The wave reads back only what it wrote itself: LDS operations of one
     // wave take effect in order, so a compiler-level fence is enough.
@@ -215,48 +243,21 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_wave_kernel(GemvArgs g) {
   }
 
   // ---- 3. the wave's units, group by group (static).
-  // fp16 data: per pair class, c = -(1024 2^-e + z) rounded to fp16; one
-  // packed FMA h 2^-e + c then gives q - z - r with the remainder
-  // r = c + 1024 2^-e + z (exact in fp32), which is zero for integer zero
-  // points |z| <= 1024. The wave checks that once, here, while its weight
-  // words are still arriving (lane group j checks group slot j); a wave with any other zero point removes the
-  // remainders in one more pass after its units (x times a B operand of -r
-  // per group), so the unit loop itself has no branch. bf16 data: q - z is
-  // formed in fp32 (czf = 1024 2^-e + z, or z alone for 1-bit codes).
-  int fix = 0;
-  if constexpr (!BF) {
-    bool inexact = false;
-#pragma unroll
-    for (int v = 0; v < VEC; ++v) {
-      const float zf = half_bits_to_float(half_bits<VEC>(zchk, v));
-      inexact = inexact || zf != __builtin_rintf(zf) || __builtin_fabsf(zf) > 1024.f;
-    }
-    fix = __builtin_amdgcn_readfirstlane((int)__any(inexact));
-  }
-  const DecodeMasks<BITS> dm = decode_masks<BITS>();
+  // fp16 data: per unit one matrix-core product of the prescaled activations
+  // with the subnormal codes (sum x q 2^-24) per column set, and one with the
+  // place values 2^e (sum x, shared by the VEC column sets); per group the
+  // scale and zero point are applied to the two sums in fp32. bf16 data:
+  // q - z is formed in fp32 per code (czf = 1024 2^-e + z, or z alone for
+  // 1-bit codes) and rounded once to bf16.
+  const DecodeMasks<BITS> dm = decode_masks<BITS, !BF>();
+  const f16x8 ones = place_ones<BITS>();
   f32x4 total[VEC];
 #pragma unroll
   for (int v = 0; v < VEC; ++v) total[v] = f32x4{0.f, 0.f, 0.f, 0.f};
   const u32x4* xrow = OWN ? xs + (wave * WSLOTS + m * WROW + j) : xs + (m * XROW + 4 * ua + j);  // unit ua + c at xrow[4 c]
-  // c per pair class and column for group slot gi, in fp16 arithmetic (one
-  // rounding of the exact -(1024 2^-e + z)).
-  auto group_zc = [&](int gi, f16x2 (&zc)[NPC][VEC]) {
-#pragma unroll
-    for (int v = 0; v < VEC; ++v) {
-      const f16 zh = __builtin_bit_cast(f16, half_bits<VEC>(zraw[gi], v));
-      const f16x2 zz = f16x2{zh, zh};
-#pragma unroll
-      for (int c = 0; c < NPC; ++c) {
-        const f16x2 base = f16x2{(f16)(1024.f / (float)(1 << code_exp<BITS>(c, 0))),
-                                 (f16)(1024.f / (float)(1 << code_exp<BITS>(c, 1)))};
-        zc[c][v] = -(base + zz);
-      }
-    }
-  };
 #pragma unroll
   for (int gi = 0; gi < GPW; ++gi) {
     float sc[VEC], czf[NPC][VEC];
-    f16x2 zc[NPC][VEC];
 #pragma unroll
     for (int v = 0; v < VEC; ++v) {
       sc[v] = bits_to_float<BF>(half_bits<VEC>(sraw[gi], v));
@@ -266,10 +267,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_wave_kernel(GemvArgs g) {
         for (int c = 0; c < NPC; ++c) czf[c][v] = SPLIT_E ? zf : 1024.f / (float)(1 << code_exp<BITS>(c, 0)) + zf;
       }
     }
-    if constexpr (!BF) group_zc(gi, zc);
     f32x4 acc[VEC];
 #pragma unroll
     for (int v = 0; v < VEC; ++v) acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 xsum = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int cu = 0; cu < GU; ++cu) {
       const int c = gi * GU + cu;
@@ -277,9 +278,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_wave_kernel(GemvArgs g) {
 #pragma unroll
       for (int v = 0; v < VEC; ++v) {
         uint32_t b[4];
-        decode8<BITS>(word_at<VEC>(wv[c][0], v), NW > 1 ? word_at<VEC>(wv[c][NW - 1], v) : 0u, j, dm, b);
-        uint32_t d[4];
+        decode8<BITS, !BF>(word_at<VEC>(wv[c][0], v), NW > 1 ? word_at<VEC>(wv[c][NW - 1], v) : 0u, j, dm, b);
         if constexpr (BF) {
+          uint32_t d[4];
           // A factor of 1 is kept opaque: the compiler would otherwise fold
           // fma(h, 1, c) into a conversion and an add, where the
           // mixed-precision FMA (v_fma_mix_f32) takes the fp16 half as is.
@@ -302,61 +303,23 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_wave_kernel(GemvArgs g) {
           const bf16x8 B = __builtin_bit_cast(bf16x8, u32x4{d[0], d[1], d[2], d[3]});
           acc[v] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[v], 0, 0, 0);
         } else {
-#pragma unroll
-          for (int p = 0; p < 4; ++p) d[p] = as_u32(scale_add<BITS>(p, as_f16x2(b[p]), zc[pair_class<BITS>(p)][v]));
           const f16x8 A = __builtin_bit_cast(f16x8, araw);
-          acc[v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, pack8(d[0], d[1], d[2], d[3]), acc[v], 0, 0, 0);
+          acc[v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, pack8(b[0], b[1], b[2], b[3]), acc[v], 0, 0, 0);
         }
       }
+      if constexpr (!BF) xsum = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, araw), ones, xsum, 0, 0, 0);
     }
+    if constexpr (BF) {
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) total[v] += sc[v] * acc[v];
-  }
-  if constexpr (!BF) {
-    if (fix) {  // scalar, once per wave: groups whose zero points leave a remainder
+      for (int v = 0; v < VEC; ++v) total[v] += sc[v] * acc[v];
+    } else {
+      // s 2^24 (acc - z 2^-24 sum x): both power-of-two factors are exact.
 #pragma unroll
-      for (int gi = 0; gi < GPW; ++gi) {
-        // The group's scales and zero points are requested again (from L2
-        // by now), so that their registers need not live through the units.
-        HT sh[HW], zh[HW];
-        const uint32_t off = ((uint32_t)(g0 + gi) * (uint32_t)g.N + (uint32_t)ncc) * 2u;
-        load_halves<VEC>(rs, off, sh);
-        load_halves<VEC>(rz, off, zh);
-        f16x2 zc[NPC][VEC];
+      for (int v = 0; v < VEC; ++v) {
+        const float zq = half_bits_to_float(half_bits<VEC>(zraw[gi], v)) * 0x1p-24f;
+        const float sq = sc[v] * 0x1p24f;
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) {
-          const f16 zhh = __builtin_bit_cast(f16, half_bits<VEC>(zh, v));
-          const f16x2 zz = f16x2{zhh, zhh};
-#pragma unroll
-          for (int c = 0; c < NPC; ++c) {
-            const f16x2 base = f16x2{(f16)(1024.f / (float)(1 << code_exp<BITS>(c, 0))),
-                                     (f16)(1024.f / (float)(1 << code_exp<BITS>(c, 1)))};
-            zc[c][v] = -(base + zz);
-          }
-        }
-        uint32_t rn[4][VEC];  // B operand halves: -r = -(c + 1024 2^-e) - z, each step exact in fp32
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) {
-          const float zf = half_bits_to_float(half_bits<VEC>(zh, v));
-#pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            const int c = pair_class<BITS>(p);
-            const float blo = 1024.f / (float)(1 << code_exp<BITS>(c, 0)), bhi = 1024.f / (float)(1 << code_exp<BITS>(c, 1));
-            rn[p][v] = as_u32(f16x2{(f16)((-(float)zc[c][v].x - blo) - zf), (f16)((-(float)zc[c][v].y - bhi) - zf)});
-          }
-        }
-        f32x4 acc[VEC];
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int cu = 0; cu < GU; ++cu) {
-          const f16x8 A = __builtin_bit_cast(f16x8, xrow[4 * (gi * GU + cu)]);
-#pragma unroll
-          for (int v = 0; v < VEC; ++v)
-            acc[v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, pack8(rn[0][v], rn[1][v], rn[2][v], rn[3][v]), acc[v], 0, 0, 0);
-        }
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) total[v] += bits_to_float<false>(half_bits<VEC>(sh, v)) * acc[v];
+        for (int i = 0; i < 4; ++i) total[v][i] = __builtin_fmaf(sq, __builtin_fmaf(-zq, xsum[i], acc[v][i]), total[v][i]);
       }
     }
   }
