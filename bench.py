@@ -44,7 +44,6 @@ prefill launches):
   gemm_int4_g128  the prefill shape again with 4-bit codes in groups of 128
   bf16          the headline decode and the prefill products with bf16 data
   readme_shapes the prefill kernel at the README's benchmark shapes (4-bit g128)
-  gptq_convert  the load-time conversions of GPTQModel-format inputs
   floors        an empty kernel as a graph node, a dense MFMA loop
   cpu_baseline  the CPU oracle on the headline workload on this host's cores
 """
@@ -369,45 +368,6 @@ def bench_readme_shapes(w, torch, datagen, clock):
     return out
 
 
-def bench_gptq_convert(w, torch, clock):
-    """The load-time conversions of GPTQModel-format inputs: average launch duration, bytes read and
-    written over it. The packed inputs are random 32-bit words (every pattern is a valid input)."""
-    dev = torch.device("cuda:0")
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(5)
-    lib = w.library()
-
-    def words(rows, cols):
-        return torch.randint(-2**31, 2**31 - 1, (rows, cols), dtype=torch.int32, device=dev, generator=gen)
-
-    out = {}
-    K, N = 2048, 6144
-    w10 = words((K + 9) // 10, N)
-    qw = torch.empty((K // 16, N), dtype=torch.int32, device=dev)
-    qlo = torch.empty((K // 32, N), dtype=torch.int32, device=dev)
-
-    def repack(i, sp):
-        if lib.qmm_repack_3bit10(w10.data_ptr(), K, N, qw.data_ptr(), qlo.data_ptr(), sp) != 0:
-            raise RuntimeError(lib.qmm_last_error().decode())
-
-    us = clock.per_step_us(repack, 50)
-    nb = w10.nbytes + qw.nbytes + qlo.nbytes
-    out["repack_3bit10"] = {"K": K, "N": N, "us_per_launch": round(us, 3), "bytes": nb, "GB/s": round(nb / us / 1e3, 1)}
-    G, N, bits = 64, 11008, 2
-    qz = words(G, (N + 15) // 16)
-    zeros = torch.empty((G, N), dtype=torch.float16, device=dev)
-
-    def unpack(i, sp):
-        if lib.qmm_unpack_qzeros(qz.data_ptr(), G, N, bits, zeros.data_ptr(), sp) != 0:
-            raise RuntimeError(lib.qmm_last_error().decode())
-
-    us = clock.per_step_us(unpack, 50)
-    nb = qz.nbytes + zeros.nbytes
-    out["unpack_qzeros"] = {"G": G, "N": N, "bits": bits, "us_per_launch": round(us, 3), "bytes": nb,
-                            "GB/s": round(nb / us / 1e3, 1)}
-    return out
-
-
 def bench_floors(torch, clock, probes):
     sink = torch.zeros(1 << 16, dtype=torch.int32, device="cuda:0")
 
@@ -640,7 +600,6 @@ def run(args, torch, datagen, w):
             p.free()
         out["bf16"] = bf
         out["readme_shapes"] = bench_readme_shapes(w, torch, datagen, clock)
-        out["gptq_convert"] = bench_gptq_convert(w, torch, clock)
         out["floors"] = bench_floors(torch, clock, probes)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(datagen, head_d, head_wl, args.cpu_seconds)

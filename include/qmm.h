@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define QMM_ABI_VERSION 5
+#define QMM_ABI_VERSION 6
 
 typedef enum qmm_status {
   QMM_OK = 0,
@@ -308,49 +308,6 @@ qmm_status qmm_gemm_ex(const uint16_t* x, int M, int K,
                        const uint16_t* zeros, const uint16_t* scales, const uint16_t* bias,
                        int N, int bits, int group_size, unsigned flags,
                        uint16_t* y, hipStream_t stream);
-
-/*
- * GPTQModel-format inputs. GPTQModel-Compatible Triton Kernel README, "API
- * Reference" (qzeros: the packed quantized zero points) and "Quantization
- * Format" (int32 words of 16, 10, 8 or 4 values for 2, 3, 4 or 8 bits, the
- * 3-bit words padded). The README does not say where a value sits in its word
- * or along which axis the zero points are packed. Read here as: value i of a
- * word at bit offset i * bits, lowest first (3-bit words hold 10 values in
- * bits 0-29, bits 30-31 unused); weights packed along K, zero points along N;
- * the last word of a row or column partly filled; the stored zero point is
- * used as is (w = scale * (q - zero), "Dequantization Formula"). In this
- * reading 2-, 4- and 8-bit GPTQModel weight words are the K-major words the
- * products take; the two calls below convert the rest, once, at load time.
- */
-
-/*
- * qmm_unpack_qzeros -- packed zero points -> (G, N) fp16 zero points.
- *   qzeros  (G, ceil(N / e)) int32, e = 16, 10, 8, 4 for bits 2, 3, 4, 8;
- *           zero point n of group g in word n / e of row g at bit offset
- *           (n % e) * bits
- *   zeros   (G, N) fp16 output: the integer zero points, exact
- * Requirements: bits in {2, 3, 4, 8} (QMM_ERR_BITS); G, N >= 1 (QMM_ERR_SHAPE);
- * qzeros 4-byte and zeros 2-byte aligned (QMM_ERR_ALIGN).
- */
-qmm_status qmm_unpack_qzeros(const int32_t* qzeros, int G, int N, int bits,
-                             uint16_t* zeros, hipStream_t stream);
-
-/* qmm_unpack_qzeros writing bf16 zero points (exact: integers below 256). */
-qmm_status qmm_unpack_qzeros_bf16(const int32_t* qzeros, int G, int N, int bits,
-                                  uint16_t* zeros, hipStream_t stream);
-
-/*
- * qmm_repack_3bit10 -- 3-bit GPTQModel weights, 10 codes per word packed
- * along K, -> the two planes of the 3-bit layout, as qmm_pack writes them.
- *   qweight10   (ceil(K / 10), N) int32; code k of column n in word k / 10 at
- *               bit offset 3 (k % 10); bits 30-31 and the slots past K ignored
- *   qweight     (K / 16, N) int32 output: the 2-bit plane of q >> 1
- *   qweight_lo  (K / 32, N) int32 output: the 1-bit plane of q & 1
- * Requirements: K a positive multiple of 32 (the planes' granularity) and
- * N >= 1 (QMM_ERR_SHAPE); every pointer 4-byte aligned (QMM_ERR_ALIGN).
- */
-qmm_status qmm_repack_3bit10(const int32_t* qweight10, int K, int N,
-                             int32_t* qweight, int32_t* qweight_lo, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -5,6 +5,5 @@ from .qmm_oracle import (  # noqa: F401
     dequantize_bf16, dequantize_fp16, elements_per_word, f64_to_bf16,
     group_rows, matmul, matmul_triple_loop, num_groups, pack, pack_3bit, pack_kmajor, parity_bound, parity_report,
     quantized_matmul, quantized_matmul_codes, unpack, unpack_3bit, unpack_kmajor,
-    GPTQ_BITS, gptq_values_per_word, gptqmodel_quantized_matmul, pack_3bit10, pack_qzeros, unpack_3bit10,
-    unpack_qzeros, STRIP_COLS, to_strips, from_strips,
+    STRIP_COLS, to_strips, from_strips,
 )

@@ -54,10 +54,7 @@ K * 2**-53). The matrix product uses numpy's float64 matmul as a library step.
 
 Parity pins: every function here is pinned by CPU tests (hand-worked words and
 products from the definitions, exact integer and rational recomputation,
-invariants). The GPTQModel-format functions at the end (packed zero points,
-3-bit words of 10 values) are "parity unpinned" against the pages: the README
-gives how many values a word holds but not where they sit, so their pins fix
-them to the reading stated there, not to a layout the pages print.
+invariants).
 """
 from __future__ import annotations
 
@@ -313,26 +310,7 @@ def parity_report(y_dev: np.ndarray, y_ref: np.ndarray, a: np.ndarray, rel_tol: 
     }
 
 
-# ---------------------------------------------------------------- GPTQModel-format variants
-#
-# GPTQModel-Compatible Triton Kernel README, "Quantization Format": weights are
-# packed into int32 words, 16 values per word for 2 bits, 10 for 3 bits (with
-# padding), 8 for 4 bits and 4 for 8 bits; "API Reference": qzeros are the
-# packed quantized zero points. The README says neither where a value sits in
-# its word nor along which axis the zero points are packed. Reading taken here
-# (parity unpinned against the pages):
-#  * value i of a word sits at bit offset i * bits, lowest first; a 3-bit word
-#    holds 10 values in bits 0-29 and bits 30-31 are zero;
-#  * weights are packed along K, as in the K-major layout above: (ceil(K / e), N)
-#    words, e values per word, the last word row partly filled when e does not
-#    divide K;
-#  * zero points are packed along N, one row of words per group:
-#    (G, ceil(N / e)) words, the last word of a row partly filled;
-#  * the dequantization is plain q - z, with no offset on the stored zero point
-#    ("Dequantization Formula").
-
-GPTQ_BITS = (2, 3, 4, 8)
-
+# ---------------------------------------------------------------- strip-major storage order
 
 STRIP_COLS = 16
 
@@ -353,66 +331,3 @@ def from_strips(strips: np.ndarray, N: int) -> np.ndarray:
     for n in range(N):
         out[:, n] = strips[n // STRIP_COLS, :, n % STRIP_COLS]
     return out
-
-
-def gptq_values_per_word(bits: int) -> int:
-    """Values per int32 word in the GPTQModel format: 16, 10, 8, 4 for 2, 3, 4, 8 bits."""
-    if bits not in GPTQ_BITS:
-        raise ValueError(f"the GPTQModel format has no {bits}-bit packing")
-    return 10 if bits == 3 else 32 // bits
-
-
-def pack_qzeros(zeros_int: np.ndarray, bits: int) -> np.ndarray:
-    """(G, N) integer zero points -> (G, ceil(N / e)) int32 words, packed along N."""
-    z = np.asarray(zeros_int).astype(np.uint32)
-    G, N = z.shape
-    e = gptq_values_per_word(bits)
-    mask = np.uint32((1 << bits) - 1)
-    words = np.zeros((G, -(-N // e)), dtype=np.uint32)
-    for n in range(N):
-        words[:, n // e] |= (z[:, n] & mask) << np.uint32((n % e) * bits)
-    return words.view(np.int32)
-
-
-def unpack_qzeros(qzeros: np.ndarray, bits: int, N: int) -> np.ndarray:
-    """(G, ceil(N / e)) int32 words -> (G, N) uint8 zero points; inverse of ``pack_qzeros``."""
-    u = np.asarray(qzeros).view(np.uint32)
-    e = gptq_values_per_word(bits)
-    if u.shape[1] * e < N:
-        raise ValueError("too few words per row for N")
-    mask = np.uint32((1 << bits) - 1)
-    z = np.empty((u.shape[0], N), dtype=np.uint8)
-    for n in range(N):
-        z[:, n] = (u[:, n // e] >> np.uint32((n % e) * bits)) & mask
-    return z
-
-
-def pack_3bit10(codes: np.ndarray) -> np.ndarray:
-    """(K, N) codes in [0, 7] -> (ceil(K / 10), N) int32 words, 10 codes per word along K."""
-    q = np.asarray(codes).astype(np.uint32)
-    K, N = q.shape
-    words = np.zeros((-(-K // 10), N), dtype=np.uint32)
-    for k in range(K):
-        words[k // 10] |= (q[k] & np.uint32(7)) << np.uint32(3 * (k % 10))
-    return words.view(np.int32)
-
-
-def unpack_3bit10(words: np.ndarray, K: int) -> np.ndarray:
-    """(ceil(K / 10), N) int32 words -> (K, N) uint8 codes; inverse of ``pack_3bit10``."""
-    u = np.asarray(words).view(np.uint32)
-    if u.shape[0] * 10 < K:
-        raise ValueError("too few word rows for K")
-    q = np.empty((K, u.shape[1]), dtype=np.uint8)
-    for k in range(K):
-        q[k] = (u[k // 10] >> np.uint32(3 * (k % 10))) & np.uint32(7)
-    return q
-
-
-def gptqmodel_quantized_matmul(x, qweight, qzeros, scales, bits: int, group_size: int, bias=None):
-    """Reference for the README's ``gptqmodel_quantized_matmul(x, qweight, qzeros, scales, bits,
-    group_size)`` with weights and zero points in the GPTQModel format read above. Returns (y, a)."""
-    K = np.asarray(x).shape[1]
-    N = np.asarray(scales).shape[1]
-    codes = unpack_3bit10(qweight, K) if bits == 3 else unpack_kmajor(qweight, bits, K)
-    zeros = unpack_qzeros(qzeros, bits, N)
-    return quantized_matmul_codes(x, codes, zeros, scales, group_size, bias)

@@ -117,12 +117,6 @@ static void conversions(void) {
   EXPECT(qmm_dequant(qw, qw, z, z, 256, 64, 5, 128, P(uint16_t), nullptr), QMM_ERR_BITS);
   EXPECT(qmm_dequant(qw, qw, z, z, 256, 64, 4, 48, P(uint16_t), nullptr), QMM_ERR_GROUP);
   EXPECT(qmm_dequant_bf16(qw, qw, z, z, 256, 64, 4, 128, (uint16_t*)((char*)A + 1), nullptr), QMM_ERR_ALIGN);
-  EXPECT(qmm_unpack_qzeros(qw, 4, 64, 1, P(uint16_t), nullptr), QMM_ERR_BITS);
-  EXPECT(qmm_unpack_qzeros(qw, INT_MAX, INT_MAX, 4, P(uint16_t), nullptr), QMM_ERR_SHAPE);
-  EXPECT(qmm_unpack_qzeros_bf16(nullptr, 4, 64, 4, P(uint16_t), nullptr), QMM_ERR_NULL);
-  EXPECT(qmm_repack_3bit10(qw, 48, 64, qw, qw, nullptr), QMM_ERR_SHAPE);
-  EXPECT(qmm_repack_3bit10(qw, INT_MAX - 31, INT_MAX, qw, qw, nullptr), QMM_ERR_SHAPE);
-  EXPECT(qmm_repack_3bit10(qw, 64, 64, qw, nullptr, nullptr), QMM_ERR_NULL);
   int32_t* st = P(int32_t);
   for (int dir = 0; dir < 2; ++dir) {
     auto f = dir == 0 ? qmm_to_strips : qmm_from_strips;

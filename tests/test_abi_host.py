@@ -33,7 +33,7 @@ def test_header_declares_the_boundary():
     assert _declared() == sorted(
         ["qmm_abi_version", "qmm_status_string", "qmm_last_error", "qmm_pack", "qmm_unpack", "qmm_dequant",
          "qmm_workspace_bytes", "qmm_gemv", "qmm_gemm", "qmm_dequant_bf16", "qmm_gemv_bf16", "qmm_gemm_bf16",
-         "qmm_unpack_qzeros", "qmm_unpack_qzeros_bf16", "qmm_repack_3bit10", "qmm_gemv_noalloc",
+         "qmm_gemv_noalloc",
          "qmm_gemv_plan_info", "qmm_gemm_plan_info", "qmm_strips_bytes", "qmm_to_strips", "qmm_from_strips",
          "qmm_gemv_ex", "qmm_gemm_ex"])
 
@@ -52,7 +52,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = _lib()
-    assert lib.qmm_abi_version() == 5
+    assert lib.qmm_abi_version() == 6
     names = [lib.qmm_status_string(i).decode() for i in range(9)]
     assert names == ["QMM_OK", "QMM_ERR_NULL", "QMM_ERR_BITS", "QMM_ERR_SHAPE", "QMM_ERR_GROUP",
                      "QMM_ERR_ALIGN", "QMM_ERR_WORKSPACE", "QMM_ERR_HIP", "QMM_ERR_FLAGS"]
@@ -178,46 +178,11 @@ def test_dequant_rejects_before_launch(host_only, suffix):
     assert lib.qmm_last_error().decode() != ""
 
 
-@pytest.mark.parametrize("suffix", SUFFIXES)
-def test_unpack_qzeros_rejects_before_launch(host_only, suffix):
-    f = getattr(host_only, "qmm_unpack_qzeros" + suffix)
-    assert f(A, 4, 64, 1, A, None) == 2       # 1-bit zero points are not a GPTQModel packing
-    assert f(A, 4, 64, 5, A, None) == 2
-    assert f(A, 0, 64, 4, A, None) == 3
-    assert f(A, 4, 0, 4, A, None) == 3
-    assert f(None, 4, 64, 4, A, None) == 1
-    assert f(A, 4, 64, 4, None, None) == 1
-    assert f(A + 2, 4, 64, 4, A, None) == 5   # qzeros not 4-byte aligned
-    assert f(A, 4, 64, 4, A + 1, None) == 5   # zeros not 2-byte aligned
-    assert host_only.qmm_last_error().decode() != ""
-
-
-def test_repack_3bit10_rejects_before_launch(host_only):
-    f = host_only.qmm_repack_3bit10
-    assert f(A, 48, 64, A, A, None) == 3      # K % 32
-    assert f(A, 0, 64, A, A, None) == 3
-    assert f(A, 64, 0, A, A, None) == 3
-    assert f(None, 64, 64, A, A, None) == 1
-    assert f(A, 64, 64, A, None, None) == 1
-    assert f(A, 64, 64, A + 2, A, None) == 5
-
-
 def test_binding_refuses_cpu_tensors():
     import torch
     import weight_only_group_amd as w
     with pytest.raises(ValueError):
         w.qmm_pack(torch.zeros((64, 8), dtype=torch.uint8), 4)
-    # GPTQModel-format calls check their arguments before any conversion
-    x16 = torch.zeros((1, 64), dtype=torch.float16)
-    with pytest.raises(TypeError):
-        w.gptqmodel_quantized_matmul(x16, torch.zeros((8, 8), dtype=torch.int32), torch.zeros((1, 1), dtype=torch.int32),
-                                     None, 4, -1)
-    with pytest.raises(ValueError):
-        w.qmm_unpack_qzeros(torch.zeros((1, 1), dtype=torch.int32), 4, 8)
-    with pytest.raises(ValueError):
-        w.qmm_repack_3bit10(torch.zeros((7, 8), dtype=torch.int32), 64)
-    with pytest.raises(ValueError):
-        w.gptq_values_per_word(5)
     with pytest.raises((ValueError, TypeError)):
         w.qmm_gemv(torch.zeros((1, 64), dtype=torch.float16), torch.zeros((8, 8), dtype=torch.int32), None,
                    torch.zeros((1, 8), dtype=torch.float16), torch.zeros((1, 8), dtype=torch.float16), 4, -1)

@@ -16,9 +16,6 @@ Functions mirror the C ABI (include/qmm.h):
 * ``qmm_gemm(x, qweight, qweight_lo, zeros, scales, bits, group_size, bias=None)`` (any M)
 * ``quantized_matmul(x, qweight, qzeros, scales, bits, group_size, qweight_lo=None, bias=None)``:
   the functional form, M <= 16 to the GEMV, larger M to the GEMM.
-* ``qmm_unpack_qzeros(qzeros, bits, N, dtype)``, ``qmm_repack_3bit10(qweight10, K)`` and
-  ``gptqmodel_quantized_matmul(x, qweight, qzeros, scales, bits, group_size, bias=None)``:
-  inputs in the GPTQModel format (packed zero points, 3-bit words of 10 values).
 
 Bit widths 1, 2, 3, 4 and 8. The floating-point data (x, zeros, scales, bias,
 the result) are all float16 or all bfloat16; bfloat16 calls the ``_bf16``
@@ -44,11 +41,11 @@ STATUS_NAMES = {
 EXPORTS = (
     "qmm_abi_version", "qmm_status_string", "qmm_last_error", "qmm_pack", "qmm_unpack", "qmm_dequant",
     "qmm_workspace_bytes", "qmm_gemv", "qmm_gemm", "qmm_dequant_bf16", "qmm_gemv_bf16", "qmm_gemm_bf16",
-    "qmm_unpack_qzeros", "qmm_unpack_qzeros_bf16", "qmm_repack_3bit10", "qmm_gemv_noalloc",
+    "qmm_gemv_noalloc",
     "qmm_gemv_plan_info", "qmm_gemm_plan_info", "qmm_strips_bytes", "qmm_to_strips", "qmm_from_strips",
     "qmm_gemv_ex", "qmm_gemm_ex",
 )
-ABI_VERSION = 5
+ABI_VERSION = 6
 QMM_BF16, QMM_STRIPS = 1, 2  # flags of qmm_gemv_ex / qmm_gemm_ex
 STRIP_COLS = 16
 DTYPES = (torch.float16, torch.bfloat16)
@@ -86,10 +83,6 @@ def _declare(lib):
         f.restype, f.argtypes = I, [P, I, I, P, P, P, P, P, I, I, I, P, P, SZ, P]
         f = getattr(lib, "qmm_gemm" + suffix)
         f.restype, f.argtypes = I, [P, I, I, P, P, P, P, P, I, I, I, P, P]
-        f = getattr(lib, "qmm_unpack_qzeros" + suffix)
-        f.restype, f.argtypes = I, [P, I, I, I, P, P]
-    lib.qmm_repack_3bit10.restype = I
-    lib.qmm_repack_3bit10.argtypes = [P, I, I, P, P, P]
     lib.qmm_gemv_noalloc.restype = I
     lib.qmm_gemv_noalloc.argtypes = [P, I, I, P, P, P, P, P, I, I, I, P, P]
     lib.qmm_gemv_plan_info.restype = I
@@ -429,69 +422,3 @@ def quantized_matmul(x, qweight, qzeros, scales, bits: int, group_size: int, qwe
             if e.status != 3:  # QMM_ERR_SHAPE: shape beyond the decode kernel's staging limits
                 raise
     return qmm_gemm(x, qweight, qweight_lo, qzeros, scales, bits, group_size, bias=bias)
-
-
-GPTQ_BITS = (2, 3, 4, 8)
-
-
-def gptq_values_per_word(bits: int) -> int:
-    """Values per int32 word of the GPTQModel format: 16, 10, 8, 4 for 2, 3, 4, 8 bits."""
-    if bits not in GPTQ_BITS:
-        raise ValueError(f"the GPTQModel format has no {bits}-bit packing")
-    return 10 if bits == 3 else 32 // bits
-
-
-def qmm_unpack_qzeros(qzeros: torch.Tensor, bits: int, N: int, dtype=torch.float16) -> torch.Tensor:
-    """(G, ceil(N / e)) int32 packed zero points -> (G, N) zero points in ``dtype``."""
-    _gpu(qzeros, "qzeros", torch.int32)
-    if dtype not in DTYPES:
-        raise TypeError(f"dtype must be float16 or bfloat16 (got {dtype})")
-    G = qzeros.shape[0]
-    if bits in GPTQ_BITS and qzeros.shape[1] != -(-N // gptq_values_per_word(bits)):
-        raise ValueError(f"qzeros has {qzeros.shape[1]} words per row; N={N} at {bits} bits needs "
-                         f"{-(-N // gptq_values_per_word(bits))}")
-    dev = qzeros.device
-    zeros = torch.empty((G, N), dtype=dtype, device=dev)
-    with torch.cuda.device(dev):
-        _check(_entry("qmm_unpack_qzeros", dtype)(_ptr(qzeros), G, N, bits, _ptr(zeros), _stream(dev)),
-               "qmm_unpack_qzeros")
-    return zeros
-
-
-def qmm_repack_3bit10(qweight10: torch.Tensor, K: int):
-    """(ceil(K / 10), N) int32 3-bit words of 10 codes -> (qweight, qweight_lo), the two planes."""
-    _gpu(qweight10, "qweight10", torch.int32)
-    N = qweight10.shape[1]
-    if qweight10.shape[0] != -(-K // 10):
-        raise ValueError(f"qweight10 has {qweight10.shape[0]} rows; K={K} needs {-(-K // 10)}")
-    dev = qweight10.device
-    shp, shp_lo = packed_shapes(K, N, 3)
-    qw = torch.empty(shp, dtype=torch.int32, device=dev)
-    qlo = torch.empty(shp_lo, dtype=torch.int32, device=dev)
-    with torch.cuda.device(dev):
-        _check(library().qmm_repack_3bit10(_ptr(qweight10), K, N, _ptr(qw), _ptr(qlo), _stream(dev)),
-               "qmm_repack_3bit10")
-    return qw, qlo
-
-
-def gptqmodel_quantized_matmul(x, qweight, qzeros, scales, bits: int, group_size: int, bias=None):
-    """output = x @ dequantize(qweight) (+ bias) with GPTQModel-format weights and zero points.
-
-    The zero points (and 3-bit weights) are converted on the GPU first, then the product runs as
-    ``quantized_matmul``. A caller that multiplies by the same weights again converts them once
-    with ``qmm_unpack_qzeros`` / ``qmm_repack_3bit10`` and calls ``quantized_matmul`` instead.
-    """
-    dt = _data_dtype(x, "x")
-    if x.dim() != 2:
-        raise ValueError("x must be (M, K)")
-    _gpu(scales, "scales", dt)
-    if bits not in GPTQ_BITS:
-        raise ValueError(f"the GPTQModel format has no {bits}-bit packing (bits must be one of {GPTQ_BITS})")
-    K = x.shape[1]
-    N = scales.shape[1]
-    zeros = qmm_unpack_qzeros(qzeros, bits, N, dt)
-    if bits == 3:
-        qw, qlo = qmm_repack_3bit10(qweight, K)
-    else:
-        qw, qlo = qweight, None
-    return quantized_matmul(x, qw, zeros, scales, bits, group_size, qweight_lo=qlo, bias=bias)

@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 SOURCES = ("api.hip", "pack.hip", "dequant.hip", "gemv.hip", "gemv_wave_b1.hip", "gemv_wave_b2.hip",
-           "gemv_wave_b3.hip", "gemv_wave_b4.hip", "gemv_wave_b8.hip", "gemm.hip", "gptq.hip", "strips.hip")
+           "gemv_wave_b3.hip", "gemv_wave_b4.hip", "gemv_wave_b8.hip", "gemm.hip", "strips.hip")
 LIB_NAME = "libqmm.so"
 # Reference kernels for measurement (empty launch, streaming read, MFMA loop);
 # a library of their own, outside the qmm ABI.

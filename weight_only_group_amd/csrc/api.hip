@@ -9,7 +9,6 @@
 
 #include "../../include/qmm.h"
 #include "common.h"
-#include "gptq.h"
 
 namespace qmm {
 
@@ -239,20 +238,6 @@ qmm_status gemv_noalloc_impl(const uint16_t* x, int M, int K, const int32_t* qwe
                   "qmm_gemv_noalloc launch");
 }
 
-qmm_status unpack_qzeros_impl(const int32_t* qzeros, int G, int N, int bits, uint16_t* zeros, bool bf16,
-                              hipStream_t stream) {
-  if (bits != 2 && bits != 3 && bits != 4 && bits != 8)
-    return fail(QMM_ERR_BITS, "bits=%d: packed zero points come in 2, 3, 4 or 8 bits", bits);
-  if (G < 1 || N < 1) return fail(QMM_ERR_SHAPE, "G=%d and N=%d must be >= 1", G, N);
-  if ((unsigned long long)G * N * 2 >= (1ull << 32)) return fail(QMM_ERR_SHAPE, "zeros must be smaller than 4 GiB");
-  if (!qzeros || !zeros) return fail(QMM_ERR_NULL, "qzeros and zeros must not be NULL");
-  if (!aligned(qzeros, 4) || !aligned(zeros, 2))
-    return fail(QMM_ERR_ALIGN, "qzeros must be 4-byte aligned and zeros 2-byte aligned");
-  return from_hip(qmm::launch_unpack_qzeros(reinterpret_cast<const uint32_t*>(qzeros), G, N, bits, zeros, bf16,
-                                            stream),
-                  "qmm_unpack_qzeros launch");
-}
-
 qmm_status gemm_impl(const uint16_t* x, int M, int K, const int32_t* qweight, const int32_t* qweight_lo,
                     const uint16_t* zeros, const uint16_t* scales, const uint16_t* bias, int N, int bits,
                     int group_size, uint16_t* y, bool bf16, bool strips, hipStream_t stream) {
@@ -428,30 +413,6 @@ qmm_status qmm_from_strips(const int32_t* strips, int rows, int N, int32_t* word
   return from_hip(qmm::launch_from_strips(reinterpret_cast<const uint32_t*>(strips), rows, N,
                                           reinterpret_cast<uint32_t*>(words), stream),
                   "qmm_from_strips launch");
-}
-
-qmm_status qmm_unpack_qzeros(const int32_t* qzeros, int G, int N, int bits, uint16_t* zeros, hipStream_t stream) {
-  return unpack_qzeros_impl(qzeros, G, N, bits, zeros, false, stream);
-}
-
-qmm_status qmm_unpack_qzeros_bf16(const int32_t* qzeros, int G, int N, int bits, uint16_t* zeros,
-                                  hipStream_t stream) {
-  return unpack_qzeros_impl(qzeros, G, N, bits, zeros, true, stream);
-}
-
-qmm_status qmm_repack_3bit10(const int32_t* qweight10, int K, int N, int32_t* qweight, int32_t* qweight_lo,
-                             hipStream_t stream) {
-  if (K < 32 || K % 32) return fail(QMM_ERR_SHAPE, "K=%d must be a positive multiple of 32", K);
-  if (N < 1) return fail(QMM_ERR_SHAPE, "N=%d must be >= 1", N);
-  if ((unsigned long long)((K + 9) / 10) * N * 4 >= (1ull << 32))
-    return fail(QMM_ERR_SHAPE, "qweight10 must be smaller than 4 GiB");
-  if (!qweight10 || !qweight || !qweight_lo) return fail(QMM_ERR_NULL, "qweight10, qweight and qweight_lo must not be NULL");
-  if (!aligned(qweight10, 4) || !aligned(qweight, 4) || !aligned(qweight_lo, 4))
-    return fail(QMM_ERR_ALIGN, "qweight10, qweight and qweight_lo must be 4-byte aligned");
-  return from_hip(qmm::launch_repack_3bit10(reinterpret_cast<const uint32_t*>(qweight10), K, N,
-                                            reinterpret_cast<uint32_t*>(qweight),
-                                            reinterpret_cast<uint32_t*>(qweight_lo), stream),
-                  "qmm_repack_3bit10 launch");
 }
 
 }  // extern "C"
