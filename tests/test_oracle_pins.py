@@ -80,6 +80,36 @@ def check_word_bijection(n_words=1 << 18, seed=7):
         assert np.array_equal(oracle.unpack_kmajor(oracle.pack_kmajor(codes, bits), bits, eps * 6), codes), bits
 
 
+def check_word_bijection_all_words_by_linearity(seed=11):
+    """The round trip holds for all 2^32 words: unpack is a bit permutation.
+
+    Unpacking moves word bit (k % eps) * bits + i to bit i of code k and does nothing else (shifts
+    and masks), so it is linear over GF(2): checked on random pairs, unpack(a ^ b) equals
+    unpack(a) ^ unpack(b). A linear map is fixed by its images of the 32 single-bit words; each
+    image is one code with one bit set, at code b // bits, bit b % bits, and the 32 images are
+    distinct, so unpack is a bijection of the 2^32 words onto the code arrays, and pack (checked to
+    invert it on the same basis) is its inverse everywhere."""
+    rng = np.random.default_rng(seed)
+    for bits in oracle.PLANE_BITS:
+        eps = 32 // bits
+        seen = set()
+        for b in range(32):
+            w = np.array([[np.uint32(1) << np.uint32(b)]], dtype=np.uint32).view(np.int32)
+            q = oracle.unpack_kmajor(w, bits, eps)[:, 0]
+            nz = np.nonzero(q)[0]
+            assert nz.tolist() == [b // bits], (bits, b, q.tolist())
+            assert int(q[nz[0]]) == 1 << (b % bits), (bits, b)
+            seen.add((int(nz[0]), int(q[nz[0]])))
+            assert np.array_equal(oracle.pack_kmajor(q[:, None], bits), w), (bits, b)
+        assert len(seen) == 32
+        a = rng.integers(0, 1 << 32, size=(64, 16), dtype=np.uint64).astype(np.uint32)
+        c = rng.integers(0, 1 << 32, size=(64, 16), dtype=np.uint64).astype(np.uint32)
+        ua = oracle.unpack_kmajor(a.view(np.int32), bits, 64 * eps)
+        uc = oracle.unpack_kmajor(c.view(np.int32), bits, 64 * eps)
+        uac = oracle.unpack_kmajor((a ^ c).view(np.int32), bits, 64 * eps)
+        assert np.array_equal(uac, ua ^ uc), bits
+
+
 def check_out_of_range_codes_masked():
     """A code wider than the field is masked to its low bits and never spills into a neighbour."""
     codes = np.zeros((8, 1), dtype=np.uint8)
@@ -506,6 +536,7 @@ def check_strips_round_trip_and_padding():
 CHECKS = [
     check_strips_hand_worked, check_strips_round_trip_and_padding,
     check_pack_words_hand_worked, check_ascending_nibbles, check_word_bijection,
+    check_word_bijection_all_words_by_linearity,
     check_out_of_range_codes_masked, check_three_bit_identity, check_dequant_examples_hand_worked,
     check_dequant_fp16_hand_worked, check_dequant_fp16_against_exact_rounding, check_bias_row,
     check_bf16_decode_every_pattern, check_bf16_encode_hand_worked, check_bf16_encode_against_exact_rounding,
