@@ -171,6 +171,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, size_
 }
 // Wait until at most n vector-memory operations of this wave are in flight
 // (s_waitcnt's vmcnt field, expcnt and lgkmcnt left unconstrained).
+#ifndef QMM_GEMM_SPREAD
+#define QMM_GEMM_SPREAD 1
+#endif
 #define QMM_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
 // A 16-byte-per-lane load from a buffer straight into LDS: lane l's bytes
@@ -225,6 +228,10 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
   constexpr int NW = Frag<BITS>::NW, NL = Frag<BITS>::NL;
   constexpr bool POST_SCALE = ZM == 2;
   constexpr int NG = ZM == 0 ? 2 : 1;  // rows of zero points / scales per slab
+  // Activation loads of a slab spread over its four steps (one 1 KiB load
+  // per wave and step) instead of four in one step, where they fill the
+  // texture unit's command queue and hold back the next instructions.
+  constexpr bool SPREAD = QMM_GEMM_SPREAD && CQ == 4 && NBUF == 3;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -310,15 +317,17 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
   // Nothing here branches, so the step's instructions stay one block.
   const __amdgpu_buffer_rsrc_t rnone = make_rsrc(g.x, 0);
   const uint32_t x_bytes = (uint32_t)g.M * (uint32_t)g.K * 2u;
-  auto dmaA = [&](int buf, int ks) {
+  // Load q of a wave's CQ loads of slab ks (each 1 KiB).
+  auto dmaA_part = [&](int buf, int ks, int q) {
     const uint32_t A = lds_offset(glds + buf * BM * BK);
     const __amdgpu_buffer_rsrc_t r = (!KTAIL && ks >= nk) ? rnone : rx;
+    uint32_t off = a_voff[q] + (uint32_t)ks * (BK * 2);
+    if constexpr (KTAIL) off = ks * BK + 8 * a_c[q] >= g.K ? x_bytes : off;
+    load_to_lds16(r, A + (gwave * CQ + q) * 1024, off);
+  };
+  auto dmaA = [&](int buf, int ks) {
 #pragma unroll
-    for (int q = 0; q < CQ; ++q) {
-      uint32_t off = a_voff[q] + (uint32_t)ks * (BK * 2);
-      if constexpr (KTAIL) off = ks * BK + 8 * a_c[q] >= g.K ? x_bytes : off;
-      load_to_lds16(r, A + (gwave * CQ + q) * 1024, off);
-    }
+    for (int q = 0; q < CQ; ++q) dmaA_part(buf, ks, q);
   };
   // Rows of the lane's fragments (32 apart) share their chunk swizzle.
   const int fr = (BM / WM) * wm + (lane & 31);
@@ -508,10 +517,12 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
       // Scheduling fence: each step's instructions stay in their step.
       __builtin_amdgcn_sched_barrier(0);
       if (s == 3) {
-        // This wave's loads of slab i + 1, issued NBUF - 1 slabs ago, are
-        // done: at least the weight loads of 4 (NBUF - 2) + 3 steps were
-        // issued after them, and loads complete in order.
-        QMM_WAIT_VMCNT(cmin((4 * (NBUF - 2) + 3) * NBI, 63));
+        // This wave's loads of slab i + 1 are done: loads complete in order,
+        // and at least this many were issued after its last one. Whole
+        // slabs (issued NBUF - 1 slabs ago): the weight loads of
+        // 4 (NBUF - 2) + 3 steps. Spread slabs (last quarter issued in step 2
+        // of slab i - 1): the weight loads and one quarter of four steps.
+        QMM_WAIT_VMCNT(cmin(SPREAD ? 4 * NBI + 4 : (4 * (NBUF - 2) + 3) * NBI, 63));
         __syncthreads();  // slab i + 1 is in LDS
       }
 #pragma unroll
@@ -536,7 +547,16 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
         loadB(Bn[0], gslab(i + 3), 0);
       }
       if (!POST_SCALE && s == 3) loadZS(Zc, gslab(i + 2));
-      if (s == 3) dmaA(cur, gslab(i + NBUF));  // every wave is past its reads of slab i
+      if constexpr (SPREAD) {
+        // A slab's four loads go out one per step: the first into slab i's
+        // buffer right after the barrier that ends its reads, the other three
+        // in steps 0-2 of the next slab (slab i + 2 into the buffer of slab
+        // i - 1, whose reads ended before the last barrier).
+        if (s == 3) dmaA_part(cur, gslab(i + NBUF), 0);
+        else dmaA_part((i + NBUF - 1) % NBUF, gslab(i + NBUF - 1), s + 1);
+      } else {
+        if (s == 3) dmaA(cur, gslab(i + NBUF));  // every wave is past its reads of slab i
+      }
       // Interleave: each MFMA is followed by a share of the step's other work.
       constexpr int NM = TM * TN;
 #pragma unroll
@@ -561,7 +581,8 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
 
   dmaA(0, gslab(0));
   dmaA(1, gslab(1));
-  dmaA(2, gslab(2));
+  if constexpr (SPREAD) dmaA_part(2, gslab(2), 0);  // its other quarters go out in slab 0's steps 0-2
+  else dmaA(2, gslab(2));
   if constexpr (NBUF > 3) dmaA(3, gslab(3));
 #pragma unroll
   for (int s = 0; s < 4; ++s) loadB(B0[s], gslab(0), s);
