@@ -93,9 +93,10 @@ template <int BITS, bool SUB = false> __device__ __forceinline__ DecodeMasks<BIT
   for (int p = 0; p < 4; ++p) {
     d.m[p] = BITS == 4 ? (p & 1 ? 0x00F000F0u : 0x000F000Fu)
            : BITS == 2 ? (p & 1 ? 0x000C000Cu : 0x00030003u)
+           : (BITS == 3 && SUB) ? (0x00060006u << (2 * p - (p > 0 ? 1 : 0)))  // pair p's 2-bit plane: bits 2p, 2p + 1 (pair 0: 1, 2)
            : BITS == 3 ? (p & 1 ? 0x00020002u : 0x000C000Cu)  // 2-bit plane at bits 2-3, 1-bit plane at bit 1
            : BITS == 1 ? ((1u << p) | (1u << (20 + p))) : 0u;
-    if (BITS == 1 || ((BITS == 2 || BITS == 3 || BITS == 4) && p < 2)) asm("" : "+v"(d.m[p]));
+    if (BITS == 1 || (BITS == 3 && SUB) || ((BITS == 2 || BITS == 3 || BITS == 4) && p < 2)) asm("" : "+v"(d.m[p]));
   }
   d.magic = SUB ? 0u : kMagic1024x2;
   if (!SUB) asm("" : "+s"(d.magic));
@@ -106,6 +107,13 @@ template <int BITS, bool SUB = false> __device__ __forceinline__ DecodeMasks<BIT
 // holds 1024 + 2^e q with e = code_exp(p, hi).
 template <int BITS> __host__ __device__ constexpr int code_exp(int p, int hi) {
   return BITS == 4 ? 4 * (p & 1) : BITS == 2 ? 2 * (p & 1) : BITS == 1 ? p + 4 * hi : BITS == 3 ? 1 : 0;
+}
+// The same for the subnormal form (decode8 with SUB): 3-bit pair p sits at
+// e = 0, 1, 3, 5, where its 2-bit plane bits already are (no shift for pairs
+// 1-3); 2-bit pair p at e = 2p, where it is in the word (no shift); every
+// other width as above.
+template <int BITS> __host__ __device__ constexpr int code_exp_sub(int p, int hi) {
+  return BITS == 3 ? (p == 0 ? 0 : 2 * p - 1) : BITS == 2 ? 2 * p : code_exp<BITS>(p, hi);
 }
 
 // Four fp16 pairs 1024 + 2^e q for the 8 codes lane group j takes from its
@@ -148,11 +156,17 @@ __device__ __forceinline__ void decode8(uint32_t w0, uint32_t w1, int j, const D
     b[3] = __builtin_amdgcn_perm(mag8, w1, 0x04030402u);
   } else if constexpr (BITS == 2) {
     const uint32_t ws = w0 >> (8 * (j & 1));
-    const uint32_t t = ws >> 4;
-    b[0] = bfi(dm.m[0], ws, magic);
-    b[1] = bfi(dm.m[1], ws, magic);
-    b[2] = bfi(dm.m[0], t, magic);
-    b[3] = bfi(dm.m[1], t, magic);
+    if constexpr (SUB) {
+      // subnormal form: pair p stays at bits 2p, 2p + 1 of each half (e = 2p)
+#pragma unroll
+      for (int p = 0; p < 4; ++p) b[p] = ws & (0x00030003u << (2 * p));
+    } else {
+      const uint32_t t = ws >> 4;
+      b[0] = bfi(dm.m[0], ws, magic);
+      b[1] = bfi(dm.m[1], ws, magic);
+      b[2] = bfi(dm.m[0], t, magic);
+      b[3] = bfi(dm.m[1], t, magic);
+    }
   } else {
     // plane2 word w0 holds q >> 1 for 16 k (slot i0 + p of pair p at bits
     // 2 (i0 + p) and 2 (i0 + p) + 16); plane1 word w1 holds q & 1 for the
@@ -163,10 +177,20 @@ __device__ __forceinline__ void decode8(uint32_t w0, uint32_t w1, int j, const D
     const uint32_t hs = w0 >> (2 * i0);
     const uint32_t t = w1 >> (16 * (j >> 1) + i0);
     const uint32_t ls = __builtin_amdgcn_perm(0u, t, 0x0C010C00u);  // bytes (0, -, 1, -) of t
-    b[0] = bfi(dm.m[0], hs << 2, bfi(dm.m[1], ls << 1, magic));
-    b[1] = bfi(dm.m[0], hs, bfi(dm.m[1], ls, magic));
-    b[2] = bfi(dm.m[0], hs >> 2, bfi(dm.m[1], ls >> 1, magic));
-    b[3] = bfi(dm.m[0], hs >> 4, bfi(dm.m[1], ls >> 2, magic));
+    if constexpr (SUB) {
+      // Subnormal form, pair p at e = code_exp_sub: (2 h + l) 2^e with the
+      // 2-bit plane where it already is (bits 2p, 2p + 1; pair 0 one place up)
+      // and the low bit just below it.
+      b[0] = bfi(dm.m[0], hs << 1, ls & 0x00010001u);
+      b[1] = bfi(dm.m[1], hs, ls & 0x00020002u);
+      b[2] = bfi(dm.m[2], hs, (ls << 1) & 0x00080008u);
+      b[3] = bfi(dm.m[3], hs, (ls << 2) & 0x00200020u);
+    } else {
+      b[0] = bfi(dm.m[0], hs << 2, bfi(dm.m[1], ls << 1, magic));
+      b[1] = bfi(dm.m[0], hs, bfi(dm.m[1], ls, magic));
+      b[2] = bfi(dm.m[0], hs >> 2, bfi(dm.m[1], ls >> 1, magic));
+      b[3] = bfi(dm.m[0], hs >> 4, bfi(dm.m[1], ls >> 2, magic));
+    }
   }
 }
 

@@ -66,7 +66,7 @@ __device__ __forceinline__ uint16_t half_bits(const typename HalfWords<VEC>::T (
 }
 
 // fp16 data: the codes enter the matrix cores as fp16 subnormals 2^e q 2^-24
-// (decode8 with SUB; e = code_exp, the code's place in the mantissa), which
+// (decode8 with SUB; e = code_exp_sub, the code's place in the mantissa), which
 // the matrix cores take exactly. The activations are staged with element
 // (p, hi) scaled by 2^-e, so every product is x q 2^-24 whatever the place,
 // and a B operand of 2^e gives the sum of x over the same k. Per group, the
@@ -76,9 +76,9 @@ template <int BITS>
 __device__ __forceinline__ u32x4 x_prescaled(u32x4 a) {
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    if (code_exp<BITS>(p, 0) != 0 || code_exp<BITS>(p, 1) != 0)
-      a[p] = as_u32(as_f16x2(a[p]) * f16x2{(f16)(1.0f / (float)(1 << code_exp<BITS>(p, 0))),
-                                           (f16)(1.0f / (float)(1 << code_exp<BITS>(p, 1)))});
+    if (code_exp_sub<BITS>(p, 0) != 0 || code_exp_sub<BITS>(p, 1) != 0)
+      a[p] = as_u32(as_f16x2(a[p]) * f16x2{(f16)(1.0f / (float)(1 << code_exp_sub<BITS>(p, 0))),
+                                           (f16)(1.0f / (float)(1 << code_exp_sub<BITS>(p, 1)))});
   }
   return a;
 }
@@ -87,8 +87,8 @@ __device__ __forceinline__ f16x8 place_ones() {
   f16x8 o;
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    o[2 * p] = (f16)(float)(1 << code_exp<BITS>(p, 0));
-    o[2 * p + 1] = (f16)(float)(1 << code_exp<BITS>(p, 1));
+    o[2 * p] = (f16)(float)(1 << code_exp_sub<BITS>(p, 0));
+    o[2 * p + 1] = (f16)(float)(1 << code_exp_sub<BITS>(p, 1));
   }
   return o;
 }
@@ -309,9 +309,13 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_wave_kernel(GemvArgs g) {
       }
       if constexpr (!BF) xsum = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, araw), ones, xsum, 0, 0, 0);
     }
+    // One row: only element 0 (row 0) of the accumulators is used.
+    constexpr int NE = M1 ? 1 : 4;
     if constexpr (BF) {
 #pragma unroll
-      for (int v = 0; v < VEC; ++v) total[v] += sc[v] * acc[v];
+      for (int v = 0; v < VEC; ++v)
+#pragma unroll
+        for (int i = 0; i < NE; ++i) total[v][i] = __builtin_fmaf(sc[v], acc[v][i], total[v][i]);
     } else {
       // s 2^24 (acc - z 2^-24 sum x): both power-of-two factors are exact.
 #pragma unroll
@@ -319,7 +323,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_wave_kernel(GemvArgs g) {
         const float zq = half_bits_to_float(half_bits<VEC>(zraw[gi], v)) * 0x1p-24f;
         const float sq = sc[v] * 0x1p24f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) total[v][i] = __builtin_fmaf(sq, __builtin_fmaf(-zq, xsum[i], acc[v][i]), total[v][i]);
+        for (int i = 0; i < NE; ++i) total[v][i] = __builtin_fmaf(sq, __builtin_fmaf(-zq, xsum[i], acc[v][i]), total[v][i]);
       }
     }
   }
