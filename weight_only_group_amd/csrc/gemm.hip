@@ -174,6 +174,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, size_
 #ifndef QMM_GEMM_SPREAD
 #define QMM_GEMM_SPREAD 1
 #endif
+#ifndef QMM_GEMM_NBUF4
+#define QMM_GEMM_NBUF4 1
+#endif
 #define QMM_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
 // A 16-byte-per-lane load from a buffer straight into LDS: lane l's bytes
@@ -217,7 +220,10 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
   constexpr int ACC = TM * TN * 16;  // accumulators per lane
   // Each group's three activation buffers; then, reusing them, the other
   // groups' partial sums.
-  constexpr int NBUF = 3;  // activation slab buffers per group
+  // Activation slab buffers per group: four where they fit the LDS (with the
+  // spread loads, the fourth lengthens how far ahead a slab's last quarter is
+  // requested from 5 steps to 9), else three.
+  constexpr int NBUF = (QMM_GEMM_NBUF4 && KG * 4 * BM * BK * 2 + BM * 4 <= 160 * 1024) ? 4 : 3;
   constexpr int kLdsHalves = cmax(KG * NBUF * BM * BK, (KG - 1) * GW * ACC * 64 * 2);
   __shared__ __attribute__((aligned(16))) f16 lds[kLdsHalves];
   __shared__ float rsum[BM];  // row sums of x, for zero points that are not integers
@@ -231,7 +237,7 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
   // Activation loads of a slab spread over its four steps (one 1 KiB load
   // per wave and step) instead of four in one step, where they fill the
   // texture unit's command queue and hold back the next instructions.
-  constexpr bool SPREAD = QMM_GEMM_SPREAD && CQ == 4 && NBUF == 3;
+  constexpr bool SPREAD = QMM_GEMM_SPREAD && CQ == 4;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -521,8 +527,9 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
         // and at least this many were issued after its last one. Whole
         // slabs (issued NBUF - 1 slabs ago): the weight loads of
         // 4 (NBUF - 2) + 3 steps. Spread slabs (last quarter issued in step 2
-        // of slab i - 1): the weight loads and one quarter of four steps.
-        QMM_WAIT_VMCNT(cmin(SPREAD ? 4 * NBI + 4 : (4 * (NBUF - 2) + 3) * NBI, 63));
+        // of slab i + 2 - NBUF): the weight loads and one quarter of each of
+        // 4 (NBUF - 2) steps.
+        QMM_WAIT_VMCNT(cmin(SPREAD ? 4 * (NBUF - 2) * (NBI + 1) : (4 * (NBUF - 2) + 3) * NBI, 63));
         __syncthreads();  // slab i + 1 is in LDS
       }
 #pragma unroll
@@ -579,11 +586,12 @@ __global__ __launch_bounds__(64 * WM * WN * KG, 1) void gemm_kernel(GemmArgs g) 
     }
   };
 
-  dmaA(0, gslab(0));
-  dmaA(1, gslab(1));
-  if constexpr (SPREAD) dmaA_part(2, gslab(2), 0);  // its other quarters go out in slab 0's steps 0-2
-  else dmaA(2, gslab(2));
-  if constexpr (NBUF > 3) dmaA(3, gslab(3));
+#pragma unroll
+  for (int b = 0; b < NBUF - 1; ++b) dmaA(b, gslab(b));
+  // the last buffer's slab: with the spread loads only its first quarter
+  // here, the other three in slab 0's steps 0-2
+  if constexpr (SPREAD) dmaA_part(NBUF - 1, gslab(NBUF - 1), 0);
+  else dmaA(NBUF - 1, gslab(NBUF - 1));
 #pragma unroll
   for (int s = 0; s < 4; ++s) loadB(B0[s], gslab(0), s);
   loadZS(Z0, gslab(0));  // with one group per column: the only zero/scale load
