@@ -255,6 +255,57 @@ def test_one_hot_rows_bit_exact(gpu, path, bits, gs):
     assert mism.size == 0, [(probe[i], n, float(got[i, n]), float(want[i, n])) for i, n in mism[:10]]
 
 
+# Extreme value regimes for the decode product's subnormal form (codes as fp16
+# subnormals, activations prescaled by 2^-e, s and z applied to per-group sums)
+# and for the GEMM: activations that are fp16 subnormals or large, zero points
+# far outside the code range (negative, above 1024, fractional), scales that
+# are fp16 subnormals or large. Each regime keeps y inside the fp16 range.
+EXTREME = ("tiny_x", "large_x", "far_zeros", "scale_range")
+
+
+def _extreme_case(regime, M, K, N, bits, gs, seed):
+    rng = np.random.default_rng(seed)
+    G = oracle.num_groups(K, gs)
+    codes = datagen.draw_codes(K, N, bits, seed=seed)
+    x = datagen.draw_x_f32(M, K, seed).astype(np.float64)
+    z = rng.integers(0, 1 << bits, size=(G, N)).astype(np.float64)
+    s = rng.uniform(0.005, 0.02, size=(G, N))
+    if regime == "tiny_x":  # a third of x below the fp16 normal range, some zeros
+        sel = rng.random(size=x.shape)
+        x = np.where(sel < 0.33, x * 2.0 ** -16, x)
+        x[sel > 0.97] = 0.0
+    elif regime == "large_x":
+        x = x * 200.0
+        s = s * 0.05
+    elif regime == "far_zeros":  # negative, fractional, above 1024
+        kind = rng.integers(0, 3, size=(G, N))
+        z = np.where(kind == 0, -rng.uniform(1, 40, size=(G, N)), np.where(kind == 1, rng.uniform(1024, 1500, size=(G, N)), z + 0.37))
+        s = s * 0.02
+    elif regime == "scale_range":  # fp16 subnormal scales next to large ones
+        kind = rng.integers(0, 3, size=(G, N))
+        s = np.where(kind == 0, rng.uniform(2.0 ** -24, 2.0 ** -15, size=(G, N)), np.where(kind == 1, rng.uniform(1, 4, size=(G, N)), s))
+    return codes, x.astype(np.float16), z.astype(np.float16), s.astype(np.float16)
+
+
+@pytest.mark.parametrize("regime", EXTREME)
+@pytest.mark.parametrize("bits", (1, 2, 3, 4, 8))
+def test_extreme_values(gpu, regime, bits):
+    cases = [("gemv", 1, 1024, 512, 128), ("gemv", 8, 1024, 528, 64), ("gemm", 96, 1024, 520, 128)]
+    for path, M, K, N, gs in cases:
+        codes, x, z, s = _extreme_case(regime, M, K, N, bits, gs, seed=31 * bits + M + len(regime))
+        _say(f"extreme {regime} {path} M={M} K={K} N={N} bits={bits} gs={gs}")
+        qw, qlo = _pack_gpu(gpu, codes, bits)
+        y_ref, a = oracle.quantized_matmul_codes(x, codes, z, s, gs)
+        assert np.all(np.abs(y_ref) < 6e4), "the case must stay inside the fp16 range"
+        y = _product(gpu, path, _t(x), qw, qlo, _t(z), _t(s), bits, gs)
+        _check(y.cpu().numpy().astype(np.float64), y_ref, a, f"{regime} {path} bits={bits}")
+        if path == "gemv":
+            sw = gpu.qmm_to_strips(qw)
+            slo = None if qlo is None else gpu.qmm_to_strips(qlo)
+            y2 = gpu.qmm_gemv(_t(x), sw, slo, _t(z), _t(s), bits, gs, strips=True)
+            _check(y2.cpu().numpy().astype(np.float64), y_ref, a, f"{regime} {path} strips bits={bits}")
+
+
 @pytest.mark.parametrize("path", ["gemv", "gemm"])
 def test_column_sums(gpu, path):
     """x = 1 sums every column of the dequantized weight."""
