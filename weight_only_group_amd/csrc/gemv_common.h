@@ -20,6 +20,9 @@
 #ifndef QMM_GEMV_WAVE_X
 #define QMM_GEMV_WAVE_X 1  // wave kernel: waves stage their own activations (0: the block, one barrier)
 #endif
+#ifndef QMM_GEMV_XSUM_LDS
+#define QMM_GEMV_XSUM_LDS 1  // wave kernel, one row with block staging: sums of x per group from the staged slots
+#endif
 #ifndef QMM_GEMV_SZ_SHARE
 #define QMM_GEMV_SZ_SHARE 1  // wave kernel, several rows: lane groups request one group's scales / zero points each and share them
 #endif

@@ -218,6 +218,21 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_wave_kernel(GemvArgs g) {
       const u32x4 a = x_operand<BITS>(xraw[i]);
       xs[xbase + (OWN ? lane + 64 * i : tid + THREADS * i)] = BF ? a : x_prescaled<BITS>(a);
     }
+  // One row, block staging (every thread one slot, the slots of a wave's
+  // units in its own lanes): the sum of x per group is the same for every
+  // column, so it comes from the staged slots instead of a second
+  // matrix-core product per unit. Each thread adds its slot's 8 values
+  // (packed dot products with ones, fp32), into an LDS array after the slots.
+  constexpr bool XSUM_LDS = QMM_GEMV_XSUM_LDS && !BF && M1 && !OWN;
+  float* const ps = reinterpret_cast<float*>(xs + THREADS);
+  if constexpr (XSUM_LDS) {
+    const f16x2 one2 = f16x2{(f16)1.f, (f16)1.f};
+    float p = __builtin_amdgcn_fdot2(as_f16x2(xraw[0].x), one2, 0.f, false);
+    p = __builtin_amdgcn_fdot2(as_f16x2(xraw[0].y), one2, p, false);
+    p = __builtin_amdgcn_fdot2(as_f16x2(xraw[0].z), one2, p, false);
+    p = __builtin_amdgcn_fdot2(as_f16x2(xraw[0].w), one2, p, false);
+    ps[tid] = p;
+  }
   if constexpr (OWN) {
     // The wave reads back only what it wrote itself: LDS operations of one
     // wave take effect in order, so a compiler-level fence is enough.
@@ -240,6 +255,21 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_wave_kernel(GemvArgs g) {
         zraw[gi][h] = (HT)__builtin_amdgcn_ds_bpermute(src, (int)zchk[h]);
       }
     }
+  }
+
+  // The wave's sums of x per group: lane l holds slot 4 ua + l (the wave's
+  // 64 slots); a butterfly over each group's lanes (fixed order, the same
+  // result in every lane) and one lane's value per group.
+  float xsg[GPW] = {};
+  if constexpr (XSUM_LDS) {
+    static_assert(4 * UPW == 64, "block staging gives a wave 64 slots");
+    constexpr int LG = 64 / GPW;  // lanes (slots) per group within the wave
+    float v = ps[4 * ua + lane];
+#pragma unroll
+    for (int off = 1; off < LG; off <<= 1) v += __shfl_xor(v, off);
+#pragma unroll
+    for (int gi = 0; gi < GPW; ++gi)
+      xsg[gi] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), LG * gi));
   }
 
   // ---- 3. the wave's units, group by group (static).
@@ -307,7 +337,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_wave_kernel(GemvArgs g) {
           acc[v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, pack8(b[0], b[1], b[2], b[3]), acc[v], 0, 0, 0);
         }
       }
-      if constexpr (!BF) xsum = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, araw), ones, xsum, 0, 0, 0);
+      if constexpr (!BF && !XSUM_LDS) xsum = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, araw), ones, xsum, 0, 0, 0);
     }
     // One row: only element 0 (row 0) of the accumulators is used.
     constexpr int NE = M1 ? 1 : 4;
@@ -323,7 +353,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_wave_kernel(GemvArgs g) {
         const float zq = half_bits_to_float(half_bits<VEC>(zraw[gi], v)) * 0x1p-24f;
         const float sq = sc[v] * 0x1p24f;
 #pragma unroll
-        for (int i = 0; i < NE; ++i) total[v][i] = __builtin_fmaf(sq, __builtin_fmaf(-zq, xsum[i], acc[v][i]), total[v][i]);
+        for (int i = 0; i < NE; ++i)
+          total[v][i] = __builtin_fmaf(sq, __builtin_fmaf(-zq, XSUM_LDS ? xsg[gi] : xsum[i], acc[v][i]), total[v][i]);
       }
     }
   }
