@@ -132,8 +132,10 @@ template <int BITS> __host__ __device__ constexpr int code_exp_sub(int p, int hi
 // high half; 3-bit: q >> 1 (2-bit plane) goes to bits 2-3 and q & 1 (1-bit
 // plane, its bytes of this lane group copied into both halves) to bit 1, so
 // each half is 1024 + 2q.
-// With SUB (decode_masks<BITS, true>) the same places hold the codes as fp16
-// subnormals: half `hi` of pair p is 2^e q 2^-24, exactly.
+// With SUB (decode_masks<BITS, true>) the codes are fp16 subnormals: half
+// `hi` of pair p is 2^e q 2^-24 exactly, with e = code_exp_sub(p, hi) (the
+// same places for 1-, 4- and 8-bit codes; 2- and 3-bit codes stay where their
+// bits are in the words). The element order is the same in both forms.
 template <int BITS, bool SUB = false>
 __device__ __forceinline__ void decode8(uint32_t w0, uint32_t w1, int j, const DecodeMasks<BITS>& dm,
                                         uint32_t (&b)[4]) {
