@@ -99,6 +99,7 @@ struct GemvPlan {
   int gl;           // wave kernel: log2 of the units per group (30: one group)
   int gpw;          // wave kernel: groups per wave (1, 2 or 4)
   int xcds;         // XCDs of the device
+  int one_xcd;      // wave kernel: strips all on XCD 0 (the grid holds xcds blocks per strip)
   size_t counters_bytes;  // arrival counters (one per strip), padded
   size_t workspace_bytes; // counters + split-K partial sums
   int valid;        // 0: the shape does not fit the decode product's staging limits

@@ -514,6 +514,11 @@ GemvPlan gemv_plan(int M, int K, int N, int bits, int group_size, DeviceTopo top
       p.gpw = gpw;
       p.ksplit = 1;
       p.units_per_block = U;
+      // Strips that fit on one XCD's CUs, with at most 1 MiB of weight
+      // words, all run on XCD 0, which starts its blocks first (one XCD's
+      // share of the memory system then carries them).
+      const long long wbytes = (long long)K * N * bits / 8;
+      p.one_xcd = (QMM_GEMV_ONE_XCD && p.xcds > 1 && p.nstrips <= cus / p.xcds && wbytes <= (1LL << 20)) ? p.xcds : 0;
       p.valid = 1;
       return p;
     }
@@ -583,6 +588,7 @@ hipError_t launch_gemv(const GemvPlan& p, const uint16_t* x, int M, int K, const
     if ((1 << l) == p.xcds && p.nstrips % p.xcds == 0) a.xcd_log2 = l;
   a.gl = p.gl;
   a.strips = strips ? 1 : 0;
+  a.one_xcd = p.kind == 1 ? p.one_xcd : 0;
   if (p.kind == 1) return launch_wave_any(p, a, bits, bf16, s);
   return bf16 ? launch_dtype<true>(p, a, bits, s) : launch_dtype<false>(p, a, bits, s);
 }

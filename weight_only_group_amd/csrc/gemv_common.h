@@ -29,6 +29,9 @@
 #ifndef QMM_GEMV_XCD_REMAP
 #define QMM_GEMV_XCD_REMAP 1
 #endif
+#ifndef QMM_GEMV_ONE_XCD
+#define QMM_GEMV_ONE_XCD 1  // wave kernel: strips that fit on one XCD's CUs all run there
+#endif
 
 namespace qmm {
 
@@ -52,6 +55,7 @@ struct GemvArgs {
   int xcd_log2;  // log2 of the XCD count when that is a power of two dividing the grid's x size, else -1
   int gl;        // wave kernel: log2 of the units per group (30 for one group over all of K)
   int strips;    // packed words in the 16-column strip-major layout (else K-major)
+  int one_xcd;   // wave kernel: the XCD count when the grid is that many times the strips and only XCD 0's blocks work, else 0
 };
 
 namespace {

@@ -111,7 +111,12 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_wave_kernel(GemvArgs g) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = lane >> 4;
   const int cl = lane & 15;
-  const int strip = xcd_strip(blockIdx.x, gridDim.x, g.xcd_log2);
+  // A grid of few strips runs on XCD 0 alone: workgroups are dealt to the
+  // XCDs round-robin by linear id, and XCD 0 starts its blocks first (the
+  // others up to ~0.7 us later on MI355X). The blocks dealt to the other XCDs
+  // return before touching memory.
+  if (g.one_xcd > 1 && blockIdx.x % g.one_xcd != 0) return;
+  const int strip = g.one_xcd > 1 ? (int)blockIdx.x / g.one_xcd : xcd_strip(blockIdx.x, gridDim.x, g.xcd_log2);
   const int n0 = strip * COLS;
   const int nc = n0 + VEC * cl;
   const int ncc = nc < g.N ? nc : 0;
@@ -396,8 +401,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_wave_kernel(GemvArgs g) {
 template <int BITS, int VEC, int WAVES, int UPW, int GPW, bool BF>
 hipError_t launch_wave_typed(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
   const size_t lds = cmax(64 * WAVES * kWaveXPerThread * 16, WAVES * a.M * 16 * VEC * 4);
-  if (a.M == 1) gemv_wave_kernel<BITS, VEC, WAVES, UPW, GPW, BF, true><<<p.nstrips, 64 * WAVES, lds, s>>>(a);
-  else gemv_wave_kernel<BITS, VEC, WAVES, UPW, GPW, BF, false><<<p.nstrips, 64 * WAVES, lds, s>>>(a);
+  const int grid = a.one_xcd > 1 ? p.nstrips * a.one_xcd : p.nstrips;
+  if (a.M == 1) gemv_wave_kernel<BITS, VEC, WAVES, UPW, GPW, BF, true><<<grid, 64 * WAVES, lds, s>>>(a);
+  else gemv_wave_kernel<BITS, VEC, WAVES, UPW, GPW, BF, false><<<grid, 64 * WAVES, lds, s>>>(a);
   return hipGetLastError();
 }
 
