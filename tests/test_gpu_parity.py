@@ -146,6 +146,24 @@ def test_gemv_sweep(gpu, M, K, N, bits, gs):
     _check(y, y_ref, a, "gemv")
 
 
+# Wave-kernel grids around the one-XCD launch: up to 32 strips (one XCD's CUs, the last strip
+# ragged in some) run on XCD 0 alone with the other XCDs' workgroups returning at once; 33
+# strips take all XCDs. Every output is compared.
+ONE_XCD = [
+    (1, 512, 504, 4, 128), (1, 512, 512, 8, -1), (8, 512, 512, 2, 64), (16, 512, 504, 3, 32),
+    (8, 512, 200, 1, 32), (1, 512, 520, 4, 128), (16, 512, 520, 8, -1),
+]
+
+
+@pytest.mark.parametrize("M,K,N,bits,gs", ONE_XCD)
+def test_gemv_one_xcd_boundary(gpu, M, K, N, bits, gs):
+    plan = gpu.gemv_plan_info(M, K, N, bits, gs)
+    assert plan["kernel"] == 1, plan  # the wave kernel, which holds the one-XCD launch
+    _say(f"gemv (one-XCD boundary, {plan['strips']} strips) M={M} K={K} N={N} bits={bits} gs={gs}")
+    y, y_ref, a = _run(gpu, "gemv", M, K, N, bits, gs, seed=M + K + N + bits, nonint_zero=True)
+    _check(y, y_ref, a, "gemv")
+
+
 SWEEP_GEMM = [
     (1, 256, 64, 4, 128), (17, 512, 264, 4, 64), (300, 256, 520, 4, -1), (257, 320, 264, 4, 32),
     (100, 512, 136, 8, 128), (260, 1024, 264, 8, -1), (64, 96, 8, 8, 32),
