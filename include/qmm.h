@@ -135,7 +135,7 @@ size_t qmm_workspace_bytes(int M, int K, int N, int bits, int group_size);
 /*
  * qmm_gemv_plan_info -- the launch plan qmm_gemv (and qmm_gemv_bf16,
  * qmm_gemv_noalloc) uses for this problem on the current device, for tests
- * and measurement. Host only: no work is enqueued. Writes min(n, 9) ints:
+ * and measurement. Host only: no work is enqueued. Writes min(n, 10) ints:
  *   info[0] kernel: 0 = blocks split along K (partial sums through the
  *           workspace when info[4] > 1), 1 = one block per column strip, each
  *           wave over its own K range
@@ -147,6 +147,10 @@ size_t qmm_workspace_bytes(int M, int K, int N, int bits, int group_size);
  *   info[6] groups per wave (kernel 1), else 0
  *   info[7] XCDs the strips are laid out for
  *   info[8] compute units of the device
+ *   info[9] 1 if every strip runs on XCD 0 (kernel 1 with at most one strip
+ *           per CU of an XCD and at most 1 MiB of weight words: the grid then
+ *           holds one workgroup per strip on each XCD, and those dealt to the
+ *           other XCDs return at once), else 0
  * Returns QMM_ERR_NULL for a NULL info with n > 0, QMM_ERR_SHAPE (etc.) for
  * arguments qmm_gemv would reject on shape alone, else QMM_OK.
  */

@@ -42,6 +42,10 @@ def test_plans_tile_the_problem(bits):
                     assert p["vec"] in (1, 2, 4)
                     assert p["strips"] == (N + cols - 1) // cols
                     assert p["xcds"] >= 1 and p["cus"] >= 1
+                    # all strips on XCD 0: the wave kernel, at most one strip per CU of an XCD,
+                    # at most 1 MiB of weight words
+                    small = p["strips"] <= p["cus"] // p["xcds"] and K * N * bits // 8 <= 1 << 20
+                    assert p["one_xcd"] == int(p["kernel"] == 1 and p["xcds"] > 1 and small)
                     if p["kernel"] == 1:
                         assert p["ksplit"] == 1
                         assert p["waves"] * p["units"] == U
@@ -118,3 +122,19 @@ def test_gemm_block_tiles():
     for args in ((0, 64, 64, 4, -1), (1, 40, 64, 4, -1), (1, 64, 60, 4, -1), (1, 64, 64, 6, -1), (1, 64, 64, 4, 48)):
         with pytest.raises(w.QmmError):
             w.gemm_plan_info(*args)
+
+
+def test_one_xcd_boundary():
+    """32 strips of a short-K product run on XCD 0 alone, 33 take every XCD; the rule needs the
+    wave kernel and at most 1 MiB of weight words (8 XCDs of 32 CUs: the default topology
+    without a device, and MI355X's)."""
+    w = _lib()
+    on = w.gemv_plan_info(1, 512, 512, 4, 128)
+    if on["xcds"] != 8 or on["cus"] != 256:
+        pytest.skip("the boundary below assumes 8 XCDs of 32 CUs")
+    assert on["kernel"] == 1 and on["strips"] == 32 and on["one_xcd"] == 1
+    off = w.gemv_plan_info(1, 512, 520, 4, 128)
+    assert off["kernel"] == 1 and off["strips"] == 33 and off["one_xcd"] == 0
+    split = w.gemv_plan_info(1, 4096, 512, 4, 128)  # few strips, long K: blocks split along K
+    assert split["kernel"] == 0 and split["one_xcd"] == 0
+

@@ -159,6 +159,7 @@ ONE_XCD = [
 def test_gemv_one_xcd_boundary(gpu, M, K, N, bits, gs):
     plan = gpu.gemv_plan_info(M, K, N, bits, gs)
     assert plan["kernel"] == 1, plan  # the wave kernel, which holds the one-XCD launch
+    assert plan["one_xcd"] == int(plan["strips"] <= plan["cus"] // plan["xcds"]), plan
     _say(f"gemv (one-XCD boundary, {plan['strips']} strips) M={M} K={K} N={N} bits={bits} gs={gs}")
     y, y_ref, a = _run(gpu, "gemv", M, K, N, bits, gs, seed=M + K + N + bits, nonint_zero=True)
     _check(y, y_ref, a, "gemv")

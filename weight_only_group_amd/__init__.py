@@ -230,7 +230,7 @@ def workspace_bytes(M: int, K: int, N: int, bits: int, group_size: int) -> int:
     return int(library().qmm_workspace_bytes(M, K, N, bits, group_size))
 
 
-GEMV_PLAN_FIELDS = ("kernel", "vec", "waves", "strips", "ksplit", "units", "groups_per_wave", "xcds", "cus")
+GEMV_PLAN_FIELDS = ("kernel", "vec", "waves", "strips", "ksplit", "units", "groups_per_wave", "xcds", "cus", "one_xcd")
 
 
 def gemv_plan_info(M: int, K: int, N: int, bits: int, group_size: int) -> dict:

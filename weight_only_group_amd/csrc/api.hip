@@ -313,9 +313,10 @@ qmm_status qmm_gemv_plan_info(int M, int K, int N, int bits, int group_size, int
   if (!p.valid)
     return fail(QMM_ERR_SHAPE, "M=%d, K=%d, group_size=%d exceed the decode product's staging limits", M, K,
                 group_size);
-  const int32_t v[9] = {p.kind, p.vec, p.waves, p.nstrips, p.ksplit,
-                        p.kind == 1 ? p.upw : p.units_per_block, p.kind == 1 ? p.gpw : 0, p.xcds, topo.cus};
-  for (int i = 0; i < n && i < 9; ++i) info[i] = v[i];
+  const int32_t v[10] = {p.kind, p.vec, p.waves, p.nstrips, p.ksplit,
+                         p.kind == 1 ? p.upw : p.units_per_block, p.kind == 1 ? p.gpw : 0, p.xcds, topo.cus,
+                         p.kind == 1 && p.one_xcd > 1 ? 1 : 0};
+  for (int i = 0; i < n && i < 10; ++i) info[i] = v[i];
   return ok();
 }
 
